@@ -1,0 +1,100 @@
+"""CPU tests of the input generators and of the matching rules (fake backends)."""
+import numpy as np
+
+import datagen
+from oracle import indexer as O
+from oracle.check import check_selection
+
+
+def test_generation_is_deterministic_and_chunk_independent():
+    wl = datagen.small(2, nq=3, n_seq=3, l_max=70000)
+    q1, w1 = datagen.queries(wl, 0)
+    q2, w2 = datagen.queries(wl, 0)
+    assert np.array_equal(q1, q2) and np.array_equal(w1, w2)
+    k_a = datagen.keys(wl, 1, q1, w1, 0)
+    k_b = datagen.all_keys(wl, q1, w1, 0, threads=3)[1]
+    assert np.array_equal(k_a, k_b)
+    q3, _ = datagen.queries(wl, 1)
+    assert not np.array_equal(q1, q3)
+
+
+def test_bf16_rounding_of_generator():
+    x = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -2.5, 0.0], dtype=np.float32)
+    b = datagen.f32_to_bf16_bits(x)
+    back = datagen.bf16_bits_to_f32(b)
+    assert back.tolist() == [1.0, 1.0, 1.0 + 2 ** -6, -2.5, 0.0]
+
+
+def test_workload_shapes_and_positions():
+    for wid, wl in datagen.WORKLOADS.items():
+        seq, pos = datagen.positions(wl)
+        assert seq.shape == (wl.nq,) and pos.shape == (wl.nq,)
+        assert pos.max() < wl.l_max and pos.min() >= 0
+        assert seq.max() < wl.n_seq
+    seq, pos = datagen.positions(datagen.WORKLOADS[1])
+    assert pos.tolist() == list(range(4080, 4096))
+
+
+def test_planted_keys_follow_queries():
+    wl = datagen.small(2, nq=2, n_seq=2, l_max=4096)
+    q, w = datagen.queries(wl, 0)
+    K = datagen.bf16_bits_to_f32(datagen.keys(wl, 0, q, w, 0)).astype(np.float64)
+    qf = datagen.bf16_bits_to_f32(q).astype(np.float64)
+    # a planted key correlates with one positive-weight head of its query
+    cos = (K @ qf[0].T) / np.linalg.norm(K, axis=1)[:, None] / np.linalg.norm(qf[0], axis=1)
+    assert (cos.max(axis=1) > 0.8).sum() == int(round(0.01 * 4096))
+
+
+def _row(seed=0, n=300, H=4, d=8):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((H, d)); w = rng.standard_normal(H); K = rng.standard_normal((n, d))
+    s, A = O.indexer_scores(q, w, K)
+    F = O.dot_magnitude(q, w, K)
+    return s, A, F
+
+
+def test_checker_accepts_oracle_and_small_noise():
+    s, A, F = _row()
+    ids = np.arange(s.size)
+    idx, val = O.top_k(s, ids, 20)
+    assert check_selection(idx, val, ids, s, A, 20, F) == []
+    perm = np.random.default_rng(1).permutation(20)
+    noisy = val[perm] * (1 + 1e-5)
+    assert check_selection(idx[perm], noisy, ids, s, A, 20, F) == []
+
+
+def test_checker_rejects_wrong_sets_and_scores():
+    s, A, F = _row()
+    ids = np.arange(s.size)
+    idx, val = O.top_k(s, ids, 20)
+    order = np.lexsort((ids, -s))
+    # swap a clear winner for a clear loser
+    bad = idx.copy(); bad[0] = order[-1]
+    assert check_selection(bad, None, ids, s, A, 20, F)
+    # duplicate
+    dup = idx.copy(); dup[1] = dup[0]
+    assert check_selection(dup, None, ids, s, A, 20, F)
+    # out of candidate set
+    oob = idx.copy(); oob[2] = 10_000
+    assert check_selection(oob, None, ids, s, A, 20, F)
+    # score outside tolerance
+    v = val.copy(); v[3] += 0.01 * max(abs(v[3]), A[idx[3]]) + 1.0
+    assert check_selection(idx, v, ids, s, A, 20, F)
+    # padding must be -1 / -inf
+    short = np.arange(5)
+    i5, v5 = O.top_k(s[:5], short, 8)
+    assert check_selection(i5, v5, short, s[:5], A[:5], 8, F[:5]) == []
+    i5b = i5.copy(); i5b[-1] = 0
+    assert check_selection(i5b, v5, short, s[:5], A[:5], 8, F[:5])
+
+
+def test_checker_tie_band_allows_swaps_only_inside_band():
+    s = np.array([5.0, 4.0, 3.0, 3.0 + 1e-9, 1.0, 0.5])
+    A = np.abs(s) + 1.0
+    ids = np.arange(6)
+    # oracle top-3 = {0, 1, 3}; 2 and 3 are within tolerance of each other
+    assert check_selection(np.array([0, 1, 2]), None, ids, s, A, 3) == []
+    assert check_selection(np.array([0, 1, 4]), None, ids, s, A, 3)
+    # all-equal scores: every swap is inside the band, but the count must hold
+    z = np.zeros(10)
+    assert check_selection(np.array([9, 8, 7]), None, np.arange(10), z, z + 1, 3) == []
