@@ -1,0 +1,177 @@
+/*
+ * dsa_indexer.h - C ABI of the gfx950 (MI355X) DSA indexer library.
+ *
+ * The DeepSeek-Sparse-Attention indexer scores every causal prefix token of a
+ * query through a pool of H_I indexer heads and keeps the k best tokens for the
+ * sparse attention that follows ("MISA: Mixture of Indexer Sparse Attention for
+ * Long-Context LLM Inference", technical summary, section "problem"):
+ *
+ *     s(t, u) = sum_j w[t, j] * max(0, q[t, j] . k[u]),   u = 0 .. pos_t,
+ *
+ * with signed per-head weights w ("DoSA: Dots Sparse Attention" review,
+ * sections 1 and 3: signed heads, exact top-K), no scale, bias or softmax; the
+ * key cache holds one key per token shared by all heads.  Ties are broken by the
+ * lower token index.  Two reduced variants are provided: MISA head routing (same
+ * MISA summary, sections "method" and "hierarchical variant") and HISA block
+ * filtering ("HISA: Efficient Hierarchical Indexing for Fine-Grained Sparse
+ * Attention" review, sections 1 and 3).
+ *
+ * Conventions shared by every entry point
+ *  - Every pointer is a DEVICE pointer (hipMalloc'ed or equivalent) on the
+ *    current HIP device; tensors are dense, row-major, in the layouts below.
+ *    q, k and k_pooled must be 16-byte aligned; workspace 256-byte aligned.
+ *  - The caller owns every buffer, including the workspace.  The library never
+ *    allocates device memory and keeps no pointer after a call returns.
+ *  - Calls are asynchronous on `stream` (NULL = the default stream).  Argument
+ *    errors return synchronously before any launch; launch errors are reported
+ *    from the launch; device faults surface at the caller's synchronisation.
+ *    With the environment variable DSA_DEBUG=1 every call synchronises and
+ *    reports device errors itself.
+ *  - On a non-zero status nothing has been launched (argument errors) or the
+ *    outputs are undefined (DSA_EHIP); dsa_last_error() gives a message.
+ *  - Queries: query t belongs to sequence q_seq[t] (q_seq may be NULL: all
+ *    queries on sequence 0) and sits at position q_pos[t]; its causal prefix is
+ *    keys 0 .. q_pos[t] inclusive.  A query whose q_seq / q_pos is out of range
+ *    (q_seq not in [0, n_seq), q_pos not in [0, l_max)) gets an all-padding row.
+ *  - Outputs: out_idx [nq, top_k] int32 and out_score [nq, top_k] float32
+ *    (out_score may be NULL).  Row t holds K_t = min(top_k, number of
+ *    candidates) selected entries first, in unspecified order (set semantics),
+ *    then top_k - K_t padding entries (-1, -inf).  Returned scores are the
+ *    float32 scores the selection was made on.
+ *  - Workspace contents on entry are ignored (the library clears what it needs
+ *    at the start of each call); two calls that run concurrently must not share
+ *    a workspace.
+ *  - Supported shapes: head_dim 64 or 128; 1 <= n_heads <= 64; bf16 inputs
+ *    use MFMA, float32 inputs (dense call only) the vector ALUs.
+ */
+#ifndef DSA_INDEXER_H
+#define DSA_INDEXER_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define DSA_OK 0
+#define DSA_EINVAL 1       /* bad shape, pointer, alignment or argument combination */
+#define DSA_EUNSUPPORTED 2 /* valid but not implemented (e.g. head_dim not 64/128) */
+#define DSA_EWORKSPACE 3   /* workspace_bytes smaller than the *_workspace_size value */
+#define DSA_EHIP 4         /* a HIP call or kernel launch failed */
+
+/* input element types of q, k (and k_pooled) */
+#define DSA_DTYPE_BF16 0   /* bf16 carried as 16-bit patterns */
+#define DSA_DTYPE_F32 1
+
+/* Message for the last non-zero status returned on the calling thread. */
+const char* dsa_last_error(void);
+
+/* ABI version of this header (increments on any signature change). */
+int dsa_abi_version(void);
+
+/*
+ * Dense DSA indexer: score every prefix key of every query with all n_heads
+ * heads and select the top_k keys (MISA summary, section "problem").
+ *
+ *   q       [nq, n_heads, head_dim]    dtype
+ *   w       [nq, n_heads]              float32, signed
+ *   k       [n_seq, l_max, head_dim]   dtype   (indexer key cache)
+ *   q_seq   [nq] int32 or NULL,  q_pos [nq] int32
+ *   out_idx [nq, top_k] int32 token indices;  out_score [nq, top_k] or NULL
+ * 1 <= top_k <= 1048576.  Workspace: indexer_score_topk_workspace_size(...).
+ */
+size_t indexer_score_topk_workspace_size(int32_t nq, int32_t n_heads, int32_t head_dim,
+                                         int32_t n_seq, int64_t l_max, int32_t top_k,
+                                         int32_t dtype);
+int indexer_score_topk(const void* q, const float* w, const void* k, int32_t dtype,
+                       const int32_t* q_seq, const int32_t* q_pos, int32_t nq, int32_t n_heads,
+                       int32_t head_dim, int32_t n_seq, int64_t l_max, int32_t top_k,
+                       int32_t* out_idx, float* out_score, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Mean-pooled block keys (MISA summary, "method" step 1: M = ceil(L/B) blocks
+ * and mean-pooled indexing keys; HISA review, section 3: pooled representative
+ * vector per block of size B).  Block b of sequence s covers tokens
+ * [b*block, min((b+1)*block, l_max)); its pooled key is their mean, accumulated
+ * in float64 and rounded once to bf16 (round to nearest, ties to even).
+ *
+ *   k         [n_seq, l_max, head_dim]             bf16
+ *   k_pooled  [n_seq, ceil(l_max/block), head_dim] bf16 (written)
+ * Only DSA_DTYPE_BF16.  Needs no workspace.
+ */
+int indexer_mean_pool_keys(const void* k, int32_t dtype, int32_t n_seq, int64_t l_max,
+                           int32_t head_dim, int32_t block, void* k_pooled, hipStream_t stream);
+
+/*
+ * MISA head-routed indexer (MISA summary, "method"): the router scores the
+ * query's pooled block keys with all heads, importance
+ *   I[t, j] = |w[t, j]| * sum_{b < M_t} max(0, q[t, j] . kbar[b]),  M_t = ceil((q_pos[t]+1)/block),
+ * keeps the n_active_heads (h) most important heads (ties: lower head index),
+ * and only those heads score every prefix token with their original weights.
+ *  - k_prime == 0 (MISA): out_idx / out_score = top_k of the h-head scores.
+ *  - k_prime >= top_k (MISA dagger, "hierarchical variant"): the h-head pass
+ *    keeps k_prime candidates (written to out_cand [nq, k_prime] if not NULL,
+ *    padded with -1), all heads rescore them, and out_idx / out_score are the
+ *    top_k of the full scores.
+ * The pooled keys of a query's partial last block (when (q_pos+1) % block != 0)
+ * are computed from k, so k_pooled only needs to hold full blocks.
+ *
+ *   k_pooled  [n_seq, ceil(l_max/block), head_dim] bf16 from
+ *             indexer_mean_pool_keys, or NULL (then the call pools into its
+ *             workspace first, which reads the whole key cache)
+ *   out_heads [nq, h] int32 routed heads, most important first, or NULL
+ *   out_importance [nq, n_heads] float32 router importance, or NULL
+ * Only DSA_DTYPE_BF16; 1 <= h <= n_heads; 1 <= block.
+ */
+size_t misa_route_score_topk_workspace_size(int32_t nq, int32_t n_heads, int32_t head_dim,
+                                            int32_t n_seq, int64_t l_max, int32_t block,
+                                            int32_t n_active_heads, int32_t k_prime,
+                                            int32_t top_k, int32_t pooled_given);
+int misa_route_score_topk(const void* q, const float* w, const void* k, const void* k_pooled,
+                          int32_t dtype, const int32_t* q_seq, const int32_t* q_pos, int32_t nq,
+                          int32_t n_heads, int32_t head_dim, int32_t n_seq, int64_t l_max,
+                          int32_t block, int32_t n_active_heads, int32_t k_prime, int32_t top_k,
+                          int32_t* out_idx, float* out_score, int32_t* out_heads,
+                          float* out_importance, int32_t* out_cand, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * HISA block-filtered indexer (HISA review, sections 1 and 3): block scores
+ *   bs[t, b] = sum_j w[t, j] * max(0, q[t, j] . kbar[b]),  b < M_t,
+ * keep the m_blocks best blocks (ties: lower block index), then score the
+ * tokens of the surviving blocks (clipped to the prefix) with all heads and
+ * keep the top_k.  Partial last blocks are pooled from k as for MISA.
+ *
+ *   out_blocks [nq, m_blocks] int32 surviving blocks (padded with -1) or NULL
+ *   out_block_score [nq, m_blocks] float32 their block scores, or NULL
+ * Only DSA_DTYPE_BF16; 1 <= m_blocks; 1 <= block.
+ */
+size_t hisa_block_filter_topk_workspace_size(int32_t nq, int32_t n_heads, int32_t head_dim,
+                                             int32_t n_seq, int64_t l_max, int32_t block,
+                                             int32_t m_blocks, int32_t top_k,
+                                             int32_t pooled_given);
+int hisa_block_filter_topk(const void* q, const float* w, const void* k, const void* k_pooled,
+                           int32_t dtype, const int32_t* q_seq, const int32_t* q_pos, int32_t nq,
+                           int32_t n_heads, int32_t head_dim, int32_t n_seq, int64_t l_max,
+                           int32_t block, int32_t m_blocks, int32_t top_k, int32_t* out_idx,
+                           float* out_score, int32_t* out_blocks, float* out_block_score,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Selection agreement (MISA summary, "results"; HISA review, section 3): per
+ * query IoU = |A & B| / |A | B| over the non-negative entries of a[t, :] and
+ * b[t, :] (two empty rows give 1).  Rows must hold no duplicate indices.
+ *   a, b [nq, k] int32;  out_iou [nq] float32;  1 <= k <= 8192.
+ */
+int indexer_selection_iou(const int32_t* a, const int32_t* b, int32_t nq, int32_t k,
+                          float* out_iou, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_INDEXER_H */

@@ -1,0 +1,300 @@
+"""Python binding of libdsa_indexer.so, the gfx950 DSA indexer library.
+
+Argument marshalling only: every step of the indexer runs in the library's HIP
+kernels.  PyTorch supplies device memory and the current HIP stream.  The C
+contract (layouts, padding, error codes) is documented in include/dsa_indexer.h;
+the functions here carry the same names.
+
+If the shared library has not been built, every call raises; there is no
+fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdsa_indexer.so")
+
+DSA_DTYPE_BF16 = 0
+DSA_DTYPE_F32 = 1
+
+_c_p = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_sz = ctypes.c_size_t
+
+_SIGS = {
+    "dsa_last_error": ([], ctypes.c_char_p),
+    "dsa_abi_version": ([], ctypes.c_int),
+    "indexer_score_topk_workspace_size": ([_i32, _i32, _i32, _i32, _i64, _i32, _i32], _sz),
+    "indexer_score_topk": ([_c_p, _c_p, _c_p, _i32, _c_p, _c_p, _i32, _i32, _i32, _i32, _i64, _i32,
+                            _c_p, _c_p, _c_p, _sz, _c_p], ctypes.c_int),
+    "indexer_mean_pool_keys": ([_c_p, _i32, _i32, _i64, _i32, _i32, _c_p, _c_p], ctypes.c_int),
+    "misa_route_score_topk_workspace_size": ([_i32, _i32, _i32, _i32, _i64, _i32, _i32, _i32, _i32,
+                                              _i32], _sz),
+    "misa_route_score_topk": ([_c_p, _c_p, _c_p, _c_p, _i32, _c_p, _c_p, _i32, _i32, _i32, _i32,
+                               _i64, _i32, _i32, _i32, _i32, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
+                               _sz, _c_p], ctypes.c_int),
+    "hisa_block_filter_topk_workspace_size": ([_i32, _i32, _i32, _i32, _i64, _i32, _i32, _i32,
+                                               _i32], _sz),
+    "hisa_block_filter_topk": ([_c_p, _c_p, _c_p, _c_p, _i32, _c_p, _c_p, _i32, _i32, _i32, _i32,
+                                _i64, _i32, _i32, _i32, _c_p, _c_p, _c_p, _c_p, _c_p, _sz, _c_p],
+                               ctypes.c_int),
+    "indexer_selection_iou": ([_c_p, _c_p, _i32, _i32, _c_p, _c_p], ctypes.c_int),
+}
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class DsaError(RuntimeError):
+    pass
+
+
+def lib() -> ctypes.CDLL:
+    """Load the shared library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run "
+                               "`python -m sparse_attention_token_indexer_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        msg = lib().dsa_last_error().decode(errors="replace")
+        raise DsaError(f"{what} failed (status {status}): {msg}")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DSA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DSA_DTYPE_F32
+    raise TypeError(f"unsupported input dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, dims=None, device=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if dims is not None and t.dim() != dims:
+        raise ValueError(f"{name} must have {dims} dims, got shape {tuple(t.shape)}")
+
+
+def _workspace(nbytes: int, dev: torch.device, given: Optional[torch.Tensor]) -> torch.Tensor:
+    if given is not None:
+        _need(given, "workspace", torch.uint8, 1, dev)
+        if given.numel() < nbytes or given.data_ptr() % 256:
+            raise ValueError(f"workspace must hold >= {nbytes} bytes, 256-byte aligned")
+        return given
+    buf = torch.empty(max(nbytes, 1) + 256, dtype=torch.uint8, device=dev)
+    off = (-buf.data_ptr()) % 256
+    return buf[off:off + max(nbytes, 1)]
+
+
+def _common(q, w, k, q_pos, q_seq):
+    _need(q, "q", dims=3)
+    dev = q.device
+    _need(w, "w", torch.float32, 2, dev)
+    _need(k, "k", q.dtype, 3, dev)
+    _need(q_pos, "q_pos", torch.int32, 1, dev)
+    if q_seq is not None:
+        _need(q_seq, "q_seq", torch.int32, 1, dev)
+    nq, H, d = q.shape
+    n_seq, l_max, dk = k.shape
+    if w.shape != (nq, H) or dk != d or q_pos.shape[0] != nq or (
+            q_seq is not None and q_seq.shape[0] != nq):
+        raise ValueError("inconsistent shapes: q [nq,H,d], w [nq,H], k [n_seq,l_max,d], "
+                         "q_pos/q_seq [nq]")
+    return dev, nq, H, d, n_seq, l_max
+
+
+def _outputs(dev, nq, k, out_idx, out_score, with_scores):
+    if out_idx is None:
+        out_idx = torch.empty((nq, k), dtype=torch.int32, device=dev)
+    else:
+        _need(out_idx, "out_idx", torch.int32, 2, dev)
+        if tuple(out_idx.shape) != (nq, k):
+            raise ValueError("out_idx must be [nq, top_k]")
+    if out_score is None and with_scores:
+        out_score = torch.empty((nq, k), dtype=torch.float32, device=dev)
+    elif out_score is not None:
+        _need(out_score, "out_score", torch.float32, 2, dev)
+        if tuple(out_score.shape) != (nq, k):
+            raise ValueError("out_score must be [nq, top_k]")
+    return out_idx, out_score
+
+
+def indexer_score_topk_workspace_size(nq, n_heads, head_dim, n_seq, l_max, top_k,
+                                      dtype=DSA_DTYPE_BF16) -> int:
+    return int(lib().indexer_score_topk_workspace_size(nq, n_heads, head_dim, n_seq, l_max,
+                                                       top_k, dtype))
+
+
+def indexer_score_topk(q: torch.Tensor, w: torch.Tensor, k: torch.Tensor, q_pos: torch.Tensor,
+                       q_seq: Optional[torch.Tensor] = None, top_k: int = 2048,
+                       out_idx: Optional[torch.Tensor] = None,
+                       out_score: Optional[torch.Tensor] = None, with_scores: bool = True,
+                       workspace: Optional[torch.Tensor] = None
+                       ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Dense DSA indexer: top_k prefix keys per query.  Returns (idx, scores)."""
+    dev, nq, H, d, n_seq, l_max = _common(q, w, k, q_pos, q_seq)
+    dt = _dtype_code(q)
+    out_idx, out_score = _outputs(dev, nq, top_k, out_idx, out_score, with_scores)
+    nbytes = indexer_score_topk_workspace_size(nq, H, d, n_seq, l_max, top_k, dt)
+    ws = _workspace(nbytes, dev, workspace)
+    st = lib().indexer_score_topk(_ptr(q), _ptr(w), _ptr(k), dt, _ptr(q_seq), _ptr(q_pos), nq, H,
+                                  d, n_seq, l_max, top_k, _ptr(out_idx), _ptr(out_score),
+                                  _ptr(ws), nbytes, _stream(dev))
+    _check(st, "indexer_score_topk")
+    return out_idx, out_score
+
+
+def indexer_mean_pool_keys(k: torch.Tensor, block: int,
+                           out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Mean-pooled bf16 block keys [n_seq, ceil(l_max/block), d]."""
+    _need(k, "k", torch.bfloat16, 3)
+    n_seq, l_max, d = k.shape
+    m = -(-l_max // block)
+    if out is None:
+        out = torch.empty((n_seq, m, d), dtype=torch.bfloat16, device=k.device)
+    else:
+        _need(out, "out", torch.bfloat16, 3, k.device)
+        if tuple(out.shape) != (n_seq, m, d):
+            raise ValueError("out must be [n_seq, ceil(l_max/block), d]")
+    st = lib().indexer_mean_pool_keys(_ptr(k), DSA_DTYPE_BF16, n_seq, l_max, d, block, _ptr(out),
+                                      _stream(k.device))
+    _check(st, "indexer_mean_pool_keys")
+    return out
+
+
+def misa_route_score_topk_workspace_size(nq, n_heads, head_dim, n_seq, l_max, block,
+                                         n_active_heads, k_prime, top_k, pooled_given) -> int:
+    return int(lib().misa_route_score_topk_workspace_size(nq, n_heads, head_dim, n_seq, l_max,
+                                                          block, n_active_heads, k_prime, top_k,
+                                                          int(bool(pooled_given))))
+
+
+def misa_route_score_topk(q, w, k, q_pos, q_seq=None, *, block: int, n_active_heads: int,
+                          top_k: int, k_prime: int = 0, k_pooled=None, with_scores=True,
+                          with_heads=True, with_importance=False, with_cand=False,
+                          out_idx=None, out_score=None, workspace=None) -> Dict[str, torch.Tensor]:
+    """MISA (k_prime == 0) or MISA dagger (k_prime >= top_k).  Returns a dict with
+    "idx", "score" and, if asked, "heads", "importance", "cand"."""
+    dev, nq, H, d, n_seq, l_max = _common(q, w, k, q_pos, q_seq)
+    if q.dtype != torch.bfloat16:
+        raise TypeError("MISA takes bf16 inputs")
+    if k_pooled is not None:
+        _need(k_pooled, "k_pooled", torch.bfloat16, 3, dev)
+        if tuple(k_pooled.shape) != (n_seq, -(-l_max // block), d):
+            raise ValueError("k_pooled must be [n_seq, ceil(l_max/block), d]")
+    out_idx, out_score = _outputs(dev, nq, top_k, out_idx, out_score, with_scores)
+    heads = torch.empty((nq, n_active_heads), dtype=torch.int32, device=dev) if with_heads else None
+    imp = torch.empty((nq, H), dtype=torch.float32, device=dev) if with_importance else None
+    cand = (torch.empty((nq, k_prime), dtype=torch.int32, device=dev)
+            if (with_cand and k_prime > 0) else None)
+    nbytes = misa_route_score_topk_workspace_size(nq, H, d, n_seq, l_max, block, n_active_heads,
+                                                  k_prime, top_k, k_pooled is not None)
+    ws = _workspace(nbytes, dev, workspace)
+    st = lib().misa_route_score_topk(_ptr(q), _ptr(w), _ptr(k), _ptr(k_pooled), DSA_DTYPE_BF16,
+                                     _ptr(q_seq), _ptr(q_pos), nq, H, d, n_seq, l_max, block,
+                                     n_active_heads, k_prime, top_k, _ptr(out_idx),
+                                     _ptr(out_score), _ptr(heads), _ptr(imp), _ptr(cand), _ptr(ws),
+                                     nbytes, _stream(dev))
+    _check(st, "misa_route_score_topk")
+    out = {"idx": out_idx, "score": out_score}
+    if heads is not None:
+        out["heads"] = heads
+    if imp is not None:
+        out["importance"] = imp
+    if cand is not None:
+        out["cand"] = cand
+    return out
+
+
+def hisa_block_filter_topk_workspace_size(nq, n_heads, head_dim, n_seq, l_max, block, m_blocks,
+                                          top_k, pooled_given) -> int:
+    return int(lib().hisa_block_filter_topk_workspace_size(nq, n_heads, head_dim, n_seq, l_max,
+                                                           block, m_blocks, top_k,
+                                                           int(bool(pooled_given))))
+
+
+def hisa_block_filter_topk(q, w, k, q_pos, q_seq=None, *, block: int, m_blocks: int, top_k: int,
+                           k_pooled=None, with_scores=True, with_blocks=True, out_idx=None,
+                           out_score=None, workspace=None) -> Dict[str, torch.Tensor]:
+    """HISA: top-m pooled blocks, then top_k tokens inside them.  Returns a dict
+    with "idx", "score" and, if asked, "blocks" and "block_score"."""
+    dev, nq, H, d, n_seq, l_max = _common(q, w, k, q_pos, q_seq)
+    if q.dtype != torch.bfloat16:
+        raise TypeError("HISA takes bf16 inputs")
+    if k_pooled is not None:
+        _need(k_pooled, "k_pooled", torch.bfloat16, 3, dev)
+        if tuple(k_pooled.shape) != (n_seq, -(-l_max // block), d):
+            raise ValueError("k_pooled must be [n_seq, ceil(l_max/block), d]")
+    out_idx, out_score = _outputs(dev, nq, top_k, out_idx, out_score, with_scores)
+    blocks = torch.empty((nq, m_blocks), dtype=torch.int32, device=dev) if with_blocks else None
+    bscore = torch.empty((nq, m_blocks), dtype=torch.float32, device=dev) if with_blocks else None
+    nbytes = hisa_block_filter_topk_workspace_size(nq, H, d, n_seq, l_max, block, m_blocks, top_k,
+                                                   k_pooled is not None)
+    ws = _workspace(nbytes, dev, workspace)
+    st = lib().hisa_block_filter_topk(_ptr(q), _ptr(w), _ptr(k), _ptr(k_pooled), DSA_DTYPE_BF16,
+                                      _ptr(q_seq), _ptr(q_pos), nq, H, d, n_seq, l_max, block,
+                                      m_blocks, top_k, _ptr(out_idx), _ptr(out_score),
+                                      _ptr(blocks), _ptr(bscore), _ptr(ws), nbytes, _stream(dev))
+    _check(st, "hisa_block_filter_topk")
+    out = {"idx": out_idx, "score": out_score}
+    if blocks is not None:
+        out["blocks"] = blocks
+        out["block_score"] = bscore
+    return out
+
+
+def indexer_selection_iou(a: torch.Tensor, b: torch.Tensor,
+                          out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Per-row IoU of two [nq, k] int32 selections (padding -1 ignored)."""
+    _need(a, "a", torch.int32, 2)
+    _need(b, "b", torch.int32, 2, a.device)
+    if a.shape != b.shape:
+        raise ValueError("a and b must have the same shape")
+    nq, k = a.shape
+    if out is None:
+        out = torch.empty(nq, dtype=torch.float32, device=a.device)
+    st = lib().indexer_selection_iou(_ptr(a), _ptr(b), nq, k, _ptr(out), _stream(a.device))
+    _check(st, "indexer_selection_iou")
+    return out
+
+
+__all__ = [
+    "DsaError", "LIB_PATH", "lib", "DSA_DTYPE_BF16", "DSA_DTYPE_F32",
+    "indexer_score_topk", "indexer_score_topk_workspace_size",
+    "indexer_mean_pool_keys",
+    "misa_route_score_topk", "misa_route_score_topk_workspace_size",
+    "hisa_block_filter_topk", "hisa_block_filter_topk_workspace_size",
+    "indexer_selection_iou",
+]

@@ -1,0 +1,477 @@
+// C-ABI layer: argument validation, workspace planning and kernel dispatch.
+// Declarations and the contract of every entry point are in include/dsa_indexer.h.
+#include "../../include/dsa_indexer.h"
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <string>
+
+#include "dsa_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+bool debug_sync() {
+  static const int on = [] {
+    const char* e = getenv("DSA_DEBUG");
+    return e && e[0] && e[0] != '0' ? 1 : 0;
+  }();
+  return on != 0;
+}
+
+int hip_status(hipError_t e, const char* what, hipStream_t stream) {
+  if (e != hipSuccess) return fail(DSA_EHIP, "%s: %s", what, hipGetErrorString(e));
+  if (debug_sync()) {
+    e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return fail(DSA_EHIP, "%s (DSA_DEBUG sync): %s", what, hipGetErrorString(e));
+  }
+  return DSA_OK;
+}
+
+constexpr int kBins = 4096;
+constexpr int kMaxChunk = 8192;
+constexpr int kMinChunk = 256;
+constexpr int64_t kTargetWorkgroups = 512;   // >= 2 per compute unit on MI355X
+constexpr size_t kMaxLds = 64 * 1024;
+constexpr int kMaxTopK = 1 << 20;
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct Arena {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    size_t o = off;
+    off += align256(bytes);
+    return o;
+  }
+};
+
+struct StagePlan {
+  int chunk = 0, n_chunks = 0;
+  size_t ghist = 0, counter = 0, nvalid = 0, cand = 0, cnt = 0;
+};
+
+// largest power-of-two chunk (<= the LDS limit) that still gives about
+// kTargetWorkgroups workgroups over the call
+int choose_chunk(int64_t n_items, int64_t nq, int f32, int head_dim) {
+  int chunk = kMaxChunk;
+  while (chunk > kMinChunk &&
+         dsa::score_select_lds_bytes(chunk, f32, head_dim) > kMaxLds)
+    chunk >>= 1;
+  while (chunk > kMinChunk && nq * cdiv(n_items, chunk) < kTargetWorkgroups) chunk >>= 1;
+  return chunk;
+}
+
+void plan_zero(Arena& A, StagePlan& s, int64_t nq) {
+  s.ghist = A.take((size_t)nq * kBins * 4);
+  s.counter = A.take((size_t)nq * 4);
+  s.nvalid = A.take((size_t)nq * 4);
+}
+
+void plan_cand(Arena& A, StagePlan& s, int64_t nq, int64_t n_items, int f32, int head_dim) {
+  s.chunk = choose_chunk(n_items, nq, f32, head_dim);
+  s.n_chunks = (int)cdiv(n_items, s.chunk);
+  s.cand = A.take((size_t)nq * s.n_chunks * s.chunk * 8);
+  s.cnt = A.take((size_t)nq * s.n_chunks * 4);
+}
+
+template <class T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(reinterpret_cast<char*>(ws) + off);
+}
+
+dsa::SelArgs stage_args(const StagePlan& s, void* ws) {
+  dsa::SelArgs a{};
+  a.chunk = s.chunk;
+  a.n_chunks = s.n_chunks;
+  a.cand = at<uint2>(ws, s.cand);
+  a.cand_cnt = at<uint32_t>(ws, s.cnt);
+  a.ghist = at<uint32_t>(ws, s.ghist);
+  a.counter = at<uint32_t>(ws, s.counter);
+  a.nvalid = at<uint32_t>(ws, s.nvalid);
+  return a;
+}
+
+int check_common(const void* q, const float* w, const void* k, int32_t dtype, const int32_t* q_pos,
+                 int32_t nq, int32_t n_heads, int32_t head_dim, int32_t n_seq, int64_t l_max,
+                 int32_t top_k, const int32_t* out_idx) {
+  if (nq < 0) return fail(DSA_EINVAL, "nq must be >= 0 (got %d)", nq);
+  if (dtype != DSA_DTYPE_BF16 && dtype != DSA_DTYPE_F32)
+    return fail(DSA_EINVAL, "dtype must be DSA_DTYPE_BF16 or DSA_DTYPE_F32 (got %d)", dtype);
+  if (n_heads < 1 || n_heads > 64) return fail(DSA_EUNSUPPORTED, "n_heads must be in [1, 64] (got %d)", n_heads);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(DSA_EUNSUPPORTED, "head_dim must be 64 or 128 (got %d)", head_dim);
+  if (n_seq < 1) return fail(DSA_EINVAL, "n_seq must be >= 1 (got %d)", n_seq);
+  if (l_max < 1 || l_max > 0x7FFFFFFF) return fail(DSA_EINVAL, "l_max must be in [1, 2^31) (got %lld)", (long long)l_max);
+  if (top_k < 1 || top_k > kMaxTopK) return fail(DSA_EINVAL, "top_k must be in [1, %d] (got %d)", kMaxTopK, top_k);
+  if (nq == 0) return DSA_OK;
+  if (!q || !w || !k || !q_pos || !out_idx)
+    return fail(DSA_EINVAL, "q, w, k, q_pos and out_idx must not be NULL");
+  if (!aligned(q, 16) || !aligned(k, 16)) return fail(DSA_EINVAL, "q and k must be 16-byte aligned");
+  if (!aligned(w, 4) || !aligned(q_pos, 4) || !aligned(out_idx, 4))
+    return fail(DSA_EINVAL, "w, q_pos and out_idx must be 4-byte aligned");
+  return DSA_OK;
+}
+
+int check_ws(void* ws, size_t have, size_t need) {
+  if (have < need)
+    return fail(DSA_EWORKSPACE, "workspace too small: %zu bytes given, %zu needed", have, need);
+  if (need && (!ws || !aligned(ws, 256))) return fail(DSA_EINVAL, "workspace must be non-NULL and 256-byte aligned");
+  return DSA_OK;
+}
+
+// ---------------------------------------------------------------- dense ----
+
+struct DensePlan {
+  StagePlan s;
+  size_t zero_bytes = 0, total = 0;
+};
+
+DensePlan plan_dense(int64_t nq, int head_dim, int64_t l_max, int f32) {
+  DensePlan p;
+  Arena A;
+  plan_zero(A, p.s, nq);
+  p.zero_bytes = A.off;
+  plan_cand(A, p.s, nq, l_max, f32, head_dim);
+  p.total = A.off;
+  return p;
+}
+
+// ----------------------------------------------------------------- MISA ----
+
+struct MisaPlan {
+  StagePlan s0, s1;
+  size_t route_counter = 0, zero_bytes = 0, part = 0, heads = 0, cand_list = 0, partial = 0, pooled = 0;
+  size_t total = 0;
+  int splits = 1, bps = 1;
+  int64_t m_max = 0;
+};
+
+MisaPlan plan_misa(int64_t nq, int n_heads, int head_dim, int n_seq, int64_t l_max, int block, int h,
+                   int k_prime, bool pooled_given) {
+  MisaPlan p;
+  Arena A;
+  p.m_max = cdiv(l_max, block);
+  plan_zero(A, p.s0, nq);
+  if (k_prime > 0) plan_zero(A, p.s1, nq);
+  p.route_counter = A.take((size_t)nq * 4);
+  p.zero_bytes = A.off;
+  // router: about kTargetWorkgroups workgroups, at least 64 blocks each
+  int64_t bps = 64;
+  while (nq * cdiv(p.m_max, bps) > kTargetWorkgroups) bps *= 2;
+  p.bps = (int)bps;
+  p.splits = (int)cdiv(p.m_max, bps);
+  p.part = A.take((size_t)nq * p.splits * n_heads * 4);
+  p.heads = A.take((size_t)nq * h * 4);
+  plan_cand(A, p.s0, nq, l_max, 0, head_dim);
+  if (k_prime > 0) {
+    p.cand_list = A.take((size_t)nq * k_prime * 4);
+    plan_cand(A, p.s1, nq, k_prime, 0, head_dim);
+  }
+  p.partial = A.take((size_t)nq * head_dim * 2);
+  if (!pooled_given) p.pooled = A.take((size_t)n_seq * p.m_max * head_dim * 2);
+  p.total = A.off;
+  return p;
+}
+
+// ----------------------------------------------------------------- HISA ----
+
+struct HisaPlan {
+  StagePlan s0, s1;
+  size_t zero_bytes = 0, blocks = 0, partial = 0, pooled = 0, total = 0;
+  int64_t m_max = 0;
+};
+
+HisaPlan plan_hisa(int64_t nq, int head_dim, int n_seq, int64_t l_max, int block, int m,
+                   bool pooled_given) {
+  HisaPlan p;
+  Arena A;
+  p.m_max = cdiv(l_max, block);
+  plan_zero(A, p.s0, nq);
+  plan_zero(A, p.s1, nq);
+  p.zero_bytes = A.off;
+  plan_cand(A, p.s0, nq, p.m_max, 0, head_dim);
+  p.blocks = A.take((size_t)nq * m * 4);
+  plan_cand(A, p.s1, nq, (int64_t)m * block, 0, head_dim);
+  p.partial = A.take((size_t)nq * head_dim * 2);
+  if (!pooled_given) p.pooled = A.take((size_t)n_seq * p.m_max * head_dim * 2);
+  p.total = A.off;
+  return p;
+}
+
+int run_prepare(void* ws, size_t zero_bytes, const void* k, const int32_t* q_seq,
+                const int32_t* q_pos, int nq, int n_seq, int head_dim, int block, int64_t l_max,
+                uint16_t* partial, hipStream_t stream) {
+  dsa::PrepArgs pa{};
+  pa.zero = at<uint32_t>(ws, 0);
+  pa.zero_words = zero_bytes / 4;
+  pa.keys = reinterpret_cast<const uint16_t*>(k);
+  pa.q_seq = q_seq;
+  pa.q_pos = q_pos;
+  pa.nq = nq;
+  pa.n_seq = n_seq;
+  pa.head_dim = head_dim;
+  pa.block = block;
+  pa.l_max = l_max;
+  pa.partial = partial;
+  return hip_status(dsa::launch_prepare(pa, stream), "prepare kernel", stream);
+}
+
+void fill_common(dsa::SelArgs& a, const void* q, const float* w, const void* k,
+                 const int32_t* q_seq, const int32_t* q_pos, int nq, int n_heads, int head_dim,
+                 int n_seq, int64_t l_max) {
+  a.q = q;
+  a.w = w;
+  a.keys = k;
+  a.q_seq = q_seq;
+  a.q_pos = q_pos;
+  a.nq = nq;
+  a.n_heads = n_heads;
+  a.h_use = n_heads;
+  a.head_dim = head_dim;
+  a.n_seq = n_seq;
+  a.l_max = l_max;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dsa_last_error(void) { return g_err.c_str(); }
+
+int dsa_abi_version(void) { return 1; }
+
+size_t indexer_score_topk_workspace_size(int32_t nq, int32_t n_heads, int32_t head_dim,
+                                         int32_t n_seq, int64_t l_max, int32_t top_k,
+                                         int32_t dtype) {
+  (void)n_heads; (void)n_seq; (void)top_k;
+  if (nq <= 0 || l_max <= 0) return 0;
+  return plan_dense(nq, head_dim, l_max, dtype == DSA_DTYPE_F32).total;
+}
+
+int indexer_score_topk(const void* q, const float* w, const void* k, int32_t dtype,
+                       const int32_t* q_seq, const int32_t* q_pos, int32_t nq, int32_t n_heads,
+                       int32_t head_dim, int32_t n_seq, int64_t l_max, int32_t top_k,
+                       int32_t* out_idx, float* out_score, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  int st = check_common(q, w, k, dtype, q_pos, nq, n_heads, head_dim, n_seq, l_max, top_k, out_idx);
+  if (st || nq == 0) return st;
+  const int f32 = dtype == DSA_DTYPE_F32;
+  DensePlan p = plan_dense(nq, head_dim, l_max, f32);
+  if ((st = check_ws(workspace, workspace_bytes, p.total))) return st;
+  if ((st = run_prepare(workspace, p.zero_bytes, k, q_seq, q_pos, nq, n_seq, head_dim, 1, l_max,
+                        nullptr, stream)))
+    return st;
+  dsa::SelArgs a = stage_args(p.s, workspace);
+  fill_common(a, q, w, k, q_seq, q_pos, nq, n_heads, head_dim, n_seq, l_max);
+  a.f32 = f32;
+  a.mode = dsa::MODE_RANGE;
+  a.top_k = top_k;
+  a.out_idx = out_idx;
+  a.out_score = out_score;
+  return hip_status(dsa::launch_score_select(a, stream), "score/select kernel", stream);
+}
+
+int indexer_mean_pool_keys(const void* k, int32_t dtype, int32_t n_seq, int64_t l_max,
+                           int32_t head_dim, int32_t block, void* k_pooled, hipStream_t stream) {
+  if (dtype != DSA_DTYPE_BF16) return fail(DSA_EUNSUPPORTED, "pooling supports bf16 keys only");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(DSA_EUNSUPPORTED, "head_dim must be 64 or 128 (got %d)", head_dim);
+  if (n_seq < 0 || l_max < 0 || l_max > 0x7FFFFFFF) return fail(DSA_EINVAL, "bad n_seq / l_max");
+  if (block < 1) return fail(DSA_EINVAL, "block must be >= 1 (got %d)", block);
+  if (n_seq == 0 || l_max == 0) return DSA_OK;
+  if (!k || !k_pooled) return fail(DSA_EINVAL, "k and k_pooled must not be NULL");
+  if (!aligned(k, 16) || !aligned(k_pooled, 16)) return fail(DSA_EINVAL, "k and k_pooled must be 16-byte aligned");
+  return hip_status(dsa::launch_mean_pool(reinterpret_cast<const uint16_t*>(k), n_seq, l_max,
+                                          head_dim, block, reinterpret_cast<uint16_t*>(k_pooled),
+                                          stream),
+                    "mean-pool kernel", stream);
+}
+
+size_t misa_route_score_topk_workspace_size(int32_t nq, int32_t n_heads, int32_t head_dim,
+                                            int32_t n_seq, int64_t l_max, int32_t block,
+                                            int32_t n_active_heads, int32_t k_prime,
+                                            int32_t top_k, int32_t pooled_given) {
+  (void)top_k;
+  if (nq <= 0 || l_max <= 0 || block <= 0 || n_active_heads <= 0) return 0;
+  return plan_misa(nq, n_heads, head_dim, n_seq, l_max, block, n_active_heads, k_prime,
+                   pooled_given != 0).total;
+}
+
+int misa_route_score_topk(const void* q, const float* w, const void* k, const void* k_pooled,
+                          int32_t dtype, const int32_t* q_seq, const int32_t* q_pos, int32_t nq,
+                          int32_t n_heads, int32_t head_dim, int32_t n_seq, int64_t l_max,
+                          int32_t block, int32_t n_active_heads, int32_t k_prime, int32_t top_k,
+                          int32_t* out_idx, float* out_score, int32_t* out_heads,
+                          float* out_importance, int32_t* out_cand, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  int st = check_common(q, w, k, dtype, q_pos, nq, n_heads, head_dim, n_seq, l_max, top_k, out_idx);
+  if (st) return st;
+  if (dtype != DSA_DTYPE_BF16) return fail(DSA_EUNSUPPORTED, "MISA supports bf16 inputs only");
+  if (block < 1) return fail(DSA_EINVAL, "block must be >= 1 (got %d)", block);
+  if (n_active_heads < 1 || n_active_heads > n_heads)
+    return fail(DSA_EINVAL, "n_active_heads must be in [1, n_heads] (got %d)", n_active_heads);
+  if (k_prime != 0 && (k_prime < top_k || k_prime > kMaxTopK))
+    return fail(DSA_EINVAL, "k_prime must be 0 or in [top_k, %d] (got %d)", kMaxTopK, k_prime);
+  if (nq == 0) return DSA_OK;
+  if (k_pooled && !aligned(k_pooled, 16)) return fail(DSA_EINVAL, "k_pooled must be 16-byte aligned");
+  MisaPlan p = plan_misa(nq, n_heads, head_dim, n_seq, l_max, block, n_active_heads, k_prime,
+                         k_pooled != nullptr);
+  if ((st = check_ws(workspace, workspace_bytes, p.total))) return st;
+  const uint16_t* pooled = reinterpret_cast<const uint16_t*>(k_pooled);
+  if (!pooled) {
+    uint16_t* dst = at<uint16_t>(workspace, p.pooled);
+    st = hip_status(dsa::launch_mean_pool(reinterpret_cast<const uint16_t*>(k), n_seq, l_max,
+                                          head_dim, block, dst, stream),
+                    "mean-pool kernel", stream);
+    if (st) return st;
+    pooled = dst;
+  }
+  uint16_t* partial = at<uint16_t>(workspace, p.partial);
+  if ((st = run_prepare(workspace, p.zero_bytes, k, q_seq, q_pos, nq, n_seq, head_dim, block,
+                        l_max, partial, stream)))
+    return st;
+  // router
+  dsa::RouteArgs ra{};
+  ra.q = reinterpret_cast<const uint16_t*>(q);
+  ra.w = w;
+  ra.pooled = pooled;
+  ra.partial = partial;
+  ra.q_seq = q_seq;
+  ra.q_pos = q_pos;
+  ra.nq = nq;
+  ra.n_heads = n_heads;
+  ra.head_dim = head_dim;
+  ra.n_seq = n_seq;
+  ra.block = block;
+  ra.h = n_active_heads;
+  ra.splits = p.splits;
+  ra.blocks_per_split = p.bps;
+  ra.l_max = l_max;
+  ra.m_max = p.m_max;
+  ra.part = at<float>(workspace, p.part);
+  ra.counter = at<uint32_t>(workspace, p.route_counter);
+  ra.heads = at<int32_t>(workspace, p.heads);
+  ra.out_heads = out_heads;
+  ra.out_importance = out_importance;
+  if ((st = hip_status(dsa::launch_route(ra, stream), "router kernel", stream))) return st;
+  // routed token pass
+  dsa::SelArgs a = stage_args(p.s0, workspace);
+  fill_common(a, q, w, k, q_seq, q_pos, nq, n_heads, head_dim, n_seq, l_max);
+  a.h_use = n_active_heads;
+  a.heads = ra.heads;
+  a.heads_stride = n_active_heads;
+  a.mode = dsa::MODE_RANGE;
+  if (k_prime == 0) {
+    a.top_k = top_k;
+    a.out_idx = out_idx;
+    a.out_score = out_score;
+    return hip_status(dsa::launch_score_select(a, stream), "routed score/select kernel", stream);
+  }
+  int32_t* cand = out_cand ? out_cand : at<int32_t>(workspace, p.cand_list);
+  a.top_k = k_prime;
+  a.out_idx = cand;
+  a.out_score = nullptr;
+  if ((st = hip_status(dsa::launch_score_select(a, stream), "routed score/select kernel", stream)))
+    return st;
+  // all-head rescoring of the k' candidates
+  dsa::SelArgs b = stage_args(p.s1, workspace);
+  fill_common(b, q, w, k, q_seq, q_pos, nq, n_heads, head_dim, n_seq, l_max);
+  b.mode = dsa::MODE_LIST;
+  b.list = cand;
+  b.list_len = k_prime;
+  b.top_k = top_k;
+  b.out_idx = out_idx;
+  b.out_score = out_score;
+  return hip_status(dsa::launch_score_select(b, stream), "rescore/select kernel", stream);
+}
+
+size_t hisa_block_filter_topk_workspace_size(int32_t nq, int32_t n_heads, int32_t head_dim,
+                                             int32_t n_seq, int64_t l_max, int32_t block,
+                                             int32_t m_blocks, int32_t top_k,
+                                             int32_t pooled_given) {
+  (void)n_heads; (void)top_k;
+  if (nq <= 0 || l_max <= 0 || block <= 0 || m_blocks <= 0) return 0;
+  return plan_hisa(nq, head_dim, n_seq, l_max, block, m_blocks, pooled_given != 0).total;
+}
+
+int hisa_block_filter_topk(const void* q, const float* w, const void* k, const void* k_pooled,
+                           int32_t dtype, const int32_t* q_seq, const int32_t* q_pos, int32_t nq,
+                           int32_t n_heads, int32_t head_dim, int32_t n_seq, int64_t l_max,
+                           int32_t block, int32_t m_blocks, int32_t top_k, int32_t* out_idx,
+                           float* out_score, int32_t* out_blocks, float* out_block_score,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_common(q, w, k, dtype, q_pos, nq, n_heads, head_dim, n_seq, l_max, top_k, out_idx);
+  if (st) return st;
+  if (dtype != DSA_DTYPE_BF16) return fail(DSA_EUNSUPPORTED, "HISA supports bf16 inputs only");
+  if (block < 1) return fail(DSA_EINVAL, "block must be >= 1 (got %d)", block);
+  if (m_blocks < 1 || m_blocks > kMaxTopK) return fail(DSA_EINVAL, "m_blocks must be in [1, %d] (got %d)", kMaxTopK, m_blocks);
+  if ((int64_t)m_blocks * block > 0x7FFFFFFF) return fail(DSA_EINVAL, "m_blocks * block too large");
+  if (nq == 0) return DSA_OK;
+  if (k_pooled && !aligned(k_pooled, 16)) return fail(DSA_EINVAL, "k_pooled must be 16-byte aligned");
+  HisaPlan p = plan_hisa(nq, head_dim, n_seq, l_max, block, m_blocks, k_pooled != nullptr);
+  if ((st = check_ws(workspace, workspace_bytes, p.total))) return st;
+  const uint16_t* pooled = reinterpret_cast<const uint16_t*>(k_pooled);
+  if (!pooled) {
+    uint16_t* dst = at<uint16_t>(workspace, p.pooled);
+    st = hip_status(dsa::launch_mean_pool(reinterpret_cast<const uint16_t*>(k), n_seq, l_max,
+                                          head_dim, block, dst, stream),
+                    "mean-pool kernel", stream);
+    if (st) return st;
+    pooled = dst;
+  }
+  uint16_t* partial = at<uint16_t>(workspace, p.partial);
+  if ((st = run_prepare(workspace, p.zero_bytes, k, q_seq, q_pos, nq, n_seq, head_dim, block,
+                        l_max, partial, stream)))
+    return st;
+  // stage 1: block scores over the pooled keys, top-m blocks
+  int32_t* blocks = out_blocks ? out_blocks : at<int32_t>(workspace, p.blocks);
+  dsa::SelArgs a = stage_args(p.s0, workspace);
+  fill_common(a, q, w, k, q_seq, q_pos, nq, n_heads, head_dim, n_seq, l_max);
+  a.mode = dsa::MODE_POOLED;
+  a.pooled = pooled;
+  a.partial = partial;
+  a.m_max = p.m_max;
+  a.block = block;
+  a.top_k = m_blocks;
+  a.out_idx = blocks;
+  a.out_score = out_block_score;
+  if ((st = hip_status(dsa::launch_score_select(a, stream), "block score/select kernel", stream)))
+    return st;
+  // stage 2: token refinement inside the surviving blocks
+  dsa::SelArgs b = stage_args(p.s1, workspace);
+  fill_common(b, q, w, k, q_seq, q_pos, nq, n_heads, head_dim, n_seq, l_max);
+  b.mode = dsa::MODE_BLOCKS;
+  b.list = blocks;
+  b.list_len = m_blocks;
+  b.block = block;
+  b.top_k = top_k;
+  b.out_idx = out_idx;
+  b.out_score = out_score;
+  return hip_status(dsa::launch_score_select(b, stream), "refine score/select kernel", stream);
+}
+
+int indexer_selection_iou(const int32_t* a, const int32_t* b, int32_t nq, int32_t k,
+                          float* out_iou, hipStream_t stream) {
+  if (nq < 0) return fail(DSA_EINVAL, "nq must be >= 0");
+  if (k < 1 || k > 8192) return fail(DSA_EUNSUPPORTED, "k must be in [1, 8192] (got %d)", k);
+  if (nq == 0) return DSA_OK;
+  if (!a || !b || !out_iou) return fail(DSA_EINVAL, "a, b and out_iou must not be NULL");
+  return hip_status(dsa::launch_iou(a, b, nq, k, out_iou, stream), "IoU kernel", stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,86 @@
+// Internal (host-side) interfaces between the C-ABI layer and the kernel
+// translation units.  Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+enum ItemMode { MODE_RANGE = 0, MODE_POOLED = 1, MODE_LIST = 2, MODE_BLOCKS = 3 };
+
+// Arguments of one score-and-select pass.  One workgroup scores `chunk` items of
+// one query; items are mapped to key rows by `mode`:
+//   RANGE   item u = token u of the query's sequence, u = 0..pos
+//   POOLED  item b = pooled block b, b = 0..ceil((pos+1)/block)-1; the partial
+//           last block (if any) is read from `partial` instead of `pooled`
+//   LIST    item i = token list[t][i] (entries < 0 or > pos are skipped)
+//   BLOCKS  item i = token list[t][i / block] * block + i % block (same rule)
+struct SelArgs {
+  const void* q;               // [nq, n_heads, D] bf16 bits or f32
+  const float* w;              // [nq, n_heads]
+  const void* keys;            // [n_seq, l_max, D]
+  const uint16_t* pooled;      // [n_seq, m_max, D] bf16 (POOLED)
+  const uint16_t* partial;     // [nq, D] bf16 (POOLED), may be null
+  const int32_t* q_seq;        // [nq] or null (all 0)
+  const int32_t* q_pos;        // [nq]
+  const int32_t* heads;        // [nq, heads_stride] routed heads, or null = all
+  const int32_t* list;         // LIST / BLOCKS
+  int nq, n_heads, h_use, heads_stride, head_dim, n_seq;
+  int64_t l_max, m_max;
+  int block, list_len, top_k, chunk, n_chunks;
+  int f32;                     // inputs are float32
+  int mode;
+  // workspace
+  uint2* cand;                 // [nq, n_chunks, chunk]
+  uint32_t* cand_cnt;          // [nq, n_chunks]
+  uint32_t* ghist;             // [nq, 4096]   (zeroed before the pass)
+  uint32_t* counter;           // [nq]         (zeroed before the pass)
+  uint32_t* nvalid;            // [nq]         (zeroed before the pass)
+  // outputs
+  int32_t* out_idx;            // [nq, top_k]
+  float* out_score;            // [nq, top_k] or null
+};
+
+hipError_t launch_score_select(const SelArgs& a, hipStream_t stream);
+size_t score_select_lds_bytes(int chunk, int f32, int head_dim);
+
+// Clears `zero_words` 32-bit words at `zero` and, if `partial` is given, pools
+// the partial last block of every query whose prefix does not end on a block
+// boundary (mean over its valid tokens, rounded once to bf16).
+struct PrepArgs {
+  uint32_t* zero;
+  size_t zero_words;
+  const uint16_t* keys;        // [n_seq, l_max, D] bf16
+  const int32_t* q_seq;
+  const int32_t* q_pos;
+  int nq, n_seq, head_dim, block;
+  int64_t l_max;
+  uint16_t* partial;           // [nq, D] or null
+};
+hipError_t launch_prepare(const PrepArgs& a, hipStream_t stream);
+
+hipError_t launch_mean_pool(const uint16_t* k, int n_seq, int64_t l_max, int head_dim, int block,
+                            uint16_t* out, hipStream_t stream);
+
+// MISA router: per-head importance from pooled keys and top-h head selection.
+struct RouteArgs {
+  const uint16_t* q;           // [nq, n_heads, D]
+  const float* w;              // [nq, n_heads]
+  const uint16_t* pooled;      // [n_seq, m_max, D]
+  const uint16_t* partial;     // [nq, D] or null
+  const int32_t* q_seq;
+  const int32_t* q_pos;
+  int nq, n_heads, head_dim, n_seq, block, h, splits, blocks_per_split;
+  int64_t l_max, m_max;
+  float* part;                 // [nq, splits, n_heads] workspace
+  uint32_t* counter;           // [nq] (zeroed)
+  int32_t* heads;              // [nq, h] (workspace)
+  int32_t* out_heads;          // [nq, h] or null
+  float* out_importance;       // [nq, n_heads] or null
+};
+hipError_t launch_route(const RouteArgs& a, hipStream_t stream);
+
+hipError_t launch_iou(const int32_t* a, const int32_t* b, int nq, int k, float* out,
+                      hipStream_t stream);
+
+}  // namespace dsa

@@ -1,0 +1,159 @@
+// MISA router: per-head importance from the mean-pooled block keys and the
+// top-h head set of each query.
+//
+// MISA summary, "method" step 1: the router computes per-head affinities
+// against pooled block-level keys instead of individual tokens, aggregates them
+// into an importance per head for the current query and keeps the top-h heads;
+// it touches only M = ceil(L/B) pooled keys, so its cost is O(H_I M).
+// Reading taken where the page gives no formula: affinity = max(0, q_j . kbar_b),
+// importance I_j = |w_j| * sum_b affinity, ties to the lower head index.
+//
+// One workgroup = one query x one slice of its blocks; bf16 MFMA with heads as
+// rows and pooled blocks as columns, the ReLU'd affinities summed per head in
+// registers, then across lanes and waves in a fixed order.  The last workgroup
+// of a query (arrival counter) adds the slices in slice order, weights by |w|
+// and ranks the heads.
+#include "dsa_internal.h"
+#include "dsa_common.h"
+
+namespace dsa {
+
+namespace {
+
+constexpr int kRT = 256;
+
+template <int HT, int D>
+__global__ __launch_bounds__(kRT) void k_route(RouteArgs a) {
+  constexpr int S = D / 16;
+  __shared__ float s_part[kRT / 64][64];
+  __shared__ float s_I[64];
+  __shared__ int s_last;
+  const int t = blockIdx.y, sp = blockIdx.x;
+  const int lane = lane_id(), wv = wave_id(), h = lane >> 5, n = lane & 31;
+  const int seq = a.q_seq ? a.q_seq[t] : 0;
+  const int64_t pos = a.q_pos[t];
+  const bool ok = seq >= 0 && seq < a.n_seq && pos >= 0 && pos < a.l_max;
+  const int64_t M = ok ? (pos + a.block) / a.block : 0;
+  const int64_t b0 = (int64_t)sp * a.blocks_per_split;
+  const int64_t b1 = (b0 + a.blocks_per_split) < M ? (b0 + a.blocks_per_split) : M;
+  const bool partial_last = a.partial && ok && ((pos + 1) % a.block) != 0;
+
+  float hsum[HT][16];
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) hsum[ht][r] = 0.f;
+
+  if (b0 < b1) {
+    bf16x8 qa[HT][S];
+    const uint16_t* q_t = a.q + (size_t)t * a.n_heads * D;
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      const int row = ht * 32 + n;
+#pragma unroll
+      for (int s = 0; s < S; ++s)
+        qa[ht][s] = row < a.n_heads ? load_bf16x8(q_t + (size_t)row * D + h * (D / 2) + 8 * s)
+                                    : zero_bf16x8();
+    }
+    const int n_tiles = (int)((b1 - b0 + 31) / 32);
+    for (int tile = wv; tile < n_tiles; tile += kRT / 64) {
+      const int64_t b = b0 + (int64_t)tile * 32 + n;
+      const bool valid = b < b1;
+      const int64_t bb = valid ? b : b0;
+      const uint16_t* rowp = (partial_last && bb == M - 1)
+                                 ? a.partial + (size_t)t * D
+                                 : a.pooled + ((size_t)seq * (size_t)a.m_max + (size_t)bb) * D;
+      bf16x8 kb[S];
+#pragma unroll
+      for (int s = 0; s < S; ++s) kb[s] = load_bf16x8(rowp + h * (D / 2) + 8 * s);
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) {
+        f32x16 acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+        for (int s = 0; s < S; ++s)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ht][s], kb[s], acc, 0, 0, 0);
+        if (valid) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) hsum[ht][r] += relu(acc[r]);
+        }
+      }
+    }
+  }
+  // sum over the 32 block columns held by lanes with the same half h
+#pragma unroll
+  for (int m = 1; m < 32; m <<= 1)
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) hsum[ht][r] += shfl_xor_f(hsum[ht][r], m);
+  if (n == 0) {
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s_part[wv][ht * 32 + 8 * (r >> 2) + 4 * h + (r & 3)] = hsum[ht][r];
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < a.n_heads; j += kRT) {
+    float p = 0.f;
+    for (int w = 0; w < kRT / 64; ++w) p += s_part[w][j];
+    a.part[((size_t)t * a.splits + sp) * a.n_heads + j] = p;
+  }
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t done = atomicAdd(a.counter + t, 1u);
+    s_last = done == (uint32_t)(a.splits - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  for (int j = threadIdx.x; j < a.n_heads; j += kRT) {
+    float tot = 0.f;
+    for (int s = 0; s < a.splits; ++s)
+      tot += __hip_atomic_load(a.part + ((size_t)t * a.splits + s) * a.n_heads + j,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    float I = fabsf(a.w[(size_t)t * a.n_heads + j]) * tot;
+    s_I[j] = I;
+    if (a.out_importance) a.out_importance[(size_t)t * a.n_heads + j] = I;
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < a.n_heads; j += kRT) {
+    if (!ok) {
+      if (j < a.h) {
+        a.heads[(size_t)t * a.h + j] = j;
+        if (a.out_heads) a.out_heads[(size_t)t * a.h + j] = -1;
+      }
+      continue;
+    }
+    const float Ij = s_I[j];
+    int rank = 0;
+    for (int i = 0; i < a.n_heads; ++i) {
+      const float Ii = s_I[i];
+      rank += (Ii > Ij) || (Ii == Ij && i < j);
+    }
+    if (rank < a.h) {
+      a.heads[(size_t)t * a.h + rank] = j;
+      if (a.out_heads) a.out_heads[(size_t)t * a.h + rank] = j;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
+  dim3 grid(a.splits, a.nq);
+  if (a.head_dim == 128) {
+    if (a.n_heads <= 32) hipLaunchKernelGGL((k_route<1, 128>), grid, dim3(kRT), 0, stream, a);
+    else hipLaunchKernelGGL((k_route<2, 128>), grid, dim3(kRT), 0, stream, a);
+  } else if (a.head_dim == 64) {
+    if (a.n_heads <= 32) hipLaunchKernelGGL((k_route<1, 64>), grid, dim3(kRT), 0, stream, a);
+    else hipLaunchKernelGGL((k_route<2, 64>), grid, dim3(kRT), 0, stream, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -1,0 +1,259 @@
+// Score-and-select kernel for decode-shaped indexer work.
+//
+// One workgroup = one query x one chunk of its items (prefix tokens, pooled
+// blocks, or a gathered candidate list).  Phase 1 streams the chunk's key rows
+// straight from HBM into MFMA operands (each lane one contiguous run of a key
+// row), computes the fused ReLU-weighted head reduction in registers and keeps
+// the chunk's scores in LDS only.  Phase 2 emits the chunk's candidates: every
+// entry whose 12-bit score bin is at or above the bin of the chunk's k-th best,
+// which always contains the chunk's share of the query's exact top-k (a chunk
+// cannot hold more winners than its own top-k).  Phase 3 runs in the last
+// workgroup to finish for that query (atomic arrival counter, release/acquire
+// fences) and merges all chunks' candidates into the exact top-k.  No score
+// vector is ever written to HBM.
+//
+// Method: the DSA indexer scores every causal prefix token with H_I heads and
+// keeps the top-k (MISA summary, "problem" section); MISA's routed pass scores
+// with h gathered heads ("method" step 2) and its dagger variant rescores a
+// candidate list with all heads ("hierarchical variant"); HISA scores pooled
+// block keys, then the tokens of the surviving blocks (HISA review, section 3).
+#include "dsa_internal.h"
+#include "dsa_scorers.h"
+#include "dsa_select.h"
+
+namespace dsa {
+
+namespace {
+
+constexpr int kNT = 512;
+constexpr int kNW = kNT / 64;
+
+struct Row {
+  int seq;
+  int64_t pos;
+  int64_t n_items;
+};
+
+template <int MODE>
+DSA_DEVICE Row row_of(const SelArgs& a, int t) {
+  Row r;
+  r.seq = a.q_seq ? a.q_seq[t] : 0;
+  r.pos = a.q_pos[t];
+  r.n_items = 0;
+  if (r.seq >= 0 && r.seq < a.n_seq && r.pos >= 0 && r.pos < a.l_max) {
+    if (MODE == MODE_RANGE) r.n_items = r.pos + 1;
+    else if (MODE == MODE_POOLED) r.n_items = (r.pos + a.block) / a.block;
+    else if (MODE == MODE_LIST) r.n_items = a.list_len;
+    else r.n_items = (int64_t)a.list_len * a.block;
+  }
+  return r;
+}
+
+// id of an item and the address of its key row; returns false (and a safe row
+// address) for items that are not valid keys of this query.
+template <int MODE>
+DSA_DEVICE bool item_of(const SelArgs& a, int t, const Row& r, int64_t item, int32_t& id,
+                        const uint16_t*& row) {
+  const size_t eb = a.f32 ? 4 : 2;
+  const char* kb = reinterpret_cast<const char*>(a.keys);
+  const size_t seq_base = (size_t)r.seq * (size_t)a.l_max;
+  int64_t v;
+  bool ok = true;
+  if (MODE == MODE_RANGE) {
+    v = item;
+  } else if (MODE == MODE_POOLED) {
+    id = (int32_t)item;
+    if (a.partial && item == r.n_items - 1 && ((r.pos + 1) % a.block) != 0) {
+      row = a.partial + (size_t)t * a.head_dim;
+    } else {
+      row = a.pooled + ((size_t)r.seq * (size_t)a.m_max + (size_t)item) * a.head_dim;
+    }
+    return true;
+  } else if (MODE == MODE_LIST) {
+    v = a.list[(size_t)t * a.list_len + item];
+    ok = v >= 0 && v <= r.pos;
+  } else {
+    int64_t b = a.list[(size_t)t * a.list_len + item / a.block];
+    v = b * a.block + item % a.block;
+    ok = b >= 0 && v <= r.pos;
+  }
+  if (!ok) v = 0;
+  id = ok ? (int32_t)v : -1;
+  row = reinterpret_cast<const uint16_t*>(kb + (seq_base + (size_t)v) * a.head_dim * eb);
+  return ok;
+}
+
+template <class SC, int MODE>
+DSA_DEVICE void load_tile(const SelArgs& a, int t, const Row& r, int64_t i0, int n_c, int tile,
+                          typename SC::Frag& f) {
+  const uint16_t* rows[SC::kRows];
+#pragma unroll
+  for (int k = 0; k < SC::kRows; ++k) {
+    int j = tile * 32 + SC::row_key(k);
+    int32_t id;
+    const uint16_t* p;
+    if (j < n_c) {
+      item_of<MODE>(a, t, r, i0 + j, id, p);
+    } else {
+      item_of<MODE>(a, t, r, i0, id, p);   // in-range stand-in; result is discarded
+    }
+    rows[k] = p;
+  }
+  SC::load(f, rows);
+}
+
+template <class SC, int MODE>
+DSA_DEVICE void store_score(const SelArgs& a, int t, const Row& r, int64_t i0, int n_c, int tile,
+                            float s, uint32_t* skey) {
+  const int lane = lane_id();
+  const int j = tile * 32 + lane;
+  if (lane < 32 && j < n_c) {
+    bool ok = true;
+    if (MODE == MODE_LIST || MODE == MODE_BLOCKS) {
+      int32_t id;
+      const uint16_t* p;
+      ok = item_of<MODE>(a, t, r, i0 + j, id, p);
+    }
+    skey[j] = ok ? score_to_key(s) : 0u;
+  }
+}
+
+template <class SC, int MODE>
+__global__ __launch_bounds__(kNT) void k_score_select(SelArgs a) {
+  extern __shared__ uint32_t smem[];
+  uint32_t* skey = smem;
+  uint32_t* hist = smem + a.chunk;
+  uint32_t* scratch = hist + kBins;
+  float* sc_lds = reinterpret_cast<float*>(scratch + 64);
+  __shared__ int s_last;
+
+  const int t = blockIdx.y, c = blockIdx.x;
+  const Row r = row_of<MODE>(a, t);
+  int32_t* out_i = a.out_idx + (size_t)t * a.top_k;
+  float* out_s = a.out_score ? a.out_score + (size_t)t * a.top_k : nullptr;
+  if (r.n_items == 0) {
+    if (c == 0) {
+      for (int i = threadIdx.x; i < a.top_k; i += kNT) {
+        out_i[i] = -1;
+        if (out_s) out_s[i] = -__builtin_inff();
+      }
+    }
+    return;
+  }
+  const int n_chunks_t = (int)((r.n_items + a.chunk - 1) / a.chunk);
+  if (c >= n_chunks_t) return;
+
+  // ---- phase 1: scores of this chunk into LDS
+  const size_t eb = a.f32 ? 4 : 2;
+  const uint16_t* q_t = reinterpret_cast<const uint16_t*>(
+      reinterpret_cast<const char*>(a.q) + (size_t)t * a.n_heads * a.head_dim * eb);
+  const float* w_t = a.w + (size_t)t * a.n_heads;
+  const int32_t* heads_t = a.heads ? a.heads + (size_t)t * a.heads_stride : nullptr;
+  SC sc;
+  sc.init(q_t, w_t, heads_t, a.h_use, sc_lds);
+  __syncthreads();
+
+  const int64_t i0 = (int64_t)c * a.chunk;
+  const int n_c = (int)((r.n_items - i0) < a.chunk ? (r.n_items - i0) : a.chunk);
+  const int n_tiles = (n_c + 31) / 32;
+  const int wv = wave_id();
+  {
+    typename SC::Frag fa, fb;
+    int tile = wv;
+    if (tile < n_tiles) load_tile<SC, MODE>(a, t, r, i0, n_c, tile, fa);
+    for (; tile < n_tiles; tile += 2 * kNW) {
+      const int t1 = tile + kNW, t2 = tile + 2 * kNW;
+      if (t1 < n_tiles) load_tile<SC, MODE>(a, t, r, i0, n_c, t1, fb);
+      float s0 = sc.score(fa);
+      store_score<SC, MODE>(a, t, r, i0, n_c, tile, s0, skey);
+      if (t2 < n_tiles) load_tile<SC, MODE>(a, t, r, i0, n_c, t2, fa);
+      if (t1 < n_tiles) {
+        float s1 = sc.score(fb);
+        store_score<SC, MODE>(a, t, r, i0, n_c, t1, s1, skey);
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 2: this chunk's candidates
+  uint2* seg = a.cand + ((size_t)t * a.n_chunks + c) * (size_t)a.chunk;
+  auto id_of = [&](int i) -> int32_t {
+    int32_t id;
+    const uint16_t* p;
+    item_of<MODE>(a, t, r, i0 + i, id, p);
+    return id;
+  };
+  uint32_t nv = chunk_emit<kNT>(skey, n_c, a.top_k, id_of, seg,
+                                a.cand_cnt + (size_t)t * a.n_chunks + c,
+                                a.ghist + (size_t)t * kBins, hist, scratch);
+  if (threadIdx.x == 0 && nv) atomicAdd(a.nvalid + t, nv);
+
+  // ---- phase 3: the last chunk of this query to finish merges
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t done = atomicAdd(a.counter + t, 1u);
+    s_last = (done == (uint32_t)(n_chunks_t - 1));
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  const uint32_t n_valid = __hip_atomic_load(a.nvalid + t, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+  merge_query<kNT>(a.cand + (size_t)t * a.n_chunks * a.chunk, a.cand_cnt + (size_t)t * a.n_chunks,
+                   n_chunks_t, a.chunk, a.ghist + (size_t)t * kBins, n_valid, a.top_k, out_i, out_s,
+                   reinterpret_cast<uint2*>(skey), (uint32_t)(a.chunk / 2), hist, scratch);
+}
+
+template <class SC, int MODE>
+hipError_t launch_t(const SelArgs& a, hipStream_t stream) {
+  const size_t lds = score_select_lds_bytes(a.chunk, a.f32, a.head_dim);
+  auto kern = k_score_select<SC, MODE>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  dim3 grid(a.n_chunks, a.nq);
+  hipLaunchKernelGGL(kern, grid, dim3(kNT), lds, stream, a);
+  return hipGetLastError();
+}
+
+template <class SC>
+hipError_t launch_mode(const SelArgs& a, hipStream_t stream) {
+  switch (a.mode) {
+    case MODE_RANGE: return launch_t<SC, MODE_RANGE>(a, stream);
+    case MODE_POOLED: return launch_t<SC, MODE_POOLED>(a, stream);
+    case MODE_LIST: return launch_t<SC, MODE_LIST>(a, stream);
+    case MODE_BLOCKS: return launch_t<SC, MODE_BLOCKS>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+size_t score_select_lds_bytes(int chunk, int f32, int head_dim) {
+  size_t b = (size_t)chunk * 4 + kBins * 4 + 64 * 4;
+  if (f32) b += (size_t)(64 * head_dim + 64) * 4;
+  return b;
+}
+
+hipError_t launch_score_select(const SelArgs& a, hipStream_t stream) {
+  if (a.f32) {
+    if (a.mode != MODE_RANGE) return hipErrorInvalidValue;
+    if (a.head_dim == 64) return launch_t<ScorerF32<64>, MODE_RANGE>(a, stream);
+    if (a.head_dim == 128) return launch_t<ScorerF32<128>, MODE_RANGE>(a, stream);
+    return hipErrorInvalidValue;
+  }
+  if (a.head_dim == 128) {
+    if (a.h_use <= 16) return launch_mode<ScorerMfma16<128>>(a, stream);
+    if (a.h_use <= 32) return launch_mode<ScorerMfma32<1, 128>>(a, stream);
+    return launch_mode<ScorerMfma32<2, 128>>(a, stream);
+  }
+  if (a.head_dim == 64) {
+    if (a.h_use <= 16) return launch_mode<ScorerMfma16<64>>(a, stream);
+    if (a.h_use <= 32) return launch_mode<ScorerMfma32<1, 64>>(a, stream);
+    return launch_mode<ScorerMfma32<2, 64>>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace dsa
