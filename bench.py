@@ -1,0 +1,298 @@
+#!/usr/bin/env python3
+"""Benchmark of the DSA indexer on one MI355X.
+
+Default: the dense decode-shaped indexer, 64 queries each against its own
+131072-key causal prefix, 64 heads, d = 128, bf16, top-k 2048.  One step = one
+indexer_score_topk call (scoring and exact top-k selection of all 64 queries)
+with inputs resident in HBM.  Prints one JSON line.
+
+Other workloads (--workload): tiny (float32, 16 queries, L = 4096),
+misa / misa_dagger (h = 8 of 64 heads, B = 64, k' = 8192), hisa (32 heads,
+L = 1M, B = 128, m = 64), pool (mean pooling of the 128K caches).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+CSRC = os.path.join(ROOT, "sparse_attention_token_indexer_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+WORKLOADS = {"dense_decode": 2, "tiny": 1, "misa": 4, "misa_dagger": 4, "hisa": 5, "pool": 4}
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel from rocprofv3 counters, if they
+    were taken on the current kernel sources (else None)."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(workload)
+    if not e or e.get("kernel_hash") != kernel_source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return 1
+
+
+def gen_inputs(wl, seed, dev):
+    import numpy as np
+    import torch
+
+    import datagen
+    q, w = datagen.queries(wl, seed)
+    q_seq, q_pos = datagen.positions(wl)
+
+    def to_dev(x):
+        if wl.dtype == datagen.BF16:
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    kdev = torch.empty((wl.n_seq, wl.l_max, wl.head_dim),
+                       dtype=torch.bfloat16 if wl.dtype == datagen.BF16 else torch.float32, device=dev)
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=16) as ex:
+        for s, ks in enumerate(ex.map(lambda s: datagen.keys(wl, s, q, w, seed), range(wl.n_seq))):
+            kdev[s].copy_(to_dev(ks))
+    return {"q": to_dev(q), "w": torch.from_numpy(w).to(dev), "k": kdev,
+            "q_seq": torch.from_numpy(q_seq).to(dev), "q_pos": torch.from_numpy(q_pos).to(dev),
+            "np": {"q": q, "w": w, "q_seq": q_seq, "q_pos": q_pos}}
+
+
+def cpu_baseline(wl, seed, seconds: float, mode: str):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload:
+    whole queries (full prefix scoring + exact top-k) until about `seconds` of
+    compute have run.  Input generation is not timed."""
+    import numpy as np
+
+    import datagen
+    from oracle import indexer as O
+    q, w = datagen.queries(wl, seed)
+    q_seq, q_pos = datagen.positions(wl)
+    done_pairs, spent, nq_done = 0, 0.0, 0
+    for t in range(wl.nq):
+        K = O.to_f64(datagen.keys(wl, int(q_seq[t]), q, w, seed), wl.dtype)
+        q_t = O.to_f64(q[t], wl.dtype)
+        w_t = w[t].astype(np.float64)
+        p = int(q_pos[t])
+        t0 = time.perf_counter()
+        if mode == "misa":
+            O.misa_row(q_t, w_t, K, p, wl.block, wl.n_active_heads, wl.top_k)
+        elif mode == "misa_dagger":
+            O.misa_dagger_row(q_t, w_t, K, p, wl.block, wl.n_active_heads, wl.k_prime, wl.top_k)
+        elif mode == "hisa":
+            O.hisa_row(q_t, w_t, K, p, wl.block, wl.m_blocks, wl.top_k)
+        else:
+            O.dense_row(q_t, w_t, K, p, wl.top_k)
+        spent += time.perf_counter() - t0
+        done_pairs += p + 1
+        nq_done += 1
+        if spent >= seconds:
+            break
+    return {"value": done_pairs / spent, "unit": "pair-scores/s", "cores": blas_threads(),
+            "kind": "oracle",
+            "sample": f"{nq_done} of {wl.nq} queries ({done_pairs} causal pairs), float64 NumPy, "
+                      f"{spent:.1f} s of compute on {os.cpu_count()} visible host cores"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dense_decode", choices=sorted(WORKLOADS))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a plain 1 GiB device copy (for HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import datagen
+    import sparse_attention_token_indexer_amd as dsa
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": src.numel() * 4,
+                          "calibrate_copy_bytes_written": dst.numel() * 4}))
+        return 0
+
+    dsa.lib()
+    name = args.workload
+    wl = datagen.WORKLOADS[WORKLOADS[name]]
+    inp = gen_inputs(wl, args.seed, dev)
+    q, w, k, q_pos, q_seq = inp["q"], inp["w"], inp["k"], inp["q_pos"], inp["q_seq"]
+    nq, H, d, L, topk = wl.nq, wl.n_heads, wl.head_dim, wl.l_max, wl.top_k
+    eb = 2 if wl.dtype == datagen.BF16 else 4
+    pos_np = inp["np"]["q_pos"]
+    pairs = int((pos_np.astype(np.int64) + 1).sum())
+    out_i = torch.empty((nq, topk), dtype=torch.int32, device=dev)
+    out_s = torch.empty((nq, topk), dtype=torch.float32, device=dev)
+    io_bytes = nq * H * d * eb + nq * H * 4 + nq * topk * 8       # q, w, outputs
+    extra = {}
+
+    if name in ("dense_decode", "tiny"):
+        nbytes = dsa.indexer_score_topk_workspace_size(nq, H, d, wl.n_seq, L, topk,
+                                                       0 if eb == 2 else 1)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+
+        def step():
+            dsa.indexer_score_topk(q, w, k, q_pos, q_seq, top_k=topk, out_idx=out_i,
+                                   out_score=out_s, workspace=ws)
+        kind = "score_tokens"
+        kernel_bytes = pairs * d * eb + io_bytes
+        bound_note = "HBM: every prefix key row is read once"
+    elif name in ("misa", "misa_dagger"):
+        kp = dsa.indexer_mean_pool_keys(k, wl.block)
+        kprime = wl.k_prime if name == "misa_dagger" else 0
+        nbytes = dsa.misa_route_score_topk_workspace_size(nq, H, d, wl.n_seq, L, wl.block,
+                                                          wl.n_active_heads, kprime, topk, 1)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+
+        def step():
+            dsa.misa_route_score_topk(q, w, k, q_pos, q_seq, block=wl.block,
+                                      n_active_heads=wl.n_active_heads, top_k=topk, k_prime=kprime,
+                                      k_pooled=kp, with_heads=False, out_idx=out_i,
+                                      out_score=out_s, workspace=ws)
+        kind = "score_tokens"
+        h = wl.n_active_heads
+        kernel_bytes = pairs * d * eb + nq * h * d * eb + nq * h * 4 + nq * (kprime or topk) * (4 if kprime else 8)
+        bound_note = "HBM: the routed pass still reads every prefix key row"
+    elif name == "hisa":
+        kp = dsa.indexer_mean_pool_keys(k, wl.block)
+        nbytes = dsa.hisa_block_filter_topk_workspace_size(nq, H, d, wl.n_seq, L, wl.block,
+                                                           wl.m_blocks, topk, 1)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+
+        def step():
+            dsa.hisa_block_filter_topk(q, w, k, q_pos, q_seq, block=wl.block, m_blocks=wl.m_blocks,
+                                       top_k=topk, k_pooled=kp, with_blocks=False, out_idx=out_i,
+                                       out_score=out_s, workspace=ws)
+        kind = "score_blocks"
+        kernel_bytes = nq * wl.m_blocks * wl.block * d * eb + nq * wl.m_blocks * 4 + io_bytes
+        bound_note = "HBM: gathers the keys of the m surviving blocks"
+    elif name == "pool":
+        M = -(-L // wl.block)
+        kp = torch.empty((wl.n_seq, M, d), dtype=torch.bfloat16, device=dev)
+
+        def step():
+            dsa.indexer_mean_pool_keys(k, wl.block, out=kp)
+        kind = "pool"
+        kernel_bytes = wl.n_seq * L * d * eb + wl.n_seq * M * d * 2
+        bound_note = "HBM: reads the key cache once, writes the pooled keys"
+    else:
+        raise ValueError(name)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    dsa.kernel_timing(True)
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for _ in range(args.steps):
+        step()
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    kt = dsa.kernel_timing_read(kind)
+    per_kernel = {}
+    for other in dsa.KERNEL_KINDS:
+        if other == kind:
+            continue
+        r = dsa.kernel_timing_read(other)
+        if r["launches"]:
+            per_kernel[other] = round(r["total_ms"] / r["launches"] * 1e3, 2)
+    dsa.kernel_timing(False)
+    k_avg_ms = kt["total_ms"] / max(kt["launches"], 1)
+    per_kernel[kind] = round(k_avg_ms * 1e3, 2)
+    achieved = kernel_bytes / (k_avg_ms * 1e-3) / 1e9
+    traffic = stored_traffic(name)
+
+    if name == "pool":
+        metric, unit, value = "mean-pooled key-cache bytes/s", "GB/s", kernel_bytes / (ms_per_step * 1e-3) / 1e9
+    else:
+        metric = "indexer q·k pair-scores/sec + top-k latency at L=128K, H_I=64 (1 MI355X)"
+        unit = "pair-scores/s"
+        value = pairs / (ms_per_step * 1e-3)
+
+    cpu = None
+    if not args.no_cpu_baseline and name != "pool":
+        cpu = cpu_baseline(wl, args.seed, args.cpu_seconds, name)
+
+    line = {
+        "metric": metric,
+        "value": value,
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if eb == 2 else "f32",
+        "data": "synthetic (seeded; planted-key recipe of the workload)",
+        "config": {"workload": wl.name, "queries": nq, "l_max": L, "n_heads": H, "head_dim": d,
+                   "top_k": topk, "causal_pairs": pairs, "parallelism": "single GPU",
+                   **({"block": wl.block} if wl.block else {}),
+                   **({"h": wl.n_active_heads} if name.startswith("misa") else {}),
+                   **({"k_prime": wl.k_prime} if name == "misa_dagger" else {}),
+                   **({"m_blocks": wl.m_blocks} if name == "hisa" else {})},
+        "topk_latency_us": ms_per_step * 1e3,
+        "kernel_avg_us": per_kernel,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": kind, "algorithmic_bytes_per_launch": kernel_bytes,
+                     "note": bound_note},
+        "cpu_baseline": cpu,
+        "host": {"cpu_count": os.cpu_count(), "machine": platform.machine(),
+                 "torch": torch.__version__},
+        **extra,
+    }
+    print(json.dumps(line))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

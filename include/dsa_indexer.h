@@ -170,6 +170,31 @@ int hisa_block_filter_topk(const void* q, const float* w, const void* k, const v
 int indexer_selection_iou(const int32_t* a, const int32_t* b, int32_t nq, int32_t k,
                           float* out_iou, hipStream_t stream);
 
+/*
+ * Kernel timing, for measurement.  While enabled (dsa_kernel_timing(1)), every
+ * kernel the library launches is bracketed by two HIP events recorded on the
+ * call's stream, tagged with its kernel kind (DSA_KERNEL_*).  Events come from
+ * a pool the library creates once and reuses (hipEventCreate, no device memory).
+ * dsa_kernel_timing_read() waits for the recorded events, returns for one kind
+ * the number of launches and their summed / minimum / maximum duration in
+ * milliseconds, and forgets the records of that kind.  Disabling drops all
+ * pending records.  Not thread-safe against concurrent calls that record.
+ */
+#define DSA_KERNEL_PREPARE 0      /* workspace clear + partial-block pooling */
+#define DSA_KERNEL_SCORE_TOKENS 1 /* score-and-select over prefix tokens */
+#define DSA_KERNEL_SCORE_POOLED 2 /* score-and-select over pooled blocks (HISA stage 1) */
+#define DSA_KERNEL_SCORE_LIST 3   /* score-and-select over a candidate list (MISA dagger) */
+#define DSA_KERNEL_SCORE_BLOCKS 4 /* score-and-select over surviving blocks (HISA stage 2) */
+#define DSA_KERNEL_ROUTE 5        /* MISA router */
+#define DSA_KERNEL_POOL 6         /* mean pooling */
+#define DSA_KERNEL_IOU 7
+#define DSA_KERNEL_PREFILL 8      /* prefill-shaped scoring */
+#define DSA_KERNEL_ROWSELECT 9    /* prefill row selection */
+#define DSA_KERNEL_KINDS 10
+int dsa_kernel_timing(int enable);
+int dsa_kernel_timing_read(int32_t kind, int64_t* launches, double* total_ms, double* min_ms,
+                           double* max_ms);
+
 #ifdef __cplusplus
 }
 #endif

@@ -45,6 +45,16 @@ _SIGS = {
                                 _i64, _i32, _i32, _i32, _c_p, _c_p, _c_p, _c_p, _c_p, _sz, _c_p],
                                ctypes.c_int),
     "indexer_selection_iou": ([_c_p, _c_p, _i32, _i32, _c_p, _c_p], ctypes.c_int),
+    "dsa_kernel_timing": ([ctypes.c_int], ctypes.c_int),
+    "dsa_kernel_timing_read": ([_i32, ctypes.POINTER(_i64), ctypes.POINTER(ctypes.c_double),
+                                ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)],
+                               ctypes.c_int),
+}
+
+# kernel kinds of dsa_kernel_timing_read
+KERNEL_KINDS = {
+    "prepare": 0, "score_tokens": 1, "score_pooled": 2, "score_list": 3, "score_blocks": 4,
+    "route": 5, "pool": 6, "iou": 7, "prefill": 8, "rowselect": 9,
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -290,7 +300,25 @@ def indexer_selection_iou(a: torch.Tensor, b: torch.Tensor,
     return out
 
 
+def kernel_timing(enable: bool) -> None:
+    """Record HIP events around every library kernel launch (measurement only)."""
+    _check(lib().dsa_kernel_timing(int(bool(enable))), "dsa_kernel_timing")
+
+
+def kernel_timing_read(kind: str) -> Dict[str, float]:
+    """Launch count and summed / min / max duration (ms) of one kernel kind since
+    the last read; waits for the recorded events."""
+    n = _i64(0)
+    tot, lo, hi = ctypes.c_double(0), ctypes.c_double(0), ctypes.c_double(0)
+    _check(lib().dsa_kernel_timing_read(KERNEL_KINDS[kind], ctypes.byref(n), ctypes.byref(tot),
+                                        ctypes.byref(lo), ctypes.byref(hi)),
+           "dsa_kernel_timing_read")
+    return {"launches": int(n.value), "total_ms": tot.value, "min_ms": lo.value,
+            "max_ms": hi.value}
+
+
 __all__ = [
+    "kernel_timing", "kernel_timing_read", "KERNEL_KINDS",
     "DsaError", "LIB_PATH", "lib", "DSA_DTYPE_BF16", "DSA_DTYPE_F32",
     "indexer_score_topk", "indexer_score_topk_workspace_size",
     "indexer_mean_pool_keys",

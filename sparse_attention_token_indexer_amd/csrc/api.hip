@@ -5,7 +5,9 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "dsa_internal.h"
 
@@ -40,6 +42,57 @@ int hip_status(hipError_t e, const char* what, hipStream_t stream) {
   return DSA_OK;
 }
 
+// ---- kernel timing (measurement support, see dsa_kernel_timing in the header)
+struct TimingRec {
+  int kind;
+  hipEvent_t a, b;
+};
+std::mutex g_tmu;
+bool g_timing = false;
+std::vector<hipEvent_t> g_event_pool;
+std::vector<TimingRec> g_recs;
+
+hipEvent_t pooled_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+template <class F>
+hipError_t timed(int kind, hipStream_t stream, F&& launch) {
+  if (!g_timing) return launch();
+  std::lock_guard<std::mutex> lk(g_tmu);
+  hipEvent_t a = pooled_event(), b = pooled_event();
+  if (a) (void)hipEventRecord(a, stream);
+  hipError_t e = launch();
+  if (b) (void)hipEventRecord(b, stream);
+  if (a && b) g_recs.push_back({kind, a, b});
+  return e;
+}
+
+int score_kind(int mode) {
+  switch (mode) {
+    case dsa::MODE_RANGE: return DSA_KERNEL_SCORE_TOKENS;
+    case dsa::MODE_POOLED: return DSA_KERNEL_SCORE_POOLED;
+    case dsa::MODE_LIST: return DSA_KERNEL_SCORE_LIST;
+    default: return DSA_KERNEL_SCORE_BLOCKS;
+  }
+}
+
+template <class F>
+hipError_t timed_pool(hipStream_t stream, F&& f) {
+  return timed(DSA_KERNEL_POOL, stream, f);
+}
+
+hipError_t run_score_select(const dsa::SelArgs& a, hipStream_t stream) {
+  return timed(score_kind(a.mode), stream, [&] { return dsa::launch_score_select(a, stream); });
+}
+
 constexpr int kBins = 4096;
 constexpr int kMaxChunk = 8192;
 constexpr int kMinChunk = 256;
@@ -62,7 +115,7 @@ struct Arena {
 
 struct StagePlan {
   int chunk = 0, n_chunks = 0;
-  size_t ghist = 0, counter = 0, nvalid = 0, cand = 0, cnt = 0;
+  size_t ghist = 0, cand = 0, cnt = 0;
 };
 
 // largest power-of-two chunk (<= the LDS limit) that still gives about
@@ -73,13 +126,13 @@ int choose_chunk(int64_t n_items, int64_t nq, int f32, int head_dim) {
          dsa::score_select_lds_bytes(chunk, f32, head_dim) > kMaxLds)
     chunk >>= 1;
   while (chunk > kMinChunk && nq * cdiv(n_items, chunk) < kTargetWorkgroups) chunk >>= 1;
+  // the merge keeps one offset per chunk in LDS
+  while (cdiv(n_items, chunk) > dsa::kMaxChunks && chunk < (1 << 20)) chunk <<= 1;
   return chunk;
 }
 
 void plan_zero(Arena& A, StagePlan& s, int64_t nq) {
   s.ghist = A.take((size_t)nq * kBins * 4);
-  s.counter = A.take((size_t)nq * 4);
-  s.nvalid = A.take((size_t)nq * 4);
 }
 
 void plan_cand(Arena& A, StagePlan& s, int64_t nq, int64_t n_items, int f32, int head_dim) {
@@ -101,8 +154,6 @@ dsa::SelArgs stage_args(const StagePlan& s, void* ws) {
   a.cand = at<uint2>(ws, s.cand);
   a.cand_cnt = at<uint32_t>(ws, s.cnt);
   a.ghist = at<uint32_t>(ws, s.ghist);
-  a.counter = at<uint32_t>(ws, s.counter);
-  a.nvalid = at<uint32_t>(ws, s.nvalid);
   return a;
 }
 
@@ -228,7 +279,8 @@ int run_prepare(void* ws, size_t zero_bytes, const void* k, const int32_t* q_seq
   pa.block = block;
   pa.l_max = l_max;
   pa.partial = partial;
-  return hip_status(dsa::launch_prepare(pa, stream), "prepare kernel", stream);
+  return hip_status(timed(DSA_KERNEL_PREPARE, stream, [&] { return dsa::launch_prepare(pa, stream); }),
+                    "prepare kernel", stream);
 }
 
 void fill_common(dsa::SelArgs& a, const void* q, const float* w, const void* k,
@@ -254,6 +306,50 @@ extern "C" {
 const char* dsa_last_error(void) { return g_err.c_str(); }
 
 int dsa_abi_version(void) { return 1; }
+
+int dsa_kernel_timing(int enable) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  g_timing = enable != 0;
+  if (!g_timing) {
+    for (auto& r : g_recs) {
+      g_event_pool.push_back(r.a);
+      g_event_pool.push_back(r.b);
+    }
+    g_recs.clear();
+  }
+  return DSA_OK;
+}
+
+int dsa_kernel_timing_read(int32_t kind, int64_t* launches, double* total_ms, double* min_ms,
+                           double* max_ms) {
+  if (kind < 0 || kind >= DSA_KERNEL_KINDS) return fail(DSA_EINVAL, "unknown kernel kind %d", kind);
+  std::lock_guard<std::mutex> lk(g_tmu);
+  int64_t n = 0;
+  double tot = 0, lo = 0, hi = 0;
+  std::vector<TimingRec> keep;
+  for (auto& r : g_recs) {
+    if (r.kind != kind) {
+      keep.push_back(r);
+      continue;
+    }
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+    g_event_pool.push_back(r.a);
+    g_event_pool.push_back(r.b);
+    if (e != hipSuccess) return fail(DSA_EHIP, "event timing: %s", hipGetErrorString(e));
+    lo = n ? (ms < lo ? ms : lo) : ms;
+    hi = n ? (ms > hi ? ms : hi) : ms;
+    tot += ms;
+    ++n;
+  }
+  g_recs.swap(keep);
+  if (launches) *launches = n;
+  if (total_ms) *total_ms = tot;
+  if (min_ms) *min_ms = lo;
+  if (max_ms) *max_ms = hi;
+  return DSA_OK;
+}
 
 size_t indexer_score_topk_workspace_size(int32_t nq, int32_t n_heads, int32_t head_dim,
                                          int32_t n_seq, int64_t l_max, int32_t top_k,
@@ -283,7 +379,7 @@ int indexer_score_topk(const void* q, const float* w, const void* k, int32_t dty
   a.top_k = top_k;
   a.out_idx = out_idx;
   a.out_score = out_score;
-  return hip_status(dsa::launch_score_select(a, stream), "score/select kernel", stream);
+  return hip_status(run_score_select(a, stream), "score/select kernel", stream);
 }
 
 int indexer_mean_pool_keys(const void* k, int32_t dtype, int32_t n_seq, int64_t l_max,
@@ -296,9 +392,9 @@ int indexer_mean_pool_keys(const void* k, int32_t dtype, int32_t n_seq, int64_t 
   if (n_seq == 0 || l_max == 0) return DSA_OK;
   if (!k || !k_pooled) return fail(DSA_EINVAL, "k and k_pooled must not be NULL");
   if (!aligned(k, 16) || !aligned(k_pooled, 16)) return fail(DSA_EINVAL, "k and k_pooled must be 16-byte aligned");
-  return hip_status(dsa::launch_mean_pool(reinterpret_cast<const uint16_t*>(k), n_seq, l_max,
+  return hip_status(timed_pool(stream, [&] { return dsa::launch_mean_pool(reinterpret_cast<const uint16_t*>(k), n_seq, l_max,
                                           head_dim, block, reinterpret_cast<uint16_t*>(k_pooled),
-                                          stream),
+                                          stream); }),
                     "mean-pool kernel", stream);
 }
 
@@ -335,8 +431,8 @@ int misa_route_score_topk(const void* q, const float* w, const void* k, const vo
   const uint16_t* pooled = reinterpret_cast<const uint16_t*>(k_pooled);
   if (!pooled) {
     uint16_t* dst = at<uint16_t>(workspace, p.pooled);
-    st = hip_status(dsa::launch_mean_pool(reinterpret_cast<const uint16_t*>(k), n_seq, l_max,
-                                          head_dim, block, dst, stream),
+    st = hip_status(timed_pool(stream, [&] { return dsa::launch_mean_pool(reinterpret_cast<const uint16_t*>(k), n_seq, l_max,
+                                          head_dim, block, dst, stream); }),
                     "mean-pool kernel", stream);
     if (st) return st;
     pooled = dst;
@@ -368,7 +464,8 @@ int misa_route_score_topk(const void* q, const float* w, const void* k, const vo
   ra.heads = at<int32_t>(workspace, p.heads);
   ra.out_heads = out_heads;
   ra.out_importance = out_importance;
-  if ((st = hip_status(dsa::launch_route(ra, stream), "router kernel", stream))) return st;
+  if ((st = hip_status(timed(DSA_KERNEL_ROUTE, stream, [&] { return dsa::launch_route(ra, stream); }),
+                       "router kernel", stream))) return st;
   // routed token pass
   dsa::SelArgs a = stage_args(p.s0, workspace);
   fill_common(a, q, w, k, q_seq, q_pos, nq, n_heads, head_dim, n_seq, l_max);
@@ -380,13 +477,13 @@ int misa_route_score_topk(const void* q, const float* w, const void* k, const vo
     a.top_k = top_k;
     a.out_idx = out_idx;
     a.out_score = out_score;
-    return hip_status(dsa::launch_score_select(a, stream), "routed score/select kernel", stream);
+    return hip_status(run_score_select(a, stream), "routed score/select kernel", stream);
   }
   int32_t* cand = out_cand ? out_cand : at<int32_t>(workspace, p.cand_list);
   a.top_k = k_prime;
   a.out_idx = cand;
   a.out_score = nullptr;
-  if ((st = hip_status(dsa::launch_score_select(a, stream), "routed score/select kernel", stream)))
+  if ((st = hip_status(run_score_select(a, stream), "routed score/select kernel", stream)))
     return st;
   // all-head rescoring of the k' candidates
   dsa::SelArgs b = stage_args(p.s1, workspace);
@@ -397,7 +494,7 @@ int misa_route_score_topk(const void* q, const float* w, const void* k, const vo
   b.top_k = top_k;
   b.out_idx = out_idx;
   b.out_score = out_score;
-  return hip_status(dsa::launch_score_select(b, stream), "rescore/select kernel", stream);
+  return hip_status(run_score_select(b, stream), "rescore/select kernel", stream);
 }
 
 size_t hisa_block_filter_topk_workspace_size(int32_t nq, int32_t n_heads, int32_t head_dim,
@@ -428,8 +525,8 @@ int hisa_block_filter_topk(const void* q, const float* w, const void* k, const v
   const uint16_t* pooled = reinterpret_cast<const uint16_t*>(k_pooled);
   if (!pooled) {
     uint16_t* dst = at<uint16_t>(workspace, p.pooled);
-    st = hip_status(dsa::launch_mean_pool(reinterpret_cast<const uint16_t*>(k), n_seq, l_max,
-                                          head_dim, block, dst, stream),
+    st = hip_status(timed_pool(stream, [&] { return dsa::launch_mean_pool(reinterpret_cast<const uint16_t*>(k), n_seq, l_max,
+                                          head_dim, block, dst, stream); }),
                     "mean-pool kernel", stream);
     if (st) return st;
     pooled = dst;
@@ -450,7 +547,7 @@ int hisa_block_filter_topk(const void* q, const float* w, const void* k, const v
   a.top_k = m_blocks;
   a.out_idx = blocks;
   a.out_score = out_block_score;
-  if ((st = hip_status(dsa::launch_score_select(a, stream), "block score/select kernel", stream)))
+  if ((st = hip_status(run_score_select(a, stream), "block score/select kernel", stream)))
     return st;
   // stage 2: token refinement inside the surviving blocks
   dsa::SelArgs b = stage_args(p.s1, workspace);
@@ -462,7 +559,7 @@ int hisa_block_filter_topk(const void* q, const float* w, const void* k, const v
   b.top_k = top_k;
   b.out_idx = out_idx;
   b.out_score = out_score;
-  return hip_status(dsa::launch_score_select(b, stream), "refine score/select kernel", stream);
+  return hip_status(run_score_select(b, stream), "refine score/select kernel", stream);
 }
 
 int indexer_selection_iou(const int32_t* a, const int32_t* b, int32_t nq, int32_t k,
@@ -471,7 +568,9 @@ int indexer_selection_iou(const int32_t* a, const int32_t* b, int32_t nq, int32_
   if (k < 1 || k > 8192) return fail(DSA_EUNSUPPORTED, "k must be in [1, 8192] (got %d)", k);
   if (nq == 0) return DSA_OK;
   if (!a || !b || !out_iou) return fail(DSA_EINVAL, "a, b and out_iou must not be NULL");
-  return hip_status(dsa::launch_iou(a, b, nq, k, out_iou, stream), "IoU kernel", stream);
+  return hip_status(timed(DSA_KERNEL_IOU, stream,
+                          [&] { return dsa::launch_iou(a, b, nq, k, out_iou, stream); }),
+                    "IoU kernel", stream);
 }
 
 }  // extern "C"

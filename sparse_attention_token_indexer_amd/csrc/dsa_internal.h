@@ -34,14 +34,15 @@ struct SelArgs {
   uint2* cand;                 // [nq, n_chunks, chunk]
   uint32_t* cand_cnt;          // [nq, n_chunks]
   uint32_t* ghist;             // [nq, 4096]   (zeroed before the pass)
-  uint32_t* counter;           // [nq]         (zeroed before the pass)
-  uint32_t* nvalid;            // [nq]         (zeroed before the pass)
   // outputs
   int32_t* out_idx;            // [nq, top_k]
   float* out_score;            // [nq, top_k] or null
 };
 
+// Launches the score-and-emit kernel, then the merge kernel, on `stream`.
 hipError_t launch_score_select(const SelArgs& a, hipStream_t stream);
+constexpr int kMaxChunks = 8192;        // chunks per query in one pass
+constexpr int kMergeListCap = 12288;    // tie-bin entries resolved in LDS
 size_t score_select_lds_bytes(int chunk, int f32, int head_dim);
 
 // Clears `zero_words` 32-bit words at `zero` and, if `partial` is given, pools

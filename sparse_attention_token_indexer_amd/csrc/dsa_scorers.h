@@ -9,8 +9,10 @@
 //  16x16x32 bf16: lane l holds A[l%16][8*(l/16)+e], B[8*(l/16)+e][l%16];
 //                 accumulator r of lane l is D[4*(l/16) + r][l%16].
 // Heads are the MFMA rows (A = q), keys the columns (B = k).  The order in which
-// the head dimension is fed to the contraction is free (it is a sum), so each
-// lane reads one contiguous run of its key row: 16-byte loads, no shuffles.
+// the head dimension is fed to the contraction is free (it is a sum): at k-step
+// s the two lane halves (or four lane groups) take adjacent 16-byte pieces of
+// the key row, so each load instruction reads 32 (64) contiguous bytes of every
+// key and the cache lines of a tile are consumed by consecutive instructions.
 //
 // After score() every lane holds the score of tile key (lane & 31).
 #pragma once
@@ -39,9 +41,9 @@ struct ScorerMfma32 {
       int slot = ht * 32 + m;
       if (slot < h_use) {
         int head = heads_t ? heads_t[slot] : slot;
-        const uint16_t* src = q_t + (size_t)head * D + h * (D / 2);
+        const uint16_t* src = q_t + (size_t)head * D + 8 * h;
 #pragma unroll
-        for (int s = 0; s < S; ++s) qa[ht][s] = load_bf16x8(src + 8 * s);
+        for (int s = 0; s < S; ++s) qa[ht][s] = load_bf16x8(src + 16 * s);
       } else {
 #pragma unroll
         for (int s = 0; s < S; ++s) qa[ht][s] = zero_bf16x8();
@@ -55,9 +57,9 @@ struct ScorerMfma32 {
   }
 
   DSA_DEVICE static void load(Frag& b, const uint16_t* const* rows) {
-    const uint16_t* src = rows[0] + (lane_id() >> 5) * (D / 2);
+    const uint16_t* src = rows[0] + (lane_id() >> 5) * 8;
 #pragma unroll
-    for (int s = 0; s < S; ++s) b[s] = load_bf16x8(src + 8 * s);
+    for (int s = 0; s < S; ++s) b[s] = load_bf16x8(src + 16 * s);
   }
 
   DSA_DEVICE float score(const Frag& b) const {
@@ -99,9 +101,9 @@ struct ScorerMfma16 {
     const int lane = lane_id(), m = lane & 15, g = lane >> 4;
     if (m < h_use) {
       int head = heads_t ? heads_t[m] : m;
-      const uint16_t* src = q_t + (size_t)head * D + g * (D / 4);
+      const uint16_t* src = q_t + (size_t)head * D + 8 * g;
 #pragma unroll
-      for (int s = 0; s < S; ++s) qa[s] = load_bf16x8(src + 8 * s);
+      for (int s = 0; s < S; ++s) qa[s] = load_bf16x8(src + 32 * s);
     } else {
 #pragma unroll
       for (int s = 0; s < S; ++s) qa[s] = zero_bf16x8();
@@ -117,9 +119,9 @@ struct ScorerMfma16 {
     const int g = lane_id() >> 4;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      const uint16_t* src = rows[c] + g * (D / 4);
+      const uint16_t* src = rows[c] + 8 * g;
 #pragma unroll
-      for (int s = 0; s < S; ++s) b[c][s] = load_bf16x8(src + 8 * s);
+      for (int s = 0; s < S; ++s) b[c][s] = load_bf16x8(src + 32 * s);
     }
   }
 

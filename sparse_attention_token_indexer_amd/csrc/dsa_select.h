@@ -1,12 +1,20 @@
 // Exact top-k selection machinery shared by the scoring kernels.
 //
 // Selection order is the composite (score key desc, id asc), see dsa_common.h.
-// A query's candidates live in per-chunk segments of (key, id) pairs in the
-// workspace; a first-level histogram over the top 12 key bits (ghist) has been
-// accumulated for exactly those candidates.  The merge finds the 12-bit bin
-// that holds the K-th entry, emits everything above it, and resolves the bin
-// itself by further radix digits over the composite key: in LDS when the bin
-// fits, otherwise by re-reading the segments from global memory.
+//
+// Two kernels per selection pass, with no ordering between workgroups of one
+// kernel:
+//  * score-and-emit: every chunk of a query adds the 12-bit histogram of ALL its
+//    scores to the query's global histogram, reads back the running histogram
+//    and appends to its workspace segment every entry whose bin is at or above
+//    the highest bin b with (running count of bins >= b) >= top_k.  The running
+//    counts only ever under-count entries that exist, so that bin never exceeds
+//    the bin of the query's k-th best entry: the segments always hold the exact
+//    top-k, whatever the other chunks have published so far.
+//  * merge: after the kernel boundary the histogram is complete; one workgroup
+//    per query finds the bin b* of the k-th entry, emits every candidate above
+//    it and resolves b* itself by further radix digits over the composite key,
+//    in LDS when the bin fits, else by re-reading the segments.
 #pragma once
 #include "dsa_common.h"
 
@@ -35,18 +43,38 @@ struct LdsSource {
   }
 };
 
-// Entries held in global per-chunk segments.
-struct SegSource {
+// Entries held in global per-chunk segments, walked as one flat index space
+// (off[c] = first flat index of chunk c, off[n_chunks] = total) so that every
+// thread keeps several independent loads in flight.
+struct FlatSegSource {
   const uint2* cand;        // query base: [n_chunks][chunk]
-  const uint32_t* cnt;      // query base: [n_chunks]
+  const uint32_t* off;      // LDS, n_chunks + 1 prefix offsets
   int n_chunks;
   int chunk;
+  DSA_DEVICE uint2 at(uint32_t f) const {
+    int lo = 0, hi = n_chunks;              // last c with off[c] <= f
+    while (hi - lo > 1) {
+      int mid = (lo + hi) >> 1;
+      if (off[mid] <= f) lo = mid; else hi = mid;
+    }
+    return cand[(size_t)lo * chunk + (f - off[lo])];
+  }
   template <int NT, class F>
   DSA_DEVICE void for_each(F&& f) const {
-    for (int c = 0; c < n_chunks; ++c) {
-      uint32_t n = cnt[c];
-      const uint2* s = cand + (size_t)c * chunk;
-      for (uint32_t i = threadIdx.x; i < n; i += NT) f(s[i]);
+    constexpr int U = 8;
+    const uint32_t total = off[n_chunks];
+    for (uint32_t base = 0; base < total; base += NT * U) {
+      uint2 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        uint32_t fi = base + threadIdx.x + u * NT;
+        if (fi < total) v[u] = at(fi);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        uint32_t fi = base + threadIdx.x + u * NT;
+        if (fi < total) f(v[u]);
+      }
     }
   }
 };
@@ -109,81 +137,45 @@ DSA_DEVICE void radix_finish(const Src& src, uint64_t prefix, uint64_t mask, int
   }
 }
 
-// Final merge of one query (run by the last workgroup of that query).
-// Writes Kt = min(top_k, n_valid) entries (any order) and pads to top_k with
-// (-1, -inf).  lds_list has room for lcap (key, id) pairs; hist for kBins.
-template <int NT>
-DSA_DEVICE void merge_query(const uint2* cand, const uint32_t* cnt, int n_chunks, int chunk,
-                            const uint32_t* ghist_g, uint32_t n_valid, int top_k,
-                            int32_t* out_idx, float* out_score, uint2* lds_list, uint32_t lcap,
-                            uint32_t* hist, uint32_t* scratch) {
-  __shared__ uint32_t s_out, s_ln;
-  const uint32_t Kt = n_valid < (uint32_t)top_k ? n_valid : (uint32_t)top_k;
-  for (int i = Kt + threadIdx.x; i < top_k; i += NT) {
-    out_idx[i] = -1;
-    if (out_score) out_score[i] = -__builtin_inff();
-  }
-  if (Kt == 0) return;
-  for (int i = threadIdx.x; i < kBins; i += NT) hist[i] = __hip_atomic_load(
-      ghist_g + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (threadIdx.x == 0) { s_out = 0; s_ln = 0; }
-  __syncthreads();
-  uint32_t above;
-  const int bstar = block_find_threshold<NT>(hist, kBins, Kt, scratch, &above);
-  const uint32_t nb = hist[bstar];
-  const uint32_t need = Kt - above;
-  __syncthreads();
-  Emitter em{out_idx, out_score, &s_out, Kt};
-  SegSource seg{cand, cnt, n_chunks, chunk};
-  const bool fits = nb <= lcap;
-  seg.for_each<NT>([&](uint2 e) {
-    int b = (int)(e.x >> kBinShift);
-    if (b > bstar) {
-      em.put(e.x, (int32_t)e.y);
-    } else if (b == bstar && fits) {
-      uint32_t l = atomicAdd(&s_ln, 1u);
-      if (l < lcap) lds_list[l] = e;
-    }
-  });
-  __syncthreads();
-  const uint64_t prefix = (uint64_t)bstar << (64 - kBinBits);
-  const uint64_t mask = (uint64_t)(kBins - 1) << (64 - kBinBits);
-  if (fits) {
-    LdsSource src{lds_list, nb};
-    radix_finish<NT>(src, prefix, mask, 64 - kBinBits, need, nb, em, hist, scratch);
-  } else {
-    radix_finish<NT>(seg, prefix, mask, 64 - kBinBits, need, nb, em, hist, scratch);
-  }
-}
-
-// Chunk-local candidate emission.  skey[0..n) holds the chunk's score keys
-// (0 = invalid item).  Every entry whose 12-bit bin is >= the bin of the
-// chunk's k-th best is appended to seg (so the chunk's top-k is always
-// included); their bin counts are added to the query's global histogram.
-// Returns the number of valid items (all threads).
+// Chunk-side half of a selection pass (run by every chunk workgroup).
+// skey[0..n) holds the chunk's score keys (0 = invalid item); hist is LDS
+// scratch of kBins words.  Appends the chunk's candidates (key, id) to seg and
+// writes their count to *seg_cnt.
 template <int NT, class IdOf>
-DSA_DEVICE uint32_t chunk_emit(const uint32_t* skey, int n, int top_k, IdOf id_of,
-                               uint2* seg, uint32_t* seg_cnt, uint32_t* ghist_g,
-                               uint32_t* hist, uint32_t* scratch) {
+DSA_DEVICE void chunk_emit(const uint32_t* skey, int n, int top_k, IdOf id_of, uint2* seg,
+                           uint32_t* seg_cnt, uint32_t* ghist_g, uint32_t* hist,
+                           uint32_t* scratch) {
   __shared__ uint32_t s_cnt;
   for (int i = threadIdx.x; i < kBins; i += NT) hist[i] = 0;
   if (threadIdx.x == 0) s_cnt = 0;
   __syncthreads();
-  uint32_t nv = 0;
   for (int i = threadIdx.x; i < n; i += NT) {
     uint32_t k = skey[i];
-    if (k) { atomicAdd(&hist[k >> kBinShift], 1u); ++nv; }
+    if (k) atomicAdd(&hist[k >> kBinShift], 1u);
+  }
+  __syncthreads();
+  // publish this chunk's histogram, then read the query's running histogram
+  for (int b = threadIdx.x; b < kBins; b += NT) {
+    uint32_t h = hist[b];
+    if (h) atomicAdd(ghist_g + b, h);
+  }
+  __syncthreads();
+  uint32_t seen = 0;
+  for (int b = threadIdx.x; b < kBins; b += NT) {
+    uint32_t g = __hip_atomic_load(ghist_g + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t own = hist[b];
+    g = g > own ? g : own;                 // never below this chunk's own count
+    hist[b] = g;
+    seen += g;
   }
   uint32_t total;
-  (void)block_exclusive_sum<NT>(nv, scratch, &total);
+  (void)block_exclusive_sum<NT>(seen, scratch, &total);
   __syncthreads();
-  if (total == 0) {
-    if (threadIdx.x == 0) *seg_cnt = 0;
-    return 0;
+  int bc = 0;
+  if (total >= (uint32_t)top_k) {
+    uint32_t above;
+    bc = block_find_threshold<NT>(hist, kBins, (uint32_t)top_k, scratch, &above);
   }
-  const uint32_t kc = total < (uint32_t)top_k ? total : (uint32_t)top_k;
-  uint32_t above;
-  const int bc = block_find_threshold<NT>(hist, kBins, kc, scratch, &above);
   const int lane = lane_id();
   for (int base = 0; base < n; base += NT) {
     int i = base + (int)threadIdx.x;
@@ -198,13 +190,81 @@ DSA_DEVICE uint32_t chunk_emit(const uint32_t* skey, int n, int top_k, IdOf id_o
       seg[wbase + off] = make_uint2(k, (uint32_t)id_of(i));
     }
   }
-  for (int b = bc + (int)threadIdx.x; b < kBins; b += NT) {
-    uint32_t h = hist[b];
-    if (h) atomicAdd(ghist_g + b, h);
-  }
   __syncthreads();
   if (threadIdx.x == 0) *seg_cnt = s_cnt;
-  return total;
+}
+
+// Merge of one query's candidates (merge kernel, one workgroup per query).
+// ghist_g is the complete histogram of all the query's valid items; off_lds
+// must hold n_chunks + 1 words; lds_list room for lcap pairs; hist kBins words.
+// Writes Kt = min(top_k, valid items) entries (any order), then (-1, -inf).
+template <int NT>
+DSA_DEVICE void merge_query(const uint2* cand, const uint32_t* cnt, int n_chunks, int chunk,
+                            const uint32_t* ghist_g, int top_k, int32_t* out_idx,
+                            float* out_score, uint2* lds_list, uint32_t lcap, uint32_t* off_lds,
+                            uint32_t* hist, uint32_t* scratch) {
+  __shared__ uint32_t s_out, s_ln;
+  uint32_t nv = 0;
+  for (int i = threadIdx.x; i < kBins; i += NT) {
+    uint32_t h = ghist_g[i];
+    hist[i] = h;
+    nv += h;
+  }
+  uint32_t n_valid;
+  (void)block_exclusive_sum<NT>(nv, scratch, &n_valid);
+  // chunk offsets (segment counts clamped to the segment capacity)
+  uint32_t run = 0;
+  for (int base = 0; base < n_chunks; base += NT) {
+    int c = base + (int)threadIdx.x;
+    uint32_t v = 0;
+    if (c < n_chunks) {
+      v = cnt[c];
+      if (v > (uint32_t)chunk) v = (uint32_t)chunk;
+    }
+    uint32_t tot;
+    uint32_t ex = block_exclusive_sum<NT>(v, scratch, &tot);
+    if (c < n_chunks) off_lds[c] = run + ex;
+    run += tot;
+  }
+  if (threadIdx.x == 0) {
+    off_lds[n_chunks] = run;
+    s_out = 0;
+    s_ln = 0;
+  }
+  const uint32_t Kt = n_valid < (uint32_t)top_k ? n_valid : (uint32_t)top_k;
+  for (int i = Kt + threadIdx.x; i < top_k; i += NT) {
+    out_idx[i] = -1;
+    if (out_score) out_score[i] = -__builtin_inff();
+  }
+  __syncthreads();
+  if (Kt == 0) return;
+  uint32_t above;
+  const int bstar = block_find_threshold<NT>(hist, kBins, Kt, scratch, &above);
+  const uint32_t nb = hist[bstar];
+  const uint32_t need = Kt - above;
+  __syncthreads();
+  Emitter em{out_idx, out_score, &s_out, Kt};
+  FlatSegSource seg{cand, off_lds, n_chunks, chunk};
+  const bool fits = nb <= lcap;
+  seg.for_each<NT>([&](uint2 e) {
+    int b = (int)(e.x >> kBinShift);
+    if (b > bstar) {
+      em.put(e.x, (int32_t)e.y);
+    } else if (b == bstar && fits) {
+      uint32_t l = atomicAdd(&s_ln, 1u);
+      if (l < lcap) lds_list[l] = e;
+    }
+  });
+  __syncthreads();
+  const uint64_t prefix = (uint64_t)bstar << (64 - kBinBits);
+  const uint64_t mask = (uint64_t)(kBins - 1) << (64 - kBinBits);
+  if (fits) {
+    const uint32_t nl = s_ln < nb ? s_ln : nb;   // the list holds s_ln <= lcap entries
+    LdsSource src{lds_list, nl};
+    radix_finish<NT>(src, prefix, mask, 64 - kBinBits, need, nl, em, hist, scratch);
+  } else {
+    radix_finish<NT>(seg, prefix, mask, 64 - kBinBits, need, nb, em, hist, scratch);
+  }
 }
 
 }  // namespace dsa

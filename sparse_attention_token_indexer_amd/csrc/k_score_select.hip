@@ -1,16 +1,13 @@
-// Score-and-select kernel for decode-shaped indexer work.
+// Score-and-select kernels for decode-shaped indexer work.
 //
-// One workgroup = one query x one chunk of its items (prefix tokens, pooled
-// blocks, or a gathered candidate list).  Phase 1 streams the chunk's key rows
-// straight from HBM into MFMA operands (each lane one contiguous run of a key
-// row), computes the fused ReLU-weighted head reduction in registers and keeps
-// the chunk's scores in LDS only.  Phase 2 emits the chunk's candidates: every
-// entry whose 12-bit score bin is at or above the bin of the chunk's k-th best,
-// which always contains the chunk's share of the query's exact top-k (a chunk
-// cannot hold more winners than its own top-k).  Phase 3 runs in the last
-// workgroup to finish for that query (atomic arrival counter, release/acquire
-// fences) and merges all chunks' candidates into the exact top-k.  No score
-// vector is ever written to HBM.
+// k_score_emit: one workgroup = one query x one chunk of its items (prefix
+// tokens, pooled blocks, or a gathered candidate list).  It streams the chunk's
+// key rows straight from HBM into MFMA operands, computes the fused
+// ReLU-weighted head reduction in registers and keeps the chunk's scores in LDS
+// only; then it emits the chunk's candidates against a bound derived from the
+// query's running score histogram (see dsa_select.h).
+// k_merge: one workgroup per query merges the candidates into the exact top-k.
+// No score vector is ever written to HBM and no workgroup waits on another.
 //
 // Method: the DSA indexer scores every causal prefix token with H_I heads and
 // keeps the top-k (MISA summary, "problem" section); MISA's routed pass scores
@@ -25,8 +22,9 @@ namespace dsa {
 
 namespace {
 
-constexpr int kNT = 512;
+constexpr int kNT = 256;                 // score-and-emit workgroup
 constexpr int kNW = kNT / 64;
+constexpr int kMT = 1024;                // merge workgroup
 
 struct Row {
   int seq;
@@ -118,32 +116,22 @@ DSA_DEVICE void store_score(const SelArgs& a, int t, const Row& r, int64_t i0, i
   }
 }
 
+// Kernel 1 of a selection pass: score one chunk of one query, emit candidates.
 template <class SC, int MODE>
-__global__ __launch_bounds__(kNT) void k_score_select(SelArgs a) {
+__global__ __launch_bounds__(kNT) void k_score_emit(SelArgs a) {
   extern __shared__ uint32_t smem[];
   uint32_t* skey = smem;
   uint32_t* hist = smem + a.chunk;
   uint32_t* scratch = hist + kBins;
   float* sc_lds = reinterpret_cast<float*>(scratch + 64);
-  __shared__ int s_last;
 
-  const int t = blockIdx.y, c = blockIdx.x;
+  const int t = blockIdx.x, c = blockIdx.y;
   const Row r = row_of<MODE>(a, t);
-  int32_t* out_i = a.out_idx + (size_t)t * a.top_k;
-  float* out_s = a.out_score ? a.out_score + (size_t)t * a.top_k : nullptr;
-  if (r.n_items == 0) {
-    if (c == 0) {
-      for (int i = threadIdx.x; i < a.top_k; i += kNT) {
-        out_i[i] = -1;
-        if (out_s) out_s[i] = -__builtin_inff();
-      }
-    }
-    return;
-  }
+  if (r.n_items == 0) return;                       // the merge pads the row
   const int n_chunks_t = (int)((r.n_items + a.chunk - 1) / a.chunk);
   if (c >= n_chunks_t) return;
 
-  // ---- phase 1: scores of this chunk into LDS
+  // ---- scores of this chunk into LDS
   const size_t eb = a.f32 ? 4 : 2;
   const uint16_t* q_t = reinterpret_cast<const uint16_t*>(
       reinterpret_cast<const char*>(a.q) + (size_t)t * a.n_heads * a.head_dim * eb);
@@ -175,7 +163,7 @@ __global__ __launch_bounds__(kNT) void k_score_select(SelArgs a) {
   }
   __syncthreads();
 
-  // ---- phase 2: this chunk's candidates
+  // ---- this chunk's candidates
   uint2* seg = a.cand + ((size_t)t * a.n_chunks + c) * (size_t)a.chunk;
   auto id_of = [&](int i) -> int32_t {
     int32_t id;
@@ -183,37 +171,46 @@ __global__ __launch_bounds__(kNT) void k_score_select(SelArgs a) {
     item_of<MODE>(a, t, r, i0 + i, id, p);
     return id;
   };
-  uint32_t nv = chunk_emit<kNT>(skey, n_c, a.top_k, id_of, seg,
-                                a.cand_cnt + (size_t)t * a.n_chunks + c,
-                                a.ghist + (size_t)t * kBins, hist, scratch);
-  if (threadIdx.x == 0 && nv) atomicAdd(a.nvalid + t, nv);
-
-  // ---- phase 3: the last chunk of this query to finish merges
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t done = atomicAdd(a.counter + t, 1u);
-    s_last = (done == (uint32_t)(n_chunks_t - 1));
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  const uint32_t n_valid = __hip_atomic_load(a.nvalid + t, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT);
-  merge_query<kNT>(a.cand + (size_t)t * a.n_chunks * a.chunk, a.cand_cnt + (size_t)t * a.n_chunks,
-                   n_chunks_t, a.chunk, a.ghist + (size_t)t * kBins, n_valid, a.top_k, out_i, out_s,
-                   reinterpret_cast<uint2*>(skey), (uint32_t)(a.chunk / 2), hist, scratch);
+  chunk_emit<kNT>(skey, n_c, a.top_k, id_of, seg, a.cand_cnt + (size_t)t * a.n_chunks + c,
+                  a.ghist + (size_t)t * kBins, hist, scratch);
 }
+
+// Kernel 2 of a selection pass: exact merge of one query's candidates.
+template <int MODE>
+__global__ __launch_bounds__(kMT) void k_merge(SelArgs a) {
+  extern __shared__ uint32_t smem[];
+  uint32_t* hist = smem;                              // [kBins]
+  uint32_t* scratch = hist + kBins;                   // [64]
+  uint32_t* off = scratch + 64;                       // [kMaxChunks + 1]
+  uint2* list = reinterpret_cast<uint2*>(off + kMaxChunks + 1 + 1);   // 8-byte aligned
+  const int t = blockIdx.x;
+  const Row r = row_of<MODE>(a, t);
+  const int n_chunks_t = (int)((r.n_items + a.chunk - 1) / a.chunk);
+  merge_query<kMT>(a.cand + (size_t)t * a.n_chunks * a.chunk, a.cand_cnt + (size_t)t * a.n_chunks,
+                   n_chunks_t, a.chunk, a.ghist + (size_t)t * kBins, a.top_k,
+                   a.out_idx + (size_t)t * a.top_k,
+                   a.out_score ? a.out_score + (size_t)t * a.top_k : nullptr, list, kMergeListCap,
+                   off, hist, scratch);
+}
+
+constexpr size_t kMergeLds = (kBins + 64 + kMaxChunks + 2) * 4 + (size_t)kMergeListCap * 8;
 
 template <class SC, int MODE>
 hipError_t launch_t(const SelArgs& a, hipStream_t stream) {
+  if (a.n_chunks > kMaxChunks) return hipErrorInvalidValue;
   const size_t lds = score_select_lds_bytes(a.chunk, a.f32, a.head_dim);
-  auto kern = k_score_select<SC, MODE>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+  auto k1 = k_score_emit<SC, MODE>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k1),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  dim3 grid(a.n_chunks, a.nq);
-  hipLaunchKernelGGL(kern, grid, dim3(kNT), lds, stream, a);
+  auto k2 = k_merge<MODE>;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(k2),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMergeLds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k1, dim3(a.nq, a.n_chunks), dim3(kNT), lds, stream, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k2, dim3(a.nq), dim3(kMT), kMergeLds, stream, a);
   return hipGetLastError();
 }
 
