@@ -181,16 +181,17 @@ int indexer_selection_iou(const int32_t* a, const int32_t* b, int32_t nq, int32_
  * pending records.  Not thread-safe against concurrent calls that record.
  */
 #define DSA_KERNEL_PREPARE 0      /* workspace clear + partial-block pooling */
-#define DSA_KERNEL_SCORE_TOKENS 1 /* score-and-select over prefix tokens */
-#define DSA_KERNEL_SCORE_POOLED 2 /* score-and-select over pooled blocks (HISA stage 1) */
-#define DSA_KERNEL_SCORE_LIST 3   /* score-and-select over a candidate list (MISA dagger) */
-#define DSA_KERNEL_SCORE_BLOCKS 4 /* score-and-select over surviving blocks (HISA stage 2) */
+#define DSA_KERNEL_SCORE_TOKENS 1 /* score-and-emit over prefix tokens */
+#define DSA_KERNEL_SCORE_POOLED 2 /* score-and-emit over pooled blocks (HISA stage 1) */
+#define DSA_KERNEL_SCORE_LIST 3   /* score-and-emit over a candidate list (MISA dagger) */
+#define DSA_KERNEL_SCORE_BLOCKS 4 /* score-and-emit over surviving blocks (HISA stage 2) */
 #define DSA_KERNEL_ROUTE 5        /* MISA router */
 #define DSA_KERNEL_POOL 6         /* mean pooling */
 #define DSA_KERNEL_IOU 7
 #define DSA_KERNEL_PREFILL 8      /* prefill-shaped scoring */
 #define DSA_KERNEL_ROWSELECT 9    /* prefill row selection */
-#define DSA_KERNEL_KINDS 10
+#define DSA_KERNEL_MERGE 10       /* exact top-k merge after a score-and-emit kernel */
+#define DSA_KERNEL_KINDS 11
 int dsa_kernel_timing(int enable);
 int dsa_kernel_timing_read(int32_t kind, int64_t* launches, double* total_ms, double* min_ms,
                            double* max_ms);

@@ -89,8 +89,11 @@ hipError_t timed_pool(hipStream_t stream, F&& f) {
   return timed(DSA_KERNEL_POOL, stream, f);
 }
 
+// One selection pass: the score-and-emit kernel, then the merge kernel.
 hipError_t run_score_select(const dsa::SelArgs& a, hipStream_t stream) {
-  return timed(score_kind(a.mode), stream, [&] { return dsa::launch_score_select(a, stream); });
+  hipError_t e = timed(score_kind(a.mode), stream, [&] { return dsa::launch_score_emit(a, stream); });
+  if (e != hipSuccess) return e;
+  return timed(DSA_KERNEL_MERGE, stream, [&] { return dsa::launch_merge(a, stream); });
 }
 
 constexpr int kBins = 4096;

@@ -39,8 +39,10 @@ struct SelArgs {
   float* out_score;            // [nq, top_k] or null
 };
 
-// Launches the score-and-emit kernel, then the merge kernel, on `stream`.
-hipError_t launch_score_select(const SelArgs& a, hipStream_t stream);
+// A selection pass is the score-and-emit kernel followed by the merge kernel,
+// launched in that order on one stream.
+hipError_t launch_score_emit(const SelArgs& a, hipStream_t stream);
+hipError_t launch_merge(const SelArgs& a, hipStream_t stream);
 constexpr int kMaxChunks = 8192;        // chunks per query in one pass
 constexpr int kMergeListCap = 12288;    // tie-bin entries resolved in LDS
 size_t score_select_lds_bytes(int chunk, int f32, int head_dim);

@@ -203,12 +203,16 @@ hipError_t launch_t(const SelArgs& a, hipStream_t stream) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k1),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  auto k2 = k_merge<MODE>;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(k2),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMergeLds);
-  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k1, dim3(a.nq, a.n_chunks), dim3(kNT), lds, stream, a);
-  e = hipGetLastError();
+  return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t launch_merge_t(const SelArgs& a, hipStream_t stream) {
+  if (a.n_chunks > kMaxChunks) return hipErrorInvalidValue;
+  auto k2 = k_merge<MODE>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k2),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMergeLds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k2, dim3(a.nq), dim3(kMT), kMergeLds, stream, a);
   return hipGetLastError();
@@ -233,7 +237,17 @@ size_t score_select_lds_bytes(int chunk, int f32, int head_dim) {
   return b;
 }
 
-hipError_t launch_score_select(const SelArgs& a, hipStream_t stream) {
+hipError_t launch_merge(const SelArgs& a, hipStream_t stream) {
+  switch (a.mode) {
+    case MODE_RANGE: return launch_merge_t<MODE_RANGE>(a, stream);
+    case MODE_POOLED: return launch_merge_t<MODE_POOLED>(a, stream);
+    case MODE_LIST: return launch_merge_t<MODE_LIST>(a, stream);
+    case MODE_BLOCKS: return launch_merge_t<MODE_BLOCKS>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_score_emit(const SelArgs& a, hipStream_t stream) {
   if (a.f32) {
     if (a.mode != MODE_RANGE) return hipErrorInvalidValue;
     if (a.head_dim == 64) return launch_t<ScorerF32<64>, MODE_RANGE>(a, stream);

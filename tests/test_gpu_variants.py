@@ -1,0 +1,197 @@
+"""GPU parity of MISA, MISA dagger and HISA against the CPU oracle.
+
+Every stage is checked on its own, conditionally on the GPU's own upstream
+choice: the routed heads against the oracle's importance, the coarse
+candidates against the oracle's routed scores given those heads, the final
+selection against the oracle's scores over the GPU's candidates.  A near-tie
+upstream therefore cannot turn into a false failure downstream.
+"""
+import numpy as np
+import pytest
+import torch
+
+import datagen
+from oracle import indexer as O
+from oracle.check import FLOOR, RTOL, check_selection
+
+from _helpers import say, upload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_attention_token_indexer_amd as m
+    m.lib()
+    return m
+
+
+def _rows(inp, wl, t):
+    s = int(inp["q_seq"][t])
+    return (O.to_f64(inp["q"][t], wl.dtype), inp["w"][t].astype(np.float64),
+            O.to_f64(inp["k"][s], wl.dtype), int(inp["q_pos"][t]))
+
+
+def _check(gi, gv, cand, s, A, k, q_t, w_t, K, what, heads=None):
+    qq, ww = (q_t, w_t) if heads is None else (q_t[heads], w_t[heads])
+    F = O.dot_magnitude(qq, ww, K[cand]) if cand.size else np.zeros(0)
+    return check_selection(gi, gv, cand, s, A, k, F, what=what)
+
+
+def _misa_case(dsa, wl, h, k, kprime, seed=0, pos=None, pooled=True):
+    inp = datagen.make(wl, seed)
+    if pos is not None:
+        inp["q_pos"] = np.asarray(pos, dtype=np.int32)
+    say(f"[misa] nq={wl.nq} L={wl.l_max} H={wl.n_heads} B={wl.block} h={h} k={k} k'={kprime} "
+        f"pooled={pooled}")
+    dev = upload(inp, wl)
+    kp = dsa.indexer_mean_pool_keys(dev["k"], wl.block) if pooled else None
+    res = dsa.misa_route_score_topk(dev["q"], dev["w"], dev["k"], dev["q_pos"], dev["q_seq"],
+                                    block=wl.block, n_active_heads=h, top_k=k, k_prime=kprime,
+                                    k_pooled=kp, with_importance=True, with_cand=kprime > 0)
+    torch.cuda.synchronize()
+    out = {key: v.cpu().numpy() for key, v in res.items() if v is not None}
+    errs = []
+    for t in range(wl.nq):
+        q_t, w_t, K, p = _rows(inp, wl, t)
+        pooled_ref = O.misa_pooled_for_query(K, wl.block, p)
+        I = O.misa_importance(q_t, w_t, pooled_ref)
+        Fi = np.abs(w_t) * (np.abs(q_t) @ np.abs(pooled_ref).T).sum(axis=1)
+        # router importance and head choice
+        gi = out["importance"][t].astype(np.float64)
+        bad = np.abs(gi - I) > RTOL * I + FLOOR * Fi
+        if bad.any():
+            errs.append(f"importance q{t}: heads {np.nonzero(bad)[0][:4]} gpu {gi[bad][:4]} ref {I[bad][:4]}")
+        errs += check_selection(out["heads"][t], None, np.arange(wl.n_heads), I, I, h, Fi,
+                                what=f"heads q{t}")
+        heads = out["heads"][t].astype(np.int64)
+        # routed pass, conditional on the GPU's heads
+        r = O.misa_row(q_t, w_t, K, p, wl.block, h, kprime or k, heads=heads)
+        if kprime == 0:
+            errs += _check(out["idx"][t], out["score"][t], r["cand"], r["s"], r["A"], k,
+                           q_t, w_t, K, f"misa q{t}", heads)
+        else:
+            errs += _check(out["cand"][t], None, r["cand"], r["s"], r["A"], kprime,
+                           q_t, w_t, K, f"coarse q{t}", heads)
+            f = O.rescore_row(q_t, w_t, K, out["cand"][t], k)
+            errs += _check(out["idx"][t], out["score"][t], f["cand"], f["s"], f["A"], k,
+                           q_t, w_t, K, f"dagger q{t}")
+    assert not errs, "\n".join(errs[:12])
+    return inp, out
+
+
+def test_misa_reduced(dsa):
+    wl = datagen.small(4, nq=8, n_seq=8, l_max=16384)
+    _misa_case(dsa, wl, h=8, k=256, kprime=0)
+
+
+def test_misa_dagger_reduced(dsa):
+    wl = datagen.small(4, nq=8, n_seq=8, l_max=16384)
+    _misa_case(dsa, wl, h=8, k=256, kprime=1024)
+
+
+def test_misa_partial_blocks_and_internal_pooling(dsa):
+    """Queries on one shared cache at positions that end inside a block: the
+    partial last block is pooled over its valid tokens only; the call pools the
+    cache itself when no pooled keys are given."""
+    wl = datagen.small(4, nq=6, n_seq=1, l_max=9000, layout="tail", plant="points", n_plant=60)
+    pos = [0, 63, 64, 100, 4097, 8999]
+    for pooled in (True, False):
+        _misa_case(dsa, wl, h=8, k=128, kprime=512, pos=pos, pooled=pooled)
+        _misa_case(dsa, wl, h=3, k=50, kprime=0, pos=pos, pooled=pooled)
+
+
+def test_misa_all_heads_equals_dense(dsa):
+    """h = H_I routes every head: the selection must be the dense indexer's."""
+    wl = datagen.small(4, nq=4, n_seq=4, l_max=8192)
+    inp = datagen.make(wl, 2)
+    dev = upload(inp, wl)
+    res = dsa.misa_route_score_topk(dev["q"], dev["w"], dev["k"], dev["q_pos"], dev["q_seq"],
+                                    block=64, n_active_heads=64, top_k=300)
+    gi, gv = res["idx"].cpu().numpy(), res["score"].cpu().numpy()
+    errs = []
+    for t in range(4):
+        q_t, w_t, K, p = _rows(inp, wl, t)
+        d = O.dense_row(q_t, w_t, K, p, 300)
+        errs += _check(gi[t], gv[t], d["cand"], d["s"], d["A"], 300, q_t, w_t, K, f"q{t}")
+    assert not errs, "\n".join(errs[:8])
+
+
+def test_misa_dagger_full_candidate_set_equals_dense(dsa):
+    """k' >= prefix length keeps every token, so the rescored top-k is dense."""
+    wl = datagen.small(4, nq=4, n_seq=4, l_max=3000)
+    inp = datagen.make(wl, 3)
+    dev = upload(inp, wl)
+    res = dsa.misa_route_score_topk(dev["q"], dev["w"], dev["k"], dev["q_pos"], dev["q_seq"],
+                                    block=64, n_active_heads=8, top_k=200, k_prime=4096)
+    gi, gv = res["idx"].cpu().numpy(), res["score"].cpu().numpy()
+    errs = []
+    for t in range(4):
+        q_t, w_t, K, p = _rows(inp, wl, t)
+        d = O.dense_row(q_t, w_t, K, p, 200)
+        errs += _check(gi[t], gv[t], d["cand"], d["s"], d["A"], 200, q_t, w_t, K, f"q{t}")
+    assert not errs, "\n".join(errs[:8])
+
+
+def _hisa_case(dsa, wl, m, k, seed=0, pos=None, pooled=True):
+    inp = datagen.make(wl, seed)
+    if pos is not None:
+        inp["q_pos"] = np.asarray(pos, dtype=np.int32)
+    say(f"[hisa] nq={wl.nq} L={wl.l_max} H={wl.n_heads} B={wl.block} m={m} k={k} pooled={pooled}")
+    dev = upload(inp, wl)
+    kp = dsa.indexer_mean_pool_keys(dev["k"], wl.block) if pooled else None
+    res = dsa.hisa_block_filter_topk(dev["q"], dev["w"], dev["k"], dev["q_pos"], dev["q_seq"],
+                                     block=wl.block, m_blocks=m, top_k=k, k_pooled=kp)
+    torch.cuda.synchronize()
+    out = {key: v.cpu().numpy() for key, v in res.items()}
+    errs = []
+    for t in range(wl.nq):
+        q_t, w_t, K, p = _rows(inp, wl, t)
+        pooled_ref = O.misa_pooled_for_query(K, wl.block, p)
+        bs, bA = O.hisa_block_scores(q_t, w_t, pooled_ref)
+        Fb = O.dot_magnitude(q_t, w_t, pooled_ref)
+        errs += check_selection(out["blocks"][t], out["block_score"][t],
+                                np.arange(pooled_ref.shape[0]), bs, bA, m, Fb, what=f"blocks q{t}")
+        r = O.hisa_row(q_t, w_t, K, p, wl.block, m, k, blocks=out["blocks"][t])
+        errs += _check(out["idx"][t], out["score"][t], r["cand"], r["s"], r["A"], k,
+                       q_t, w_t, K, f"hisa q{t}")
+    assert not errs, "\n".join(errs[:12])
+    return inp, out
+
+
+def test_hisa_reduced(dsa):
+    wl = datagen.small(5, nq=8, n_seq=8, l_max=65536, n_plant=48)
+    _hisa_case(dsa, wl, m=16, k=512)
+
+
+def test_hisa_partial_blocks_and_internal_pooling(dsa):
+    wl = datagen.small(5, nq=6, n_seq=1, l_max=9000, layout="tail", plant="points", n_plant=60)
+    pos = [0, 127, 128, 300, 4097, 8999]
+    for pooled in (True, False):
+        _hisa_case(dsa, wl, m=8, k=200, pos=pos, pooled=pooled)
+
+
+def test_hisa_all_blocks_equals_dense_and_iou(dsa):
+    """m >= M keeps every block, so HISA equals dense; with m < M the IoU kernel
+    agrees with the oracle's IoU of the same two selections."""
+    wl = datagen.small(5, nq=4, n_seq=4, l_max=16384, n_plant=24)
+    inp = datagen.make(wl, 4)
+    dev = upload(inp, wl)
+    M = 16384 // wl.block
+    res = dsa.hisa_block_filter_topk(dev["q"], dev["w"], dev["k"], dev["q_pos"], dev["q_seq"],
+                                     block=wl.block, m_blocks=M, top_k=256)
+    dn, _ = dsa.indexer_score_topk(dev["q"], dev["w"], dev["k"], dev["q_pos"], dev["q_seq"], top_k=256)
+    gi, gv = res["idx"].cpu().numpy(), res["score"].cpu().numpy()
+    errs = []
+    for t in range(4):
+        q_t, w_t, K, p = _rows(inp, wl, t)
+        d = O.dense_row(q_t, w_t, K, p, 256)
+        errs += _check(gi[t], gv[t], d["cand"], d["s"], d["A"], 256, q_t, w_t, K, f"q{t}")
+    assert not errs, "\n".join(errs[:8])
+    small = dsa.hisa_block_filter_topk(dev["q"], dev["w"], dev["k"], dev["q_pos"], dev["q_seq"],
+                                       block=wl.block, m_blocks=8, top_k=256)
+    iou = dsa.indexer_selection_iou(small["idx"], dn).cpu().numpy()
+    ref = O.iou_rows(small["idx"].cpu().numpy(), dn.cpu().numpy())
+    np.testing.assert_allclose(iou, ref, rtol=1e-6)
