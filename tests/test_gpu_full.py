@@ -1,0 +1,148 @@
+"""GPU parity at the full workload sizes, in the launch configuration bench.py
+times; the oracle checks sampled queries one by one (keys of the sampled
+queries' sequences are regenerated on the host from the same seeds)."""
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+import torch
+
+import datagen
+from oracle import indexer as O
+from oracle.check import check_selection
+
+from _helpers import say, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_attention_token_indexer_amd as m
+    m.lib()
+    return m
+
+
+def _device_inputs(wl, seed=0):
+    """q, w, positions on the device; K generated per sequence straight into a
+    device tensor (host memory stays at one sequence per worker)."""
+    q, w = datagen.queries(wl, seed)
+    q_seq, q_pos = datagen.positions(wl)
+    kdev = torch.empty((wl.n_seq, wl.l_max, wl.head_dim), dtype=torch.bfloat16, device="cuda")
+    with ThreadPoolExecutor(max_workers=16) as ex:
+        for s, ks in enumerate(ex.map(lambda s: datagen.keys(wl, s, q, w, seed), range(wl.n_seq))):
+            kdev[s].copy_(to_device(ks, wl.dtype))
+    dev = {"q": to_device(q, wl.dtype), "w": torch.from_numpy(w).cuda(), "k": kdev,
+           "q_seq": torch.from_numpy(q_seq).cuda(), "q_pos": torch.from_numpy(q_pos).cuda()}
+    return dev, {"q": q, "w": w, "q_seq": q_seq, "q_pos": q_pos}
+
+
+def _host_row(wl, hostin, t, seed=0):
+    s = int(hostin["q_seq"][t])
+    K = O.to_f64(datagen.keys(wl, s, hostin["q"], hostin["w"], seed), wl.dtype)
+    return O.to_f64(hostin["q"][t], wl.dtype), hostin["w"][t].astype(np.float64), K, int(hostin["q_pos"][t])
+
+
+def _check(gi, gv, r, k, q_t, w_t, K, what, heads=None):
+    qq, ww = (q_t, w_t) if heads is None else (q_t[heads], w_t[heads])
+    F = O.dot_magnitude(qq, ww, K[r["cand"]])
+    return check_selection(gi, gv, r["cand"], r["s"], r["A"], k, F, what=what)
+
+
+def test_dense_decode_full(dsa):
+    """64 queries x 131072 keys, 64 heads, d 128, bf16, k 2048: every query."""
+    wl = datagen.WORKLOADS[2]
+    say("[full] dense decode 64 x 131072")
+    dev, h = _device_inputs(wl)
+    idx, val = dsa.indexer_score_topk(dev["q"], dev["w"], dev["k"], dev["q_pos"], dev["q_seq"],
+                                      top_k=wl.top_k)
+    gi, gv = idx.cpu().numpy(), val.cpu().numpy()
+    errs = []
+    for t in range(wl.nq):
+        q_t, w_t, K, p = _host_row(wl, h, t)
+        r = O.dense_row(q_t, w_t, K, p, wl.top_k)
+        errs += _check(gi[t], gv[t], r, wl.top_k, q_t, w_t, K, f"q{t}")
+    assert not errs, "\n".join(errs[:10])
+
+
+def test_misa_full(dsa):
+    """64 x 131072, B 64, h 8 of 64 heads, k 2048 (MISA) and k' 8192 (dagger)."""
+    wl = datagen.WORKLOADS[4]
+    say("[full] MISA 64 x 131072")
+    dev, h = _device_inputs(wl)
+    kp = dsa.indexer_mean_pool_keys(dev["k"], wl.block)
+    m = dsa.misa_route_score_topk(dev["q"], dev["w"], dev["k"], dev["q_pos"], dev["q_seq"],
+                                  block=wl.block, n_active_heads=wl.n_active_heads,
+                                  top_k=wl.top_k, k_pooled=kp)
+    md = dsa.misa_route_score_topk(dev["q"], dev["w"], dev["k"], dev["q_pos"], dev["q_seq"],
+                                   block=wl.block, n_active_heads=wl.n_active_heads,
+                                   top_k=wl.top_k, k_prime=wl.k_prime, k_pooled=kp, with_cand=True)
+    mi, mv, heads = (m[x].cpu().numpy() for x in ("idx", "score", "heads"))
+    di, dv, cand, dheads = (md[x].cpu().numpy() for x in ("idx", "score", "cand", "heads"))
+    assert np.array_equal(heads, dheads)
+    errs = []
+    for t in range(0, wl.nq, 8):
+        q_t, w_t, K, p = _host_row(wl, h, t)
+        pooled = O.misa_pooled_for_query(K, wl.block, p)
+        I = O.misa_importance(q_t, w_t, pooled)
+        errs += check_selection(heads[t], None, np.arange(wl.n_heads), I, I, wl.n_active_heads,
+                                what=f"heads q{t}")
+        hs = heads[t].astype(np.int64)
+        r = O.misa_row(q_t, w_t, K, p, wl.block, wl.n_active_heads, wl.k_prime, heads=hs)
+        errs += _check(cand[t], None, r, wl.k_prime, q_t, w_t, K, f"coarse q{t}", hs)
+        rk = dict(r)
+        errs += _check(mi[t], mv[t], rk, wl.top_k, q_t, w_t, K, f"misa q{t}", hs)
+        f = O.rescore_row(q_t, w_t, K, cand[t], wl.top_k)
+        errs += _check(di[t], dv[t], f, wl.top_k, q_t, w_t, K, f"dagger q{t}")
+    assert not errs, "\n".join(errs[:10])
+
+
+def test_hisa_full_with_iou(dsa):
+    """32 queries x 1048576 keys, 32 heads, B 128, m 64, k 2048; IoU against the
+    dense 32-head indexer on the same inputs."""
+    wl = datagen.WORKLOADS[5]
+    say("[full] HISA 32 x 1048576")
+    dev, h = _device_inputs(wl)
+    kp = dsa.indexer_mean_pool_keys(dev["k"], wl.block)
+    r = dsa.hisa_block_filter_topk(dev["q"], dev["w"], dev["k"], dev["q_pos"], dev["q_seq"],
+                                   block=wl.block, m_blocks=wl.m_blocks, top_k=wl.top_k, k_pooled=kp)
+    dn, _ = dsa.indexer_score_topk(dev["q"], dev["w"], dev["k"], dev["q_pos"], dev["q_seq"],
+                                   top_k=wl.top_k)
+    iou = dsa.indexer_selection_iou(r["idx"], dn).cpu().numpy()
+    hi, hv, blocks, bsc = (r[x].cpu().numpy() for x in ("idx", "score", "blocks", "block_score"))
+    dni = dn.cpu().numpy()
+    np.testing.assert_allclose(iou, O.iou_rows(hi, dni), rtol=1e-6)
+    say(f"[full] HISA IoU vs dense: mean {iou.mean():.4f} min {iou.min():.4f}")
+    errs = []
+    for t in (0, 13, 31):
+        q_t, w_t, K, p = _host_row(wl, h, t)
+        pooled = O.misa_pooled_for_query(K, wl.block, p)
+        bs, bA = O.hisa_block_scores(q_t, w_t, pooled)
+        errs += check_selection(blocks[t], bsc[t], np.arange(pooled.shape[0]), bs, bA, wl.m_blocks,
+                                O.dot_magnitude(q_t, w_t, pooled), what=f"blocks q{t}")
+        rr = O.hisa_row(q_t, w_t, K, p, wl.block, wl.m_blocks, wl.top_k, blocks=blocks[t])
+        errs += _check(hi[t], hv[t], rr, wl.top_k, q_t, w_t, K, f"hisa q{t}")
+        d = O.dense_row(q_t, w_t, K, p, wl.top_k)
+        errs += _check(dni[t], None, d, wl.top_k, q_t, w_t, K, f"dense q{t}")
+    assert not errs, "\n".join(errs[:10])
+
+
+def test_dense_prefill_full_sampled_rows(dsa):
+    """32768 causal rows x 32768 keys, 64 heads, k 2048 (rows shorter than k
+    return every key); sampled rows across the triangle."""
+    wl = datagen.WORKLOADS[3]
+    say("[full] dense prefill 32768 x 32768")
+    dev, h = _device_inputs(wl)
+    idx, val = dsa.indexer_score_topk(dev["q"], dev["w"], dev["k"], dev["q_pos"], None,
+                                      top_k=wl.top_k)
+    rows = [0, 1, 2046, 2047, 2048, 5000, 16383, 32767]
+    gi, gv = idx[rows].cpu().numpy(), val[rows].cpu().numpy()
+    K = O.to_f64(datagen.keys(wl, 0, h["q"], h["w"]), wl.dtype)
+    errs = []
+    for i, t in enumerate(rows):
+        q_t, w_t = O.to_f64(h["q"][t], wl.dtype), h["w"][t].astype(np.float64)
+        r = O.dense_row(q_t, w_t, K, t, wl.top_k)
+        errs += _check(gi[i], gv[i], r, wl.top_k, q_t, w_t, K, f"row {t}")
+    assert not errs, "\n".join(errs[:10])
