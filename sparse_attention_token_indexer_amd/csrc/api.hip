@@ -209,7 +209,7 @@ DensePlan plan_dense(int64_t nq, int head_dim, int64_t l_max, int f32) {
 
 struct MisaPlan {
   StagePlan s0, s1;
-  size_t route_counter = 0, zero_bytes = 0, part = 0, heads = 0, cand_list = 0, partial = 0, pooled = 0;
+  size_t zero_bytes = 0, part = 0, cand_list = 0, partial = 0, pooled = 0;
   size_t total = 0;
   int splits = 1, bps = 1;
   int64_t m_max = 0;
@@ -222,7 +222,6 @@ MisaPlan plan_misa(int64_t nq, int n_heads, int head_dim, int n_seq, int64_t l_m
   p.m_max = cdiv(l_max, block);
   plan_zero(A, p.s0, nq);
   if (k_prime > 0) plan_zero(A, p.s1, nq);
-  p.route_counter = A.take((size_t)nq * 4);
   p.zero_bytes = A.off;
   // router: about kTargetWorkgroups workgroups, at least 64 blocks each
   int64_t bps = 64;
@@ -230,7 +229,7 @@ MisaPlan plan_misa(int64_t nq, int n_heads, int head_dim, int n_seq, int64_t l_m
   p.bps = (int)bps;
   p.splits = (int)cdiv(p.m_max, bps);
   p.part = A.take((size_t)nq * p.splits * n_heads * 4);
-  p.heads = A.take((size_t)nq * h * 4);
+  (void)h;
   plan_cand(A, p.s0, nq, l_max, 0, head_dim);
   if (k_prime > 0) {
     p.cand_list = A.take((size_t)nq * k_prime * 4);
@@ -447,7 +446,6 @@ int misa_route_score_topk(const void* q, const float* w, const void* k, const vo
   // router
   dsa::RouteArgs ra{};
   ra.q = reinterpret_cast<const uint16_t*>(q);
-  ra.w = w;
   ra.pooled = pooled;
   ra.partial = partial;
   ra.q_seq = q_seq;
@@ -457,24 +455,21 @@ int misa_route_score_topk(const void* q, const float* w, const void* k, const vo
   ra.head_dim = head_dim;
   ra.n_seq = n_seq;
   ra.block = block;
-  ra.h = n_active_heads;
   ra.splits = p.splits;
   ra.blocks_per_split = p.bps;
   ra.l_max = l_max;
   ra.m_max = p.m_max;
   ra.part = at<float>(workspace, p.part);
-  ra.counter = at<uint32_t>(workspace, p.route_counter);
-  ra.heads = at<int32_t>(workspace, p.heads);
-  ra.out_heads = out_heads;
-  ra.out_importance = out_importance;
   if ((st = hip_status(timed(DSA_KERNEL_ROUTE, stream, [&] { return dsa::launch_route(ra, stream); }),
                        "router kernel", stream))) return st;
   // routed token pass
   dsa::SelArgs a = stage_args(p.s0, workspace);
   fill_common(a, q, w, k, q_seq, q_pos, nq, n_heads, head_dim, n_seq, l_max);
   a.h_use = n_active_heads;
-  a.heads = ra.heads;
-  a.heads_stride = n_active_heads;
+  a.route_part = ra.part;
+  a.route_splits = ra.splits;
+  a.out_heads = out_heads;
+  a.out_importance = out_importance;
   a.mode = dsa::MODE_RANGE;
   if (k_prime == 0) {
     a.top_k = top_k;

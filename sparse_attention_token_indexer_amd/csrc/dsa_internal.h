@@ -23,7 +23,11 @@ struct SelArgs {
   const uint16_t* partial;     // [nq, D] bf16 (POOLED), may be null
   const int32_t* q_seq;        // [nq] or null (all 0)
   const int32_t* q_pos;        // [nq]
-  const int32_t* heads;        // [nq, heads_stride] routed heads, or null = all
+  const int32_t* heads;        // [nq, heads_stride] given heads, or null = all
+  const float* route_part;     // [nq, route_splits, n_heads] router sums, or null
+  int route_splits;            // (route_part given: heads are the top h_use by importance)
+  int32_t* out_heads;          // [nq, h_use] routed heads or null (route_part given)
+  float* out_importance;       // [nq, n_heads] router importance or null
   const int32_t* list;         // LIST / BLOCKS
   int nq, n_heads, h_use, heads_stride, head_dim, n_seq;
   int64_t l_max, m_max;
@@ -66,20 +70,18 @@ hipError_t launch_mean_pool(const uint16_t* k, int n_seq, int64_t l_max, int hea
                             uint16_t* out, hipStream_t stream);
 
 // MISA router: per-head importance from pooled keys and top-h head selection.
+// The router kernel writes, per query and slice of pooled blocks, the per-head
+// sums of max(0, q_j . kbar_b); the routed scoring pass adds the slices in slice
+// order, weights by |w_j| and ranks the heads itself (route_heads below).
 struct RouteArgs {
   const uint16_t* q;           // [nq, n_heads, D]
-  const float* w;              // [nq, n_heads]
   const uint16_t* pooled;      // [n_seq, m_max, D]
   const uint16_t* partial;     // [nq, D] or null
   const int32_t* q_seq;
   const int32_t* q_pos;
-  int nq, n_heads, head_dim, n_seq, block, h, splits, blocks_per_split;
+  int nq, n_heads, head_dim, n_seq, block, splits, blocks_per_split;
   int64_t l_max, m_max;
   float* part;                 // [nq, splits, n_heads] workspace
-  uint32_t* counter;           // [nq] (zeroed)
-  int32_t* heads;              // [nq, h] (workspace)
-  int32_t* out_heads;          // [nq, h] or null
-  float* out_importance;       // [nq, n_heads] or null
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream);
 

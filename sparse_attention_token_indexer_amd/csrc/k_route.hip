@@ -10,9 +10,9 @@
 //
 // One workgroup = one query x one slice of its blocks; bf16 MFMA with heads as
 // rows and pooled blocks as columns, the ReLU'd affinities summed per head in
-// registers, then across lanes and waves in a fixed order.  The last workgroup
-// of a query (arrival counter) adds the slices in slice order, weights by |w|
-// and ranks the heads.
+// registers, then across lanes and waves in a fixed order, and written per
+// slice.  The routed scoring pass adds the slices in slice order, weights by |w|
+// and ranks the heads (route_heads in k_score_select.hip), so no workgroup waits on another.
 #include "dsa_internal.h"
 #include "dsa_common.h"
 
@@ -26,8 +26,6 @@ template <int HT, int D>
 __global__ __launch_bounds__(kRT) void k_route(RouteArgs a) {
   constexpr int S = D / 16;
   __shared__ float s_part[kRT / 64][64];
-  __shared__ float s_I[64];
-  __shared__ int s_last;
   const int t = blockIdx.y, sp = blockIdx.x;
   const int lane = lane_id(), wv = wave_id(), h = lane >> 5, n = lane & 31;
   const int seq = a.q_seq ? a.q_seq[t] : 0;
@@ -52,7 +50,7 @@ __global__ __launch_bounds__(kRT) void k_route(RouteArgs a) {
       const int row = ht * 32 + n;
 #pragma unroll
       for (int s = 0; s < S; ++s)
-        qa[ht][s] = row < a.n_heads ? load_bf16x8(q_t + (size_t)row * D + h * (D / 2) + 8 * s)
+        qa[ht][s] = row < a.n_heads ? load_bf16x8(q_t + (size_t)row * D + 8 * h + 16 * s)
                                     : zero_bf16x8();
     }
     const int n_tiles = (int)((b1 - b0 + 31) / 32);
@@ -65,7 +63,7 @@ __global__ __launch_bounds__(kRT) void k_route(RouteArgs a) {
                                  : a.pooled + ((size_t)seq * (size_t)a.m_max + (size_t)bb) * D;
       bf16x8 kb[S];
 #pragma unroll
-      for (int s = 0; s < S; ++s) kb[s] = load_bf16x8(rowp + h * (D / 2) + 8 * s);
+      for (int s = 0; s < S; ++s) kb[s] = load_bf16x8(rowp + 8 * h + 16 * s);
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
         f32x16 acc;
@@ -99,44 +97,6 @@ __global__ __launch_bounds__(kRT) void k_route(RouteArgs a) {
     float p = 0.f;
     for (int w = 0; w < kRT / 64; ++w) p += s_part[w][j];
     a.part[((size_t)t * a.splits + sp) * a.n_heads + j] = p;
-  }
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t done = atomicAdd(a.counter + t, 1u);
-    s_last = done == (uint32_t)(a.splits - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  for (int j = threadIdx.x; j < a.n_heads; j += kRT) {
-    float tot = 0.f;
-    for (int s = 0; s < a.splits; ++s)
-      tot += __hip_atomic_load(a.part + ((size_t)t * a.splits + s) * a.n_heads + j,
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    float I = fabsf(a.w[(size_t)t * a.n_heads + j]) * tot;
-    s_I[j] = I;
-    if (a.out_importance) a.out_importance[(size_t)t * a.n_heads + j] = I;
-  }
-  __syncthreads();
-  for (int j = threadIdx.x; j < a.n_heads; j += kRT) {
-    if (!ok) {
-      if (j < a.h) {
-        a.heads[(size_t)t * a.h + j] = j;
-        if (a.out_heads) a.out_heads[(size_t)t * a.h + j] = -1;
-      }
-      continue;
-    }
-    const float Ij = s_I[j];
-    int rank = 0;
-    for (int i = 0; i < a.n_heads; ++i) {
-      const float Ii = s_I[i];
-      rank += (Ii > Ij) || (Ii == Ij && i < j);
-    }
-    if (rank < a.h) {
-      a.heads[(size_t)t * a.h + rank] = j;
-      if (a.out_heads) a.out_heads[(size_t)t * a.h + rank] = j;
-    }
   }
 }
 

@@ -116,6 +116,36 @@ DSA_DEVICE void store_score(const SelArgs& a, int t, const Row& r, int64_t i0, i
   }
 }
 
+// MISA head routing, finished by every workgroup of the routed pass: adds the
+// router's per-slice head sums in slice order, I_j = |w_j| * sum, and ranks the
+// heads by (I desc, j asc).  The order is fixed, so every workgroup of a query
+// obtains the same head set; the chunk-0 workgroup reports it.
+DSA_DEVICE void route_heads(const SelArgs& a, int t, int32_t* s_heads, float* s_I, bool report) {
+  const int H = a.n_heads;
+  for (int j = threadIdx.x; j < H; j += blockDim.x) {
+    float tot = 0.f;
+    for (int sp = 0; sp < a.route_splits; ++sp)
+      tot += a.route_part[((size_t)t * a.route_splits + sp) * H + j];
+    const float I = fabsf(a.w[(size_t)t * H + j]) * tot;
+    s_I[j] = I;
+    if (report && a.out_importance) a.out_importance[(size_t)t * H + j] = I;
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < H; j += blockDim.x) {
+    const float Ij = s_I[j];
+    int rank = 0;
+    for (int i = 0; i < H; ++i) {
+      const float Ii = s_I[i];
+      rank += (Ii > Ij) || (Ii == Ij && i < j);
+    }
+    if (rank < a.h_use) {
+      s_heads[rank] = j;
+      if (report && a.out_heads) a.out_heads[(size_t)t * a.h_use + rank] = j;
+    }
+  }
+  __syncthreads();
+}
+
 // Kernel 1 of a selection pass: score one chunk of one query, emit candidates.
 template <class SC, int MODE>
 __global__ __launch_bounds__(kNT) void k_score_emit(SelArgs a) {
@@ -125,9 +155,19 @@ __global__ __launch_bounds__(kNT) void k_score_emit(SelArgs a) {
   uint32_t* scratch = hist + kBins;
   float* sc_lds = reinterpret_cast<float*>(scratch + 64);
 
+  __shared__ int32_t s_heads[64];
+  __shared__ float s_I[64];
   const int t = blockIdx.x, c = blockIdx.y;
   const Row r = row_of<MODE>(a, t);
-  if (r.n_items == 0) return;                       // the merge pads the row
+  if (r.n_items == 0) {                             // the merge pads the row
+    if (a.route_part && c == 0) {
+      for (int j = threadIdx.x; j < a.h_use; j += kNT)
+        if (a.out_heads) a.out_heads[(size_t)t * a.h_use + j] = -1;
+      for (int j = threadIdx.x; j < a.n_heads; j += kNT)
+        if (a.out_importance) a.out_importance[(size_t)t * a.n_heads + j] = 0.f;
+    }
+    return;
+  }
   const int n_chunks_t = (int)((r.n_items + a.chunk - 1) / a.chunk);
   if (c >= n_chunks_t) return;
 
@@ -137,6 +177,10 @@ __global__ __launch_bounds__(kNT) void k_score_emit(SelArgs a) {
       reinterpret_cast<const char*>(a.q) + (size_t)t * a.n_heads * a.head_dim * eb);
   const float* w_t = a.w + (size_t)t * a.n_heads;
   const int32_t* heads_t = a.heads ? a.heads + (size_t)t * a.heads_stride : nullptr;
+  if (a.route_part) {
+    route_heads(a, t, s_heads, s_I, c == 0);
+    heads_t = s_heads;
+  }
   SC sc;
   sc.init(q_t, w_t, heads_t, a.h_use, sc_lds);
   __syncthreads();
