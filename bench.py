@@ -27,7 +27,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 CSRC = os.path.join(ROOT, "sparse_attention_token_indexer_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
-WORKLOADS = {"dense_decode": 2, "tiny": 1, "misa": 4, "misa_dagger": 4, "hisa": 5, "pool": 4}
+WORKLOADS = {"dense_decode": 2, "tiny": 1, "dense_prefill": 3, "misa": 4, "misa_dagger": 4,
+             "hisa": 5, "pool": 4}
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
 
 
 def kernel_source_hash() -> str:
@@ -96,8 +98,16 @@ def cpu_baseline(wl, seed, seconds: float, mode: str):
     q, w = datagen.queries(wl, seed)
     q_seq, q_pos = datagen.positions(wl)
     done_pairs, spent, nq_done = 0, 0.0, 0
-    for t in range(wl.nq):
-        K = O.to_f64(datagen.keys(wl, int(q_seq[t]), q, w, seed), wl.dtype)
+    order = range(wl.nq)
+    cache = {}
+    if mode == "dense_prefill":   # rows spread over the causal triangle
+        order = np.random.default_rng(seed).permutation(wl.nq)
+    for t in order:
+        s_id = int(q_seq[t])
+        if s_id not in cache:
+            cache.clear()
+            cache[s_id] = O.to_f64(datagen.keys(wl, s_id, q, w, seed), wl.dtype)
+        K = cache[s_id]
         q_t = O.to_f64(q[t], wl.dtype)
         w_t = w[t].astype(np.float64)
         p = int(q_pos[t])
@@ -117,7 +127,7 @@ def cpu_baseline(wl, seed, seconds: float, mode: str):
             break
     return {"value": done_pairs / spent, "unit": "pair-scores/s", "cores": blas_threads(),
             "kind": "oracle",
-            "sample": f"{nq_done} of {wl.nq} queries ({done_pairs} causal pairs), float64 NumPy, "
+            "sample": f"{nq_done} of {wl.nq} query rows ({done_pairs} causal pairs), float64 NumPy, "
                       f"{spent:.1f} s of compute on {os.cpu_count()} visible host cores"}
 
 
@@ -170,7 +180,18 @@ def main() -> int:
     io_bytes = nq * H * d * eb + nq * H * 4 + nq * topk * 8       # q, w, outputs
     extra = {}
 
-    if name in ("dense_decode", "tiny"):
+    if name == "dense_prefill":
+        nbytes = dsa.indexer_score_topk_workspace_size(nq, H, d, wl.n_seq, L, topk, 0)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+
+        def step():
+            dsa.indexer_score_topk(q, w, k, q_pos, None, top_k=topk, out_idx=out_i,
+                                   out_score=out_s, workspace=ws)
+        kind = "prefill"
+        kernel_bytes = None
+        kernel_flops = pairs * H * d * 2
+        bound_note = "MFMA: the head contraction of every causal (query, key) pair"
+    elif name in ("dense_decode", "tiny"):
         nbytes = dsa.indexer_score_topk_workspace_size(nq, H, d, wl.n_seq, L, topk,
                                                        0 if eb == 2 else 1)
         ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
@@ -246,8 +267,18 @@ def main() -> int:
     dsa.kernel_timing(False)
     k_avg_ms = kt["total_ms"] / max(kt["launches"], 1)
     per_kernel[kind] = round(k_avg_ms * 1e3, 2)
-    achieved = kernel_bytes / (k_avg_ms * 1e-3) / 1e9
     traffic = stored_traffic(name)
+    if kernel_bytes is None:       # compute-bound kernel
+        achieved = kernel_flops / (k_avg_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                    "traffic": traffic, "kernel": kind,
+                    "algorithmic_flops_per_launch": kernel_flops, "note": bound_note}
+    else:
+        achieved = kernel_bytes / (k_avg_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": kind,
+                    "algorithmic_bytes_per_launch": kernel_bytes, "note": bound_note}
 
     if name == "pool":
         metric, unit, value = "mean-pooled key-cache bytes/s", "GB/s", kernel_bytes / (ms_per_step * 1e-3) / 1e9
@@ -281,10 +312,7 @@ def main() -> int:
                    **({"m_blocks": wl.m_blocks} if name == "hisa" else {})},
         "topk_latency_us": ms_per_step * 1e3,
         "kernel_avg_us": per_kernel,
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": kind, "algorithmic_bytes_per_launch": kernel_bytes,
-                     "note": bound_note},
+        "roofline": roofline,
         "cpu_baseline": cpu,
         "host": {"cpu_count": os.cpu_count(), "machine": platform.machine(),
                  "torch": torch.__version__},

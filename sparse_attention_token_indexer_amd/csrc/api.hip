@@ -190,6 +190,25 @@ int check_ws(void* ws, size_t have, size_t need) {
 
 // ---------------------------------------------------------------- dense ----
 
+// Prefill-shaped calls (many queries on one sequence) run the query-grouped
+// kernels; the per-row LDS histograms hold 16-bit counts, hence the l_max limit.
+bool use_prefill(int32_t dtype, int64_t nq, int n_seq, int64_t l_max) {
+  return dtype == DSA_DTYPE_BF16 && n_seq == 1 && nq >= 64 && l_max <= 65535;
+}
+
+struct PrefillPlan {
+  size_t scores = 0, rowmeta = 0, total = 0;
+};
+
+PrefillPlan plan_prefill(int64_t nq, int64_t l_max) {
+  PrefillPlan p;
+  Arena A;
+  p.scores = A.take((size_t)nq * ((l_max + 3) & ~(int64_t)3) * 4);
+  p.rowmeta = A.take((size_t)nq * 16);
+  p.total = A.off;
+  return p;
+}
+
 struct DensePlan {
   StagePlan s;
   size_t zero_bytes = 0, total = 0;
@@ -356,8 +375,9 @@ int dsa_kernel_timing_read(int32_t kind, int64_t* launches, double* total_ms, do
 size_t indexer_score_topk_workspace_size(int32_t nq, int32_t n_heads, int32_t head_dim,
                                          int32_t n_seq, int64_t l_max, int32_t top_k,
                                          int32_t dtype) {
-  (void)n_heads; (void)n_seq; (void)top_k;
+  (void)n_heads; (void)top_k;
   if (nq <= 0 || l_max <= 0) return 0;
+  if (use_prefill(dtype, nq, n_seq, l_max)) return plan_prefill(nq, l_max).total;
   return plan_dense(nq, head_dim, l_max, dtype == DSA_DTYPE_F32).total;
 }
 
@@ -369,6 +389,33 @@ int indexer_score_topk(const void* q, const float* w, const void* k, int32_t dty
   int st = check_common(q, w, k, dtype, q_pos, nq, n_heads, head_dim, n_seq, l_max, top_k, out_idx);
   if (st || nq == 0) return st;
   const int f32 = dtype == DSA_DTYPE_F32;
+  if (use_prefill(dtype, nq, n_seq, l_max)) {
+    PrefillPlan pp = plan_prefill(nq, l_max);
+    if ((st = check_ws(workspace, workspace_bytes, pp.total))) return st;
+    dsa::PrefillArgs pa{};
+    pa.q = reinterpret_cast<const uint16_t*>(q);
+    pa.w = w;
+    pa.keys = reinterpret_cast<const uint16_t*>(k);
+    pa.q_seq = q_seq;
+    pa.q_pos = q_pos;
+    pa.nq = nq;
+    pa.n_heads = n_heads;
+    pa.head_dim = head_dim;
+    pa.top_k = top_k;
+    pa.l_max = l_max;
+    pa.row_stride = (l_max + 3) & ~(int64_t)3;
+    pa.scores = at<float>(workspace, pp.scores);
+    pa.rowmeta = at<int32_t>(workspace, pp.rowmeta);
+    pa.out_idx = out_idx;
+    pa.out_score = out_score;
+    st = hip_status(timed(DSA_KERNEL_PREFILL, stream,
+                          [&] { return dsa::launch_prefill_score(pa, stream); }),
+                    "prefill score kernel", stream);
+    if (st) return st;
+    return hip_status(timed(DSA_KERNEL_ROWSELECT, stream,
+                            [&] { return dsa::launch_prefill_select(pa, stream); }),
+                      "prefill select kernel", stream);
+  }
   DensePlan p = plan_dense(nq, head_dim, l_max, f32);
   if ((st = check_ws(workspace, workspace_bytes, p.total))) return st;
   if ((st = run_prepare(workspace, p.zero_bytes, k, q_seq, q_pos, nq, n_seq, head_dim, 1, l_max,

@@ -85,6 +85,25 @@ struct RouteArgs {
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream);
 
+// Prefill-shaped dense pass: all queries on sequence 0, grouped by 8 rows.
+struct PrefillArgs {
+  const uint16_t* q;           // [nq, n_heads, D] bf16
+  const float* w;              // [nq, n_heads]
+  const uint16_t* keys;        // [1, l_max, D] bf16
+  const int32_t* q_seq;        // [nq] or null
+  const int32_t* q_pos;        // [nq]
+  int nq, n_heads, head_dim, top_k;
+  int64_t l_max;
+  int64_t row_stride;          // floats per score row (l_max rounded up to 4)
+  float* scores;               // [nq, row_stride] workspace (only u <= pos written)
+  int32_t* rowmeta;            // [nq, 4] workspace: threshold bin, count above, count in bin
+  int32_t* out_idx;
+  float* out_score;
+};
+constexpr int kPrefillRows = 8;   // query rows per scoring workgroup
+hipError_t launch_prefill_score(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_prefill_select(const PrefillArgs& a, hipStream_t stream);
+
 hipError_t launch_iou(const int32_t* a, const int32_t* b, int nq, int k, float* out,
                       hipStream_t stream);
 

@@ -25,13 +25,36 @@ struct Emitter {
   float* out_score;    // row base or null
   uint32_t* counter;   // LDS slot counter
   uint32_t cap;        // slots available in the row
-  DSA_DEVICE void put(uint32_t key, int32_t id) const {
-    uint32_t o = atomicAdd(counter, 1u);
+  DSA_DEVICE void write(uint32_t o, uint32_t key, int32_t id) const {
     if (o >= cap) return;
     out_idx[o] = id;
     if (out_score) out_score[o] = key_to_score(key);
   }
+  DSA_DEVICE void put(uint32_t key, int32_t id) const { write(atomicAdd(counter, 1u), key, id); }
+  // Wave-collective: every lane of the wave calls it; lanes with take set
+  // append their entry (one LDS atomic per wave).
+  DSA_DEVICE void put_wave(bool take, uint32_t key, int32_t id) const {
+    const uint64_t m = __ballot(take);
+    if (!m) return;
+    const int lane = lane_id();
+    uint32_t base = 0;
+    if (lane == 0) base = atomicAdd(counter, (uint32_t)__popcll(m));
+    base = __shfl(base, 0, 64);
+    if (take) write(base + (uint32_t)__popcll(m & ((1ull << lane) - 1ull)), key, id);
+  }
 };
+
+// Wave-collective append of (key, id) to an LDS list of capacity cap.
+DSA_DEVICE void list_put_wave(bool take, uint2 e, uint2* list, uint32_t* count, uint32_t cap) {
+  const uint64_t m = __ballot(take);
+  if (!m) return;
+  const int lane = lane_id();
+  uint32_t base = 0;
+  if (lane == 0) base = atomicAdd(count, (uint32_t)__popcll(m));
+  base = __shfl(base, 0, 64);
+  const uint32_t o = base + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
+  if (take && o < cap) list[o] = e;
+}
 
 // Entries held in LDS.
 struct LdsSource {
@@ -135,6 +158,66 @@ DSA_DEVICE void radix_finish(const Src& src, uint64_t prefix, uint64_t mask, int
       return;
     }
   }
+}
+
+// Exact finish of a tied 12-bit bin held in LDS (list[0..nl), all entries share
+// the top kBinBits of their key): emit the `need` best by composite order.  One
+// 10-bit digit histogram narrows the tie to a sub-bin; if that holds at most 64
+// entries they are ranked by brute force inside one wave, otherwise the general
+// radix finish takes over.  hist needs 1024 words, tie 64 pairs of LDS.
+template <int NT>
+DSA_DEVICE void finish_bin(const uint2* list, uint32_t nl, uint32_t need, int bstar,
+                           const Emitter& em, uint32_t* hist, uint32_t* scratch, uint2* tie) {
+  __shared__ uint32_t s_tn;
+  if (need == 0) return;
+  if (need >= nl) {
+    for (uint32_t i = threadIdx.x; i < nl; i += NT) em.put(list[i].x, (int32_t)list[i].y);
+    __syncthreads();
+    return;
+  }
+  constexpr int D2 = 10;
+  constexpr int SH2 = 32 - kBinBits - D2;          // key bits [19:10]
+  for (int i = threadIdx.x; i < (1 << D2); i += NT) hist[i] = 0;
+  if (threadIdx.x == 0) s_tn = 0;
+  __syncthreads();
+  for (uint32_t i = threadIdx.x; i < nl; i += NT)
+    atomicAdd(&hist[(list[i].x >> SH2) & ((1u << D2) - 1u)], 1u);
+  __syncthreads();
+  uint32_t above2;
+  const int d2 = block_find_threshold<NT>(hist, 1 << D2, need, scratch, &above2);
+  const uint32_t nd2 = hist[d2];
+  const uint32_t need2 = need - above2;
+  __syncthreads();
+  for (uint32_t base = 0; base < nl; base += NT) {
+    const uint32_t i = base + threadIdx.x;
+    const uint2 e = i < nl ? list[i] : make_uint2(0u, 0u);
+    const int dg = i < nl ? (int)((e.x >> SH2) & ((1u << D2) - 1u)) : -1;
+    em.put_wave(dg > d2, e.x, (int32_t)e.y);
+    if (nd2 <= 64) list_put_wave(dg == d2, e, tie, &s_tn, 64u);
+  }
+  __syncthreads();
+  if (need2 == 0) return;
+  if (nd2 <= 64) {
+    if (threadIdx.x < 64) {
+      const int lane = threadIdx.x;
+      const uint32_t nt = s_tn < nd2 ? s_tn : nd2;
+      const bool have = (uint32_t)lane < nt;
+      const uint2 me = have ? tie[lane] : make_uint2(0u, 0u);
+      const uint64_t cm = composite(me.x, (int32_t)me.y);
+      uint32_t rank = 0;
+      for (uint32_t j = 0; j < nt; ++j) {
+        const uint2 o = tie[j];
+        rank += composite(o.x, (int32_t)o.y) > cm;
+      }
+      em.put_wave(have && rank < need2, me.x, (int32_t)me.y);
+    }
+    __syncthreads();
+    return;
+  }
+  LdsSource src{list, nl};
+  const uint64_t prefix = ((uint64_t)bstar << (64 - kBinBits)) | ((uint64_t)d2 << (32 + SH2));
+  const uint64_t mask = ((uint64_t)((1u << (kBinBits + D2)) - 1u)) << (32 + SH2);
+  radix_finish<NT>(src, prefix, mask, 32 + SH2, need2, nd2, em, hist, scratch);
 }
 
 // Chunk-side half of a selection pass (run by every chunk workgroup).
