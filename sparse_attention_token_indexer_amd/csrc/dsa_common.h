@@ -38,7 +38,12 @@ DSA_DEVICE uint64_t composite(uint32_t key, int32_t id) {
   return ((uint64_t)key << 32) | (uint64_t)(~(uint32_t)id);
 }
 
-DSA_DEVICE float relu(float x) { return x > 0.f ? x : 0.f; }
+// max(0, x) in one integer max on the IEEE bit pattern: every negative value
+// (sign bit set, -0.0 included) compares below 0 and becomes +0.0, every
+// positive value keeps its bits.  (The float max would first canonicalise x.)
+DSA_DEVICE float relu(float x) {
+  return __int_as_float(__builtin_elementwise_max(__float_as_int(x), 0));
+}
 
 // Wave-wide sum / exchange helpers (wave64).
 DSA_DEVICE float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }

@@ -100,7 +100,6 @@ struct PrefillArgs {
   int32_t* out_idx;
   float* out_score;
 };
-constexpr int kPrefillRows = 8;   // query rows per scoring workgroup
 hipError_t launch_prefill_score(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_select(const PrefillArgs& a, hipStream_t stream);
 

@@ -3,57 +3,99 @@
 // scores every prefix token; its cost grows as O(L^2) over a prefill, HISA
 // review section 2) and keeps the exact top-k.
 //
-// k_prefill_score: one workgroup = 8 consecutive query rows, one wave per row
-// with its 64x128 query block resident in registers.  The rows share the key
-// cache: 64-key stages are staged in LDS (double-buffered, XOR-swizzled so the
-// MFMA operand reads are free of bank conflicts) and each wave runs
+// k_prefill_score: one workgroup = 8 consecutive query rows, one wave
+// per row with its query block (heads x 128) resident in registers.  The rows
+// share the key cache: 128-key stages are staged in LDS (double-buffered, rows
+// padded so the MFMA operand reads are free of bank conflicts) and each wave runs
 // v_mfma_f32_32x32x16_bf16 with heads as rows and keys as columns, then the
-// fused ReLU-weighted head reduction in registers.  Scores go to a workspace row
-// and into a per-row 12-bit histogram in LDS; at the end each wave finds the
-// bin that holds its row's k-th score.  Workgroups run longest rows first.
+// fused ReLU-weighted head reduction in registers.  Two 32-key sub-tiles are
+// finished together (one lane-half exchange gives 64 consecutive keys' scores
+// across the wave).  Scores go to a workspace row and into a per-row 12-bit
+// histogram in LDS; at the end each wave finds the bin that holds its row's
+// k-th score.  Workgroups run longest rows first.
 // k_prefill_select: one workgroup per row emits every score above that bin and
 // resolves the bin itself exactly (radix digits over (score, ~index)).
 #include "dsa_internal.h"
 #include "dsa_common.h"
 #include "dsa_select.h"
 
+#include <utility>
+
 namespace dsa {
 
 namespace {
 
-constexpr int kPT = 64 * kPrefillRows;   // one wave per query row
-constexpr int kStageKeys = 64;
+constexpr int kStageKeys = 128;          // keys per LDS stage (2 pairs of 32-key sub-tiles)
+constexpr int kPBinBits = kBinBits;      // per-row histogram: top 12 bits of the score key
+constexpr int kPBins = 1 << kPBinBits;
+constexpr int kPBinShift = 32 - kPBinBits;
 constexpr int kST = 256;                 // select workgroup
 constexpr uint32_t kSelListCap = 2048;   // tie-bin entries kept in LDS (global fallback beyond)
 
-template <int D>
+// Query rows per scoring workgroup (one wave each).  With 64 heads the row's
+// query block takes 64 VGPRs; 8 rows keep each wave within 256 registers (two
+// waves per SIMD) and the stages plus 8 KB histograms per row within 160 KB.
+constexpr int kRows = 8;
+
+template <int D, int ROWS>
 constexpr size_t prefill_lds_bytes() {
-  return 2 * (size_t)kStageKeys * D * 2 + (size_t)kPrefillRows * (kBins / 2) * 4;
+  return 2 * (size_t)kStageKeys * (D * 2 + 16) + (size_t)ROWS * (kPBins / 2) * 4;
 }
 
-template <int HT, int D>
-__global__ __launch_bounds__(kPT) void k_prefill_score(PrefillArgs a) {
+// p + W[16*(lane/16) + R] * x: the weight comes from lane R of the lane's own
+// 16-lane row (DPP row_newbcast on the first operand), so one VGPR carries 16
+// per-row constants for each of the four rows.  Register operands only.
+template <int R>
+DSA_DEVICE float fmac_rowbcast(float p, float W, float x) {
+  asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+      : "+v"(p)
+      : "v"(W), "v"(x), "n"(R));
+  return p;
+}
+
+template <int HT, int... R>
+DSA_DEVICE float weighted_relu_sum(const f32x16 (&acc)[HT], const float (&W)[HT],
+                                   std::integer_sequence<int, R...>) {
+  float p = 0.f;
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) ((p = fmac_rowbcast<R>(p, W[ht], relu(acc[ht][R]))), ...);
+  return p;
+}
+
+// Order-preserving score key without the -0.0 fold: the scores computed here
+// are sums w*max(0, x) started from +0.0, which can never produce -0.0, so this
+// agrees with score_to_key on every value it sees.
+DSA_DEVICE uint32_t fast_key(float f) {
+  const uint32_t b = __float_as_uint(f);
+  return b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);
+}
+
+template <int HT, int D, int ROWS>
+__global__ __launch_bounds__(64 * ROWS) void k_prefill_score(PrefillArgs a) {
+  constexpr int kPT = 64 * ROWS;
   constexpr int S = D / 16;                    // k-steps
-  constexpr int RB = D * 2;                    // bytes per key row
+  constexpr int RB = D * 2;                    // bytes per key row in the cache
   constexpr int NC = RB / 16;                  // 16-byte pieces per key row
-  constexpr int STAGE = kStageKeys * RB;       // bytes per LDS stage
-  constexpr int LOADS = STAGE / 16 / kPT;      // 16-byte loads per thread per stage
-  static_assert(LOADS >= 1 && STAGE % (16 * kPT) == 0, "stage size");
+  constexpr int LB = RB + 16;                  // LDS row stride: one pad piece per key
+  constexpr int STAGE = kStageKeys * LB;       // bytes per LDS stage
+  constexpr int PIECES = kStageKeys * NC;
+  constexpr int LOADS = (PIECES + kPT - 1) / kPT;   // 16-byte loads per thread per stage
+  constexpr int PAIRS = kStageKeys / 64;
   extern __shared__ __align__(16) uint8_t smem[];
   uint8_t* ktile = smem;                                           // [2][STAGE]
-  uint32_t* hist = reinterpret_cast<uint32_t*>(smem + 2 * STAGE);  // [rows][kBins / 2]
+  uint32_t* hist = reinterpret_cast<uint32_t*>(smem + 2 * STAGE);  // [rows][kPBins / 2]
   __shared__ int s_maxpos;
 
   const int wv = wave_id(), lane = lane_id();
   const int grp = (int)gridDim.x - 1 - (int)blockIdx.x;            // longest rows first
-  const int t = grp * kPrefillRows + wv;
+  const int t = grp * ROWS + wv;
   int pos = -1;
   if (t < a.nq) {
     const int seq = a.q_seq ? a.q_seq[t] : 0;
     const int p = a.q_pos[t];
     if (seq == 0 && p >= 0 && (int64_t)p < a.l_max) pos = p;
   }
-  for (int i = threadIdx.x; i < kPrefillRows * (kBins / 2); i += kPT) hist[i] = 0u;
+  for (int i = threadIdx.x; i < ROWS * (kPBins / 2); i += kPT) hist[i] = 0u;
   if (threadIdx.x == 0) s_maxpos = -1;
   __syncthreads();
   if (lane == 0) atomicMax(&s_maxpos, pos);
@@ -62,10 +104,19 @@ __global__ __launch_bounds__(kPT) void k_prefill_score(PrefillArgs a) {
   if (maxpos < 0) return;                      // the select kernel pads these rows
   const int n_stages = maxpos / kStageKeys + 1;
 
-  // this wave's query row (zeros for an invalid row)
+  // this wave's query row in registers (zeros for an invalid row).  Head
+  // weights: accumulator register r of head tile ht holds head
+  // ht*32 + 8*(r/4) + 4*(lane/32) + r%4, and W[ht] holds that head's weight
+  // for r = lane%16 in every 16-lane row, ready for a row broadcast.
   const int m = lane & 31, h = lane >> 5;
   bf16x8 qa[HT][S];
-  float wr[HT][16];
+  float W[HT];
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+    const int r = lane & 15;
+    const int head = ht * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+    W[ht] = (pos >= 0 && head < a.n_heads) ? a.w[(size_t)t * a.n_heads + head] : 0.f;
+  }
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) {
     const int row = ht * 32 + m;
@@ -73,84 +124,120 @@ __global__ __launch_bounds__(kPT) void k_prefill_score(PrefillArgs a) {
     const uint16_t* src = a.q + ((size_t)t * a.n_heads + (ok ? row : 0)) * D + 8 * h;
 #pragma unroll
     for (int s = 0; s < S; ++s) qa[ht][s] = ok ? load_bf16x8(src + 16 * s) : zero_bf16x8();
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int rs = ht * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-      wr[ht][r] = (pos >= 0 && rs < a.n_heads) ? a.w[(size_t)t * a.n_heads + rs] : 0.f;
-    }
   }
+  // The padded row stride keeps both LDS access patterns conflict-free: 16
+  // lanes storing one key's pieces touch 256 contiguous bytes, and 16 lanes
+  // reading piece 2s+h of 16 consecutive keys start 4 banks apart.  The lane's
+  // read offset is one base plus compile-time offsets.
+  const uint32_t boff = (uint32_t)(m * LB + h * 16);
 
-  // stage loading: thread piece p = threadIdx.x + j * kPT is key p / NC, piece
-  // p % NC, stored at LDS slot (piece ^ (key % NC)) of that key's row
+  // stage loading: thread piece p is key p / NC, piece p % NC
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.keys);
   u32x4 pre[LOADS];
   auto fetch = [&](int st) {
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
       const int p = threadIdx.x + j * kPT;
-      int key = st * kStageKeys + p / NC;
-      if (key > maxpos) key = maxpos;          // stays inside the cache; never scored
-      pre[j] = *reinterpret_cast<const u32x4*>(kbase + (size_t)key * RB + (p % NC) * 16);
+      if (p < PIECES) {
+        int key = st * kStageKeys + p / NC;
+        if (key > maxpos) key = maxpos;        // stays inside the cache; never scored
+        pre[j] = *reinterpret_cast<const u32x4*>(kbase + (size_t)key * RB + (p % NC) * 16);
+      }
     }
   };
   auto stash = [&](int buf) {
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
       const int p = threadIdx.x + j * kPT;
-      const int key = p / NC, pc = p % NC;
-      *reinterpret_cast<u32x4*>(ktile + buf * STAGE + key * RB + ((pc ^ (key % NC)) * 16)) = pre[j];
+      if (p < PIECES) {
+        const int key = p / NC, pc = p % NC;
+        *reinterpret_cast<u32x4*>(ktile + buf * STAGE + key * LB + pc * 16) = pre[j];
+      }
+    }
+  };
+  // B operands of the sub-tile at `sub` of a stage
+  auto load_b = [&](bf16x8 (&b)[S], const uint8_t* tile, int sub) {
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+      b[s] = __builtin_bit_cast(bf16x8,
+                                *reinterpret_cast<const u32x4*>(tile + boff + sub * 32 * LB + s * 32));
+  };
+  auto mfma = [&](f32x16 (&acc)[HT], const bf16x8 (&b)[S]) {
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[ht][r] = 0.f;
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht)
+        acc[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ht][s], b[s], acc[ht], 0, 0, 0);
+  };
+  // partial score of this lane's heads for key column m
+  auto epi = [&](const f32x16 (&acc)[HT]) {
+    return weighted_relu_sum<HT>(acc, W, std::make_integer_sequence<int, 16>{});
+  };
+  float* srow = a.scores + (size_t)(t < a.nq ? t : 0) * (size_t)a.row_stride;
+  uint32_t* hrow = hist + wv * (kPBins / 2);
+  // sub-tiles A = keys key0..key0+31 and B = key0+32..key0+63: lanes 0..31 get
+  // A's key l, lanes 32..63 B's key l-32, and the two lane halves' partials of
+  // one key meet in one add
+  auto finish = [&](int key0, float pa, float pb) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(pa), __float_as_uint(pb),
+                                                     false, false);
+    const float sc = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    const int u = key0 + lane;
+    if (u <= pos) {
+      srow[u] = sc;
+      const uint32_t bin = fast_key(sc) >> kPBinShift;
+      atomicAdd(hrow + (bin >> 1), 1u << ((bin & 1u) * 16));
     }
   };
 
-  float* srow = a.scores + (size_t)(t < a.nq ? t : 0) * (size_t)a.row_stride;
-  uint32_t* hrow = hist + wv * (kBins / 2);
+  // Software pipeline over the workgroup's 32-key sub-tiles (the same count for
+  // every wave; keys past a row's position are computed and dropped): sub-tile
+  // j's operands are read one sub-tile ahead, and its epilogue runs under the
+  // MFMAs of sub-tile j+1.  The barrier that publishes stage st+1 sits in
+  // sub-tile 2 of stage st, after every wave has read its last operands of
+  // stage st-1 (whose buffer the stash overwrites), so sub-tile 3 can already
+  // read stage st+1.
   fetch(0);
   stash(0);
   __syncthreads();
+  if (n_stages > 1) fetch(1);
+  bf16x8 b0[S], b1[S];
+  f32x16 accx[HT], accy[HT];
+  float pe = 0.f;
+  load_b(b0, ktile, 0);
   for (int st = 0; st < n_stages; ++st) {
-    const int buf = st & 1;
+    const uint8_t* tile = ktile + (st & 1) * STAGE;
     const bool more = st + 1 < n_stages;
-    if (more) fetch(st + 1);
-#pragma unroll
-    for (int sub = 0; sub < kStageKeys / 32; ++sub) {
-      const int key0 = st * kStageKeys + sub * 32;
-      if (key0 <= pos) {                       // wave-uniform
-        const int kl = sub * 32 + m;           // key within the stage for this lane's column
-        const uint8_t* krow = ktile + buf * STAGE + kl * RB;
-        bf16x8 b[S];
-#pragma unroll
-        for (int s = 0; s < S; ++s) {
-          const int pc = 2 * s + h;
-          b[s] = __builtin_bit_cast(bf16x8,
-                                    *reinterpret_cast<const u32x4*>(krow + ((pc ^ (kl % NC)) * 16)));
-        }
-        f32x16 acc[HT];
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[ht][r] = 0.f;
-#pragma unroll
-        for (int s = 0; s < S; ++s)
-#pragma unroll
-          for (int ht = 0; ht < HT; ++ht)
-            acc[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ht][s], b[s], acc[ht], 0, 0, 0);
-        float p = 0.f;
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) p = __builtin_fmaf(wr[ht][r], relu(acc[ht][r]), p);
-        p += shfl_xor_f(p, 32);
-        const int u = key0 + lane;
-        if (lane < 32 && u <= pos) {
-          srow[u] = p;
-          const uint32_t bin = score_to_key(p) >> kBinShift;
-          atomicAdd(hrow + (bin >> 1), 1u << ((bin & 1u) * 16));
-        }
-      }
+    const int k0 = st * kStageKeys;
+    // (the scheduling fences keep each step's loads, MFMAs and epilogue
+    // together, so no operand set is loaded more than one step ahead)
+    load_b(b1, tile, 1);
+    mfma(accx, b0);
+    if (st > 0) finish(k0 - 64, pe, epi(accy));
+    __builtin_amdgcn_sched_barrier(0);
+    load_b(b0, tile, 2);
+    mfma(accy, b1);
+    pe = epi(accx);
+    __builtin_amdgcn_sched_barrier(0);
+    load_b(b1, tile, 3);
+    mfma(accx, b0);
+    finish(k0, pe, epi(accy));
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) {
+      stash((st + 1) & 1);
+      __syncthreads();
+      if (st + 2 < n_stages) fetch(st + 2);
+      load_b(b0, ktile + ((st + 1) & 1) * STAGE, 0);
     }
-    if (more) stash(buf ^ 1);
-    __syncthreads();
+    mfma(accy, b1);
+    pe = epi(accx);
+    __builtin_amdgcn_sched_barrier(0);
   }
+  finish(n_stages * kStageKeys - 64, pe, epi(accy));
 
   // this row's threshold: the 12-bit bin holding its k-th score
   if (pos < 0) return;
@@ -159,10 +246,11 @@ __global__ __launch_bounds__(kPT) void k_prefill_score(PrefillArgs a) {
     if (lane == 0) { meta[0] = -1; meta[1] = 0; meta[2] = 0; }
     return;
   }
-  // lane l owns bins [kBins - 64 (l + 1), kBins - 64 l), counted from the top
-  const int b_hi = kBins - 64 * lane;           // exclusive
+  // lane l owns bins [kPBins - PER (l + 1), kPBins - PER l), counted from the top
+  constexpr int PER = kPBins / 64;
+  const int b_hi = kPBins - PER * lane;         // exclusive
   uint32_t mine = 0;
-  for (int wd = (b_hi - 64) / 2; wd < b_hi / 2; ++wd) {
+  for (int wd = (b_hi - PER) / 2; wd < b_hi / 2; ++wd) {
     const uint32_t v = hrow[wd];
     mine += (v & 0xFFFFu) + (v >> 16);
   }
@@ -175,7 +263,7 @@ __global__ __launch_bounds__(kPT) void k_prefill_score(PrefillArgs a) {
   const uint32_t before = incl - mine, need = (uint32_t)a.top_k;
   if (before < need && incl >= need) {
     uint32_t accum = before;
-    for (int b = b_hi - 1; b >= b_hi - 64; --b) {
+    for (int b = b_hi - 1; b >= b_hi - PER; --b) {
       const uint32_t c = (hrow[b >> 1] >> ((b & 1) * 16)) & 0xFFFFu;
       if (accum + c >= need) {
         meta[0] = b;
@@ -255,7 +343,7 @@ __global__ __launch_bounds__(kST) void k_prefill_select(PrefillArgs a) {
         const uint32_t u = 4 * i4 + e;
         const bool ok = i4 < n4 && u < n;
         const uint32_t key = ok ? score_to_key(v[j][e]) : 0u;
-        const int b = ok ? (int)(key >> kBinShift) : -1;
+        const int b = ok ? (int)(key >> kPBinShift) : -1;
         em.put_wave(b > bstar, key, (int32_t)u);
         if (fits) list_put_wave(b == bstar, make_uint2(key, u), list, &s_ln, kSelListCap);
       }
@@ -267,22 +355,24 @@ __global__ __launch_bounds__(kST) void k_prefill_select(PrefillArgs a) {
     const uint32_t nl = s_ln < nb ? s_ln : nb;
     finish_bin<kST>(list, nl, need, bstar, em, hist, scratch, tie);
   } else {
-    const uint64_t prefix = (uint64_t)bstar << (64 - kBinBits);
-    const uint64_t mask = (uint64_t)(kBins - 1) << (64 - kBinBits);
+    const uint64_t prefix = (uint64_t)bstar << (64 - kPBinBits);
+    const uint64_t mask = (uint64_t)(kPBins - 1) << (64 - kPBinBits);
     RowSource src{sc, n};
-    radix_finish<kST>(src, prefix, mask, 64 - kBinBits, need, nb, em, hist, scratch);
+    radix_finish<kST>(src, prefix, mask, 64 - kPBinBits, need, nb, em, hist, scratch);
   }
 }
 
 template <int HT, int D>
 hipError_t launch_score_t(const PrefillArgs& a, hipStream_t stream) {
-  const size_t lds = prefill_lds_bytes<D>();
-  auto k = k_prefill_score<HT, D>;
+  constexpr int ROWS = kRows;
+  const size_t lds = prefill_lds_bytes<D, ROWS>();
+  static_assert(prefill_lds_bytes<D, ROWS>() <= 160 * 1024, "LDS");
+  auto k = k_prefill_score<HT, D, ROWS>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  const int groups = (a.nq + kPrefillRows - 1) / kPrefillRows;
-  hipLaunchKernelGGL(k, dim3(groups), dim3(kPT), lds, stream, a);
+  const int groups = (a.nq + ROWS - 1) / ROWS;
+  hipLaunchKernelGGL(k, dim3(groups), dim3(64 * ROWS), lds, stream, a);
   return hipGetLastError();
 }
 
