@@ -9,6 +9,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 #define DSA_DEVICE __device__ __forceinline__
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -43,6 +45,29 @@ DSA_DEVICE uint64_t composite(uint32_t key, int32_t id) {
 // positive value keeps its bits.  (The float max would first canonicalise x.)
 DSA_DEVICE float relu(float x) {
   return __int_as_float(__builtin_elementwise_max(__float_as_int(x), 0));
+}
+
+// p + W[16*(lane/16) + R] * x: the weight comes from lane R of the lane's own
+// 16-lane row (DPP row_newbcast on the first operand), so one VGPR carries 16
+// per-row constants for each of the four rows.  Register operands only.
+template <int R>
+DSA_DEVICE float fmac_rowbcast(float p, float W, float x) {
+  asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+      : "+v"(p)
+      : "v"(W), "v"(x), "n"(R));
+  return p;
+}
+
+// sum over head tiles ht and accumulator registers r of w(ht, r) * max(0, acc),
+// where W[ht] holds, in lane 16*g + r, the weight of the head that register r
+// holds in lanes of row group g (see the MFMA layouts in dsa_scorers.h).
+template <int HT, int... R>
+DSA_DEVICE float weighted_relu_sum(const f32x16 (&acc)[HT], const float (&W)[HT],
+                                   std::integer_sequence<int, R...>) {
+  float p = 0.f;
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) ((p = fmac_rowbcast<R>(p, W[ht], relu(acc[ht][R]))), ...);
+  return p;
 }
 
 // Wave-wide sum / exchange helpers (wave64).

@@ -29,7 +29,7 @@ struct ScorerMfma32 {
   typedef bf16x8 Frag[S];
 
   bf16x8 qa[HT][S];
-  float wr[HT][16];
+  float W[HT];   // row-broadcast weights (see weighted_relu_sum)
 
   DSA_DEVICE static int row_key(int) { return lane_id() & 31; }
 
@@ -48,11 +48,11 @@ struct ScorerMfma32 {
 #pragma unroll
         for (int s = 0; s < S; ++s) qa[ht][s] = zero_bf16x8();
       }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        int rs = ht * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        wr[ht][r] = rs < h_use ? w_t[heads_t ? heads_t[rs] : rs] : 0.f;
-      }
+      // lane 16*g + r: the head slot that accumulator register r holds in
+      // lanes of row group g (lane half g/2 = h)
+      const int r = lane & 15;
+      const int rs = ht * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+      W[ht] = rs < h_use ? w_t[heads_t ? heads_t[rs] : rs] : 0.f;
     }
   }
 
@@ -73,11 +73,7 @@ struct ScorerMfma32 {
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht)
         acc[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ht][s], b[s], acc[ht], 0, 0, 0);
-    float p = 0.f;
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) p = __builtin_fmaf(wr[ht][r], relu(acc[ht][r]), p);
+    float p = weighted_relu_sum<HT>(acc, W, std::make_integer_sequence<int, 16>{});
     p += shfl_xor_f(p, 32);
     return p;
   }

@@ -19,8 +19,6 @@
 #include "dsa_common.h"
 #include "dsa_select.h"
 
-#include <utility>
-
 namespace dsa {
 
 namespace {
@@ -40,26 +38,6 @@ constexpr int kRows = 8;
 template <int D, int ROWS>
 constexpr size_t prefill_lds_bytes() {
   return 2 * (size_t)kStageKeys * (D * 2 + 16) + (size_t)ROWS * (kPBins / 2) * 4;
-}
-
-// p + W[16*(lane/16) + R] * x: the weight comes from lane R of the lane's own
-// 16-lane row (DPP row_newbcast on the first operand), so one VGPR carries 16
-// per-row constants for each of the four rows.  Register operands only.
-template <int R>
-DSA_DEVICE float fmac_rowbcast(float p, float W, float x) {
-  asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
-      : "+v"(p)
-      : "v"(W), "v"(x), "n"(R));
-  return p;
-}
-
-template <int HT, int... R>
-DSA_DEVICE float weighted_relu_sum(const f32x16 (&acc)[HT], const float (&W)[HT],
-                                   std::integer_sequence<int, R...>) {
-  float p = 0.f;
-#pragma unroll
-  for (int ht = 0; ht < HT; ++ht) ((p = fmac_rowbcast<R>(p, W[ht], relu(acc[ht][R]))), ...);
-  return p;
 }
 
 // Order-preserving score key without the -0.0 fold: the scores computed here
@@ -131,28 +109,33 @@ __global__ __launch_bounds__(64 * ROWS) void k_prefill_score(PrefillArgs a) {
   // read offset is one base plus compile-time offsets.
   const uint32_t boff = (uint32_t)(m * LB + h * 16);
 
-  // stage loading: thread piece p is key p / NC, piece p % NC
+  // stage loading: thread piece p is key p / NC, piece p % NC.  A stage is
+  // loaded in four slots, LOADS / 4 pieces per thread each (see the pipeline
+  // below); pre[j] carries piece j from its global load to its LDS store.
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.keys);
+  constexpr int PER_SLOT = (LOADS + 3) / 4;
   u32x4 pre[LOADS];
-  auto fetch = [&](int st) {
-#pragma unroll
-    for (int j = 0; j < LOADS; ++j) {
-      const int p = threadIdx.x + j * kPT;
-      if (p < PIECES) {
-        int key = st * kStageKeys + p / NC;
-        if (key > maxpos) key = maxpos;        // stays inside the cache; never scored
-        pre[j] = *reinterpret_cast<const u32x4*>(kbase + (size_t)key * RB + (p % NC) * 16);
-      }
-    }
+  static_assert(PIECES % kPT == 0, "every thread stores whole pieces");
+  // (no branches around these memory operations: the wait counts before the
+  // stores then stay exact.  Keys past the last stage are clamped to the last
+  // key and land in a buffer nobody reads.)
+  auto fetch_piece = [&](int j, int st) {
+    const int p = threadIdx.x + j * kPT;
+    const int key = min(st * kStageKeys + p / NC, maxpos);   // inside the cache
+    pre[j] = *reinterpret_cast<const u32x4*>(kbase + (size_t)key * RB + (p % NC) * 16);
   };
-  auto stash = [&](int buf) {
+  auto stash_piece = [&](int j, int buf) {
+    const int p = threadIdx.x + j * kPT;
+    const int key = p / NC, pc = p % NC;
+    *reinterpret_cast<u32x4*>(ktile + buf * STAGE + key * LB + pc * 16) = pre[j];
+  };
+  // slot q of the round that publishes stage st: store its pieces of slot q
+  // and fetch the same pieces of stage st + 1 (one round = one stage ahead)
+  auto slot = [&](int q, int st) {
 #pragma unroll
-    for (int j = 0; j < LOADS; ++j) {
-      const int p = threadIdx.x + j * kPT;
-      if (p < PIECES) {
-        const int key = p / NC, pc = p % NC;
-        *reinterpret_cast<u32x4*>(ktile + buf * STAGE + key * LB + pc * 16) = pre[j];
-      }
+    for (int j = q * PER_SLOT; j < (q + 1) * PER_SLOT && j < LOADS; ++j) {
+      stash_piece(j, st & 1);
+      fetch_piece(j, st + 1);
     }
   };
   // B operands of the sub-tile at `sub` of a stage
@@ -181,17 +164,20 @@ __global__ __launch_bounds__(64 * ROWS) void k_prefill_score(PrefillArgs a) {
   uint32_t* hrow = hist + wv * (kPBins / 2);
   // sub-tiles A = keys key0..key0+31 and B = key0+32..key0+63: lanes 0..31 get
   // A's key l, lanes 32..63 B's key l-32, and the two lane halves' partials of
-  // one key meet in one add
-  auto finish = [&](int key0, float pa, float pb) {
+  // one key meet in one add.  The score is counted in the row's histogram here
+  // and stored later (see below).
+  auto score_pair = [&](int key0, float pa, float pb) {
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(pa), __float_as_uint(pb),
                                                      false, false);
     const float sc = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    const int u = key0 + lane;
-    if (u <= pos) {
-      srow[u] = sc;
+    if (key0 + lane <= pos) {
       const uint32_t bin = fast_key(sc) >> kPBinShift;
       atomicAdd(hrow + (bin >> 1), 1u << ((bin & 1u) * 16));
     }
+    return sc;
+  };
+  auto store_pair = [&](int key0, float sc) {
+    if (key0 + lane <= pos) srow[key0 + lane] = sc;
   };
 
   // Software pipeline over the workgroup's 32-key sub-tiles (the same count for
@@ -199,45 +185,61 @@ __global__ __launch_bounds__(64 * ROWS) void k_prefill_score(PrefillArgs a) {
   // j's operands are read one sub-tile ahead, and its epilogue runs under the
   // MFMAs of sub-tile j+1.  The barrier that publishes stage st+1 sits in
   // sub-tile 2 of stage st, after every wave has read its last operands of
-  // stage st-1 (whose buffer the stash overwrites), so sub-tile 3 can already
-  // read stage st+1.
-  fetch(0);
-  stash(0);
+  // stage st-1 (whose buffer stage st+1 reuses), so sub-tile 3 can already
+  // read stage st+1.  Stage st+1 is stored in four slots spread over the
+  // sub-tiles before that barrier (sub-tile 3 of stage st-1, sub-tiles 0-2 of
+  // stage st), each slot a full stage after the global loads it stores.
+  // Loads and stores share one completion counter, so a store-slot wait also
+  // covers every score store issued before it: both pairs' score stores go
+  // out together right after the barrier.
+#pragma unroll
+  for (int j = 0; j < LOADS; ++j) fetch_piece(j, 0);
+#pragma unroll
+  for (int j = 0; j < LOADS; ++j) stash_piece(j, 0);
+#pragma unroll
+  for (int j = 0; j < LOADS; ++j) fetch_piece(j, 1);
+  slot(0, 1);
   __syncthreads();
-  if (n_stages > 1) fetch(1);
   bf16x8 b0[S], b1[S];
   f32x16 accx[HT], accy[HT];
-  float pe = 0.f;
+  float pe = 0.f, sc_prev = 0.f;
   load_b(b0, ktile, 0);
   for (int st = 0; st < n_stages; ++st) {
     const uint8_t* tile = ktile + (st & 1) * STAGE;
-    const bool more = st + 1 < n_stages;
     const int k0 = st * kStageKeys;
     // (the scheduling fences keep each step's loads, MFMAs and epilogue
     // together, so no operand set is loaded more than one step ahead)
     load_b(b1, tile, 1);
     mfma(accx, b0);
-    if (st > 0) finish(k0 - 64, pe, epi(accy));
+    if (st > 0) sc_prev = score_pair(k0 - 64, pe, epi(accy));
+    slot(1, st + 1);
     __builtin_amdgcn_sched_barrier(0);
     load_b(b0, tile, 2);
     mfma(accy, b1);
     pe = epi(accx);
+    slot(2, st + 1);
     __builtin_amdgcn_sched_barrier(0);
     load_b(b1, tile, 3);
     mfma(accx, b0);
-    finish(k0, pe, epi(accy));
+    slot(3, st + 1);
+    __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
-    if (more) {
-      stash((st + 1) & 1);
-      __syncthreads();
-      if (st + 2 < n_stages) fetch(st + 2);
-      load_b(b0, ktile + ((st + 1) & 1) * STAGE, 0);
+    {
+      const float sc = score_pair(k0, pe, epi(accy));
+      if (st > 0) store_pair(k0 - 64, sc_prev);
+      store_pair(k0, sc);
     }
+    load_b(b0, ktile + ((st + 1) & 1) * STAGE, 0);
+    __builtin_amdgcn_sched_barrier(0);
     mfma(accy, b1);
     pe = epi(accx);
+    slot(0, st + 2);
     __builtin_amdgcn_sched_barrier(0);
   }
-  finish(n_stages * kStageKeys - 64, pe, epi(accy));
+  {
+    const int k_last = n_stages * kStageKeys - 64;
+    store_pair(k_last, score_pair(k_last, pe, epi(accy)));
+  }
 
   // this row's threshold: the 12-bit bin holding its k-th score
   if (pos < 0) return;
