@@ -295,7 +295,7 @@ __global__ __launch_bounds__(kST) void k_prefill_select(PrefillArgs a) {
   uint32_t* hist = reinterpret_cast<uint32_t*>(tie + 64);                 // [1024]
   uint32_t* scratch = hist + 1024;                                        // [64]
   __shared__ uint32_t s_out, s_ln;
-  const int t = blockIdx.x;
+  const int t = (int)gridDim.x - 1 - (int)blockIdx.x;          // longest rows first
   int pos = -1;
   {
     const int seq = a.q_seq ? a.q_seq[t] : 0;
@@ -327,7 +327,10 @@ __global__ __launch_bounds__(kST) void k_prefill_select(PrefillArgs a) {
   const Emitter em{out_i, out_s, &s_out, Kt};
   const bool fits = nb <= kSelListCap;
   // one pass over the row (16-byte loads): emit every score above the bin,
-  // collect the bin itself
+  // collect the bin itself.  The loads are unconditional (clamped to the
+  // row's last piece, masked afterwards) so that all of them are in flight
+  // together.  Keys are formed as in the scoring kernel's histogram (the
+  // stored scores are never -0.0).
   constexpr int U = 4;
   const uint32_t n4 = (n + 3) / 4;
   for (uint32_t base = 0; base < n4; base += kST * U) {
@@ -335,8 +338,9 @@ __global__ __launch_bounds__(kST) void k_prefill_select(PrefillArgs a) {
 #pragma unroll
     for (int j = 0; j < U; ++j) {
       const uint32_t i4 = base + threadIdx.x + j * kST;
-      if (i4 < n4) v[j] = *reinterpret_cast<const f32x4*>(sc + 4 * (size_t)i4);
+      v[j] = *reinterpret_cast<const f32x4*>(sc + 4 * (size_t)(i4 < n4 ? i4 : n4 - 1));
     }
+    __builtin_amdgcn_sched_barrier(0);             // issue every load first
 #pragma unroll
     for (int j = 0; j < U; ++j) {
       const uint32_t i4 = base + threadIdx.x + j * kST;
@@ -344,7 +348,7 @@ __global__ __launch_bounds__(kST) void k_prefill_select(PrefillArgs a) {
       for (int e = 0; e < 4; ++e) {
         const uint32_t u = 4 * i4 + e;
         const bool ok = i4 < n4 && u < n;
-        const uint32_t key = ok ? score_to_key(v[j][e]) : 0u;
+        const uint32_t key = ok ? fast_key(v[j][e]) : 0u;
         const int b = ok ? (int)(key >> kPBinShift) : -1;
         em.put_wave(b > bstar, key, (int32_t)u);
         if (fits) list_put_wave(b == bstar, make_uint2(key, u), list, &s_ln, kSelListCap);
