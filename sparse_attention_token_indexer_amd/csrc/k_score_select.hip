@@ -190,19 +190,22 @@ __global__ __launch_bounds__(kNT) void k_score_emit(SelArgs a) {
   const int n_tiles = (n_c + 31) / 32;
   const int wv = wave_id();
   {
-    typename SC::Frag fa, fb;
+    // three tile fragments in rotation: while one tile is scored, the wave's
+    // next two tiles are in flight
+    typename SC::Frag fa, fb, fc;
     int tile = wv;
     if (tile < n_tiles) load_tile<SC, MODE>(a, t, r, i0, n_c, tile, fa);
-    for (; tile < n_tiles; tile += 2 * kNW) {
-      const int t1 = tile + kNW, t2 = tile + 2 * kNW;
-      if (t1 < n_tiles) load_tile<SC, MODE>(a, t, r, i0, n_c, t1, fb);
-      float s0 = sc.score(fa);
-      store_score<SC, MODE>(a, t, r, i0, n_c, tile, s0, skey);
-      if (t2 < n_tiles) load_tile<SC, MODE>(a, t, r, i0, n_c, t2, fa);
-      if (t1 < n_tiles) {
-        float s1 = sc.score(fb);
-        store_score<SC, MODE>(a, t, r, i0, n_c, t1, s1, skey);
-      }
+    if (tile + kNW < n_tiles) load_tile<SC, MODE>(a, t, r, i0, n_c, tile + kNW, fb);
+    for (; tile < n_tiles; tile += 3 * kNW) {
+      const int t1 = tile + kNW, t2 = tile + 2 * kNW, t3 = tile + 3 * kNW, t4 = tile + 4 * kNW;
+      if (t2 < n_tiles) load_tile<SC, MODE>(a, t, r, i0, n_c, t2, fc);
+      store_score<SC, MODE>(a, t, r, i0, n_c, tile, sc.score(fa), skey);
+      if (t1 >= n_tiles) break;
+      if (t3 < n_tiles) load_tile<SC, MODE>(a, t, r, i0, n_c, t3, fa);
+      store_score<SC, MODE>(a, t, r, i0, n_c, t1, sc.score(fb), skey);
+      if (t2 >= n_tiles) break;
+      if (t4 < n_tiles) load_tile<SC, MODE>(a, t, r, i0, n_c, t4, fb);
+      store_score<SC, MODE>(a, t, r, i0, n_c, t2, sc.score(fc), skey);
     }
   }
   __syncthreads();
