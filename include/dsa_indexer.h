@@ -42,7 +42,9 @@
  *    at the start of each call); two calls that run concurrently must not share
  *    a workspace.
  *  - Supported shapes: head_dim 64 or 128; 1 <= n_heads <= 64; bf16 inputs
- *    use MFMA, float32 inputs (dense call only) the vector ALUs.
+ *    use MFMA, float32 inputs (dense call only) the vector ALUs; l_max (and
+ *    any candidate list a pass scores) at most 67108864 = 8192 * 8192
+ *    items per query (DSA_EUNSUPPORTED beyond).
  */
 #ifndef DSA_INDEXER_H
 #define DSA_INDEXER_H

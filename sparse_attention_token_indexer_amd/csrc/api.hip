@@ -97,10 +97,14 @@ hipError_t run_score_select(const dsa::SelArgs& a, hipStream_t stream) {
 }
 
 constexpr int kBins = 4096;
+// Chunks of up to 8192 items.  (One round of 16384-item chunks over 64
+// queries x 128K keys, which leaves a single selection phase per call,
+// measured slower than two rounds of 8192.)
 constexpr int kMaxChunk = 8192;
 constexpr int kMinChunk = 256;
 constexpr int64_t kTargetWorkgroups = 512;   // >= 2 per compute unit on MI355X
 constexpr size_t kMaxLds = 64 * 1024;
+constexpr int64_t kMaxItems = (int64_t)kMaxChunk * dsa::kMaxChunks;   // per query and pass
 constexpr int kMaxTopK = 1 << 20;
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -129,8 +133,9 @@ int choose_chunk(int64_t n_items, int64_t nq, int f32, int head_dim) {
          dsa::score_select_lds_bytes(chunk, f32, head_dim) > kMaxLds)
     chunk >>= 1;
   while (chunk > kMinChunk && nq * cdiv(n_items, chunk) < kTargetWorkgroups) chunk >>= 1;
-  // the merge keeps one offset per chunk in LDS
-  while (cdiv(n_items, chunk) > dsa::kMaxChunks && chunk < (1 << 20)) chunk <<= 1;
+  // the merge keeps one offset per chunk in LDS (n_items is at most
+  // kMaxChunk * kMaxChunks, checked with the arguments)
+  while (cdiv(n_items, chunk) > dsa::kMaxChunks && chunk < kMaxChunk) chunk <<= 1;
   return chunk;
 }
 
@@ -171,6 +176,9 @@ int check_common(const void* q, const float* w, const void* k, int32_t dtype, co
     return fail(DSA_EUNSUPPORTED, "head_dim must be 64 or 128 (got %d)", head_dim);
   if (n_seq < 1) return fail(DSA_EINVAL, "n_seq must be >= 1 (got %d)", n_seq);
   if (l_max < 1 || l_max > 0x7FFFFFFF) return fail(DSA_EINVAL, "l_max must be in [1, 2^31) (got %lld)", (long long)l_max);
+  if (l_max > kMaxItems)
+    return fail(DSA_EUNSUPPORTED, "l_max above %lld is not supported (got %lld)",
+                (long long)kMaxItems, (long long)l_max);
   if (top_k < 1 || top_k > kMaxTopK) return fail(DSA_EINVAL, "top_k must be in [1, %d] (got %d)", kMaxTopK, top_k);
   if (nq == 0) return DSA_OK;
   if (!q || !w || !k || !q_pos || !out_idx)

@@ -73,9 +73,12 @@ struct ScorerMfma32 {
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht)
         acc[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ht][s], b[s], acc[ht], 0, 0, 0);
-    float p = weighted_relu_sum<HT>(acc, W, std::make_integer_sequence<int, 16>{});
-    p += shfl_xor_f(p, 32);
-    return p;
+    const float p = weighted_relu_sum<HT>(acc, W, std::make_integer_sequence<int, 16>{});
+    // the two lane halves' partials of key lane%32 meet in one add (a lane
+    // half swap keeps this off the LDS queue)
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p), __float_as_uint(p),
+                                                     false, false);
+    return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   }
 };
 

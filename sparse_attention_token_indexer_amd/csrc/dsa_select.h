@@ -221,44 +221,77 @@ DSA_DEVICE void finish_bin(const uint2* list, uint32_t nl, uint32_t need, int bs
 }
 
 // Chunk-side half of a selection pass (run by every chunk workgroup).
-// skey[0..n) holds the chunk's score keys (0 = invalid item); hist is LDS
-// scratch of kBins words.  Appends the chunk's candidates (key, id) to seg and
-// writes their count to *seg_cnt.
+// skey[0..n) holds the chunk's score keys (0 = invalid item); hist is LDS of
+// kBins words, already zeroed (the caller has synchronised the workgroup).
+// Appends the chunk's candidates (key, id) to seg and writes their count to
+// *seg_cnt.
 template <int NT, class IdOf>
 DSA_DEVICE void chunk_emit(const uint32_t* skey, int n, int top_k, IdOf id_of, uint2* seg,
                            uint32_t* seg_cnt, uint32_t* ghist_g, uint32_t* hist,
                            uint32_t* scratch) {
+  static_assert(kBins % NT == 0, "whole bin runs per thread");
+  constexpr int PER = kBins / NT;
+  constexpr int U = 8;
   __shared__ uint32_t s_cnt;
-  for (int i = threadIdx.x; i < kBins; i += NT) hist[i] = 0;
-  if (threadIdx.x == 0) s_cnt = 0;
-  __syncthreads();
-  for (int i = threadIdx.x; i < n; i += NT) {
-    uint32_t k = skey[i];
-    if (k) atomicAdd(&hist[k >> kBinShift], 1u);
+  __shared__ int s_bc;
+  // the chunk's 12-bit histogram (keys read U at a time so that the reads
+  // are in flight together)
+  for (int base = 0; base < n; base += NT * U) {
+    uint32_t k[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = base + (int)threadIdx.x + u * NT;
+      k[u] = i < n ? skey[i] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (k[u]) atomicAdd(&hist[k[u] >> kBinShift], 1u);
   }
   __syncthreads();
-  // publish this chunk's histogram, then read the query's running histogram
-  for (int b = threadIdx.x; b < kBins; b += NT) {
-    uint32_t h = hist[b];
-    if (h) atomicAdd(ghist_g + b, h);
+  // Publish this chunk's histogram and read back the query's running counts
+  // (bin b = threadIdx.x + j * NT: every instruction covers consecutive
+  // words), never taking less than this chunk's own count (its own
+  // publication may not be visible yet; other chunks' counts only ever
+  // under-count).
+  {
+    uint32_t own[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) own[j] = hist[threadIdx.x + j * NT];
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      if (own[j]) atomicAdd(ghist_g + threadIdx.x + j * NT, own[j]);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const uint32_t g = __hip_atomic_load(ghist_g + threadIdx.x + j * NT, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+      hist[threadIdx.x + j * NT] = g > own[j] ? g : own[j];
+    }
   }
+  if (threadIdx.x == 0) { s_cnt = 0; s_bc = 0; }
   __syncthreads();
-  uint32_t seen = 0;
-  for (int b = threadIdx.x; b < kBins; b += NT) {
-    uint32_t g = __hip_atomic_load(ghist_g + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    uint32_t own = hist[b];
-    g = g > own ? g : own;                 // never below this chunk's own count
-    hist[b] = g;
-    seen += g;
+  // the bound: the highest bin b with (running count of bins >= b) >= top_k,
+  // bin 0 (every entry) when the running counts hold fewer than top_k.
+  // Thread t scans the run of PER bins just below the runs of threads < t.
+  const int top = kBins - 1 - (int)threadIdx.x * PER;
+  uint32_t cnt[PER];
+  uint32_t mine = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    cnt[i] = hist[top - i];
+    mine += cnt[i];
   }
   uint32_t total;
-  (void)block_exclusive_sum<NT>(seen, scratch, &total);
-  __syncthreads();
-  int bc = 0;
-  if (total >= (uint32_t)top_k) {
-    uint32_t above;
-    bc = block_find_threshold<NT>(hist, kBins, (uint32_t)top_k, scratch, &above);
+  const uint32_t before = block_exclusive_sum<NT>(mine, scratch, &total);   // higher bins
+  if (total >= (uint32_t)top_k && before < (uint32_t)top_k && before + mine >= (uint32_t)top_k) {
+    uint32_t acc = before;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      acc += cnt[i];
+      if (acc >= (uint32_t)top_k) { s_bc = top - i; break; }
+    }
   }
+  __syncthreads();
+  const int bc = s_bc;
   const int lane = lane_id();
   for (int base = 0; base < n; base += NT) {
     int i = base + (int)threadIdx.x;

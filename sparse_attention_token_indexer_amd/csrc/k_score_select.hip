@@ -183,6 +183,7 @@ __global__ __launch_bounds__(kNT) void k_score_emit(SelArgs a) {
   }
   SC sc;
   sc.init(q_t, w_t, heads_t, a.h_use, sc_lds);
+  for (int i = threadIdx.x; i < kBins; i += kNT) hist[i] = 0;   // counted after the loop
   __syncthreads();
 
   const int64_t i0 = (int64_t)c * a.chunk;

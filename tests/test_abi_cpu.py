@@ -71,6 +71,8 @@ def test_argument_errors_return_before_any_launch(lib):
     assert _call_dense(lib, q=aligned, k=aligned, ws_bytes=10) == 3    # workspace too small
     assert b"workspace" in lib.dsa_last_error()
     assert _call_dense(lib, nq=0) == 0                                 # nothing to do
+    assert _call_dense(lib, q=aligned, k=aligned, l_max=8192 * 8192 + 1) == 2   # too long
+    assert b"l_max" in lib.dsa_last_error()
     assert lib.indexer_mean_pool_keys(aligned, 1, 1, 100, 128, 64, aligned, None) == 2
     assert lib.indexer_selection_iou(aligned, aligned, 1, 9000, aligned, None) == 2
     assert lib.misa_route_score_topk(aligned, aligned, aligned, None, 0, None, aligned, 1, 8, 128,
