@@ -310,45 +310,109 @@ DSA_DEVICE void chunk_emit(const uint32_t* skey, int n, int top_k, IdOf id_of, u
   if (threadIdx.x == 0) *seg_cnt = s_cnt;
 }
 
+// Brute-force finish of nl <= 64 entries held in LDS (distinct composites),
+// by the first wave alone: entry i is emitted iff fewer than `need` entries
+// beat it.
+DSA_DEVICE void rank_finish64(const uint2* list, uint32_t nl, uint32_t need, const Emitter& em) {
+  if (threadIdx.x < 64) {
+    const uint32_t i = threadIdx.x;
+    const bool have = i < nl;
+    const uint2 me = have ? list[i] : make_uint2(0u, 0u);
+    const uint64_t cm = composite(me.x, (int32_t)me.y);
+    uint32_t rank = 0;
+    for (uint32_t j = 0; j < nl; ++j) {         // every lane reads the same entry
+      const uint2 o = list[j];
+      rank += composite(o.x, (int32_t)o.y) > cm ? 1u : 0u;
+    }
+    em.put_wave(have && rank < need, me.x, (int32_t)me.y);
+  }
+  __syncthreads();
+}
+
+// Block-wide exclusive prefix of v (returned) and totals of v and u, with one
+// pair of barriers.  scratch: 2 * NT / 64 words.
+template <int NT>
+DSA_DEVICE uint32_t block_exclusive_sum2(uint32_t v, uint32_t u, uint32_t* scratch,
+                                         uint32_t* tot_v, uint32_t* tot_u) {
+  constexpr int NW = NT / 64;
+  const int lane = lane_id(), wv = wave_id();
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  uint32_t su = u;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) su += __shfl_xor(su, o, 64);
+  if (lane == 63) scratch[wv] = x;
+  if (lane == 0) scratch[NW + wv] = su;
+  __syncthreads();
+  uint32_t base = 0, tv = 0, tu = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const uint32_t sv = scratch[i];
+    if (i < wv) base += sv;
+    tv += sv;
+    tu += scratch[NW + i];
+  }
+  __syncthreads();
+  *tot_v = tv;
+  *tot_u = tu;
+  return base + x - v;
+}
+
 // Merge of one query's candidates (merge kernel, one workgroup per query).
 // ghist_g is the complete histogram of all the query's valid items; off_lds
-// must hold n_chunks + 1 words; lds_list room for lcap pairs; hist kBins words.
-// Writes Kt = min(top_k, valid items) entries (any order), then (-1, -inf).
+// must hold n_chunks + 1 words; lds_list room for lcap pairs; hist kBins words;
+// scratch 64 words.  Writes Kt = min(top_k, valid items) entries (any order),
+// then (-1, -inf).
 template <int NT>
 DSA_DEVICE void merge_query(const uint2* cand, const uint32_t* cnt, int n_chunks, int chunk,
                             const uint32_t* ghist_g, int top_k, int32_t* out_idx,
                             float* out_score, uint2* lds_list, uint32_t lcap, uint32_t* off_lds,
                             uint32_t* hist, uint32_t* scratch) {
+  static_assert(kBins % NT == 0 && 2 * NT / 64 <= 64, "merge block shape");
+  constexpr int PER = kBins / NT;
   __shared__ uint32_t s_out, s_ln;
-  uint32_t nv = 0;
-  for (int i = threadIdx.x; i < kBins; i += NT) {
-    uint32_t h = ghist_g[i];
-    hist[i] = h;
-    nv += h;
+  const int tid = (int)threadIdx.x;
+  // the histogram and the first NT segment counts are loaded together
+  uint32_t h[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) h[j] = ghist_g[tid + j * NT];
+  uint32_t v0 = 0;
+  if (tid < n_chunks) {
+    v0 = cnt[tid];
+    if (v0 > (uint32_t)chunk) v0 = (uint32_t)chunk;   // clamp to the segment capacity
   }
-  uint32_t n_valid;
-  (void)block_exclusive_sum<NT>(nv, scratch, &n_valid);
-  // chunk offsets (segment counts clamped to the segment capacity)
-  uint32_t run = 0;
-  for (int base = 0; base < n_chunks; base += NT) {
-    int c = base + (int)threadIdx.x;
+  uint32_t nv = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    hist[tid + j * NT] = h[j];
+    nv += h[j];
+  }
+  uint32_t run, n_valid;
+  const uint32_t ex0 = block_exclusive_sum2<NT>(v0, nv, scratch, &run, &n_valid);
+  if (tid < n_chunks) off_lds[tid] = ex0;
+  for (int base = NT; base < n_chunks; base += NT) {     // more than NT chunks
+    const int c = base + tid;
     uint32_t v = 0;
     if (c < n_chunks) {
       v = cnt[c];
       if (v > (uint32_t)chunk) v = (uint32_t)chunk;
     }
     uint32_t tot;
-    uint32_t ex = block_exclusive_sum<NT>(v, scratch, &tot);
+    const uint32_t ex = block_exclusive_sum<NT>(v, scratch, &tot);
     if (c < n_chunks) off_lds[c] = run + ex;
     run += tot;
   }
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     off_lds[n_chunks] = run;
     s_out = 0;
     s_ln = 0;
   }
   const uint32_t Kt = n_valid < (uint32_t)top_k ? n_valid : (uint32_t)top_k;
-  for (int i = Kt + threadIdx.x; i < top_k; i += NT) {
+  for (int i = Kt + tid; i < top_k; i += NT) {
     out_idx[i] = -1;
     if (out_score) out_score[i] = -__builtin_inff();
   }
@@ -359,25 +423,41 @@ DSA_DEVICE void merge_query(const uint2* cand, const uint32_t* cnt, int n_chunks
   const uint32_t nb = hist[bstar];
   const uint32_t need = Kt - above;
   __syncthreads();
-  Emitter em{out_idx, out_score, &s_out, Kt};
-  FlatSegSource seg{cand, off_lds, n_chunks, chunk};
+  const Emitter em{out_idx, out_score, &s_out, Kt};
+  const FlatSegSource seg{cand, off_lds, n_chunks, chunk};
   const bool fits = nb <= lcap;
-  seg.for_each<NT>([&](uint2 e) {
-    int b = (int)(e.x >> kBinShift);
-    if (b > bstar) {
-      em.put(e.x, (int32_t)e.y);
-    } else if (b == bstar && fits) {
-      uint32_t l = atomicAdd(&s_ln, 1u);
-      if (l < lcap) lds_list[l] = e;
+  // one wave-uniform pass over the candidates: emit everything above the
+  // k-th entry's bin, collect that bin
+  {
+    constexpr int U = 4;
+    const uint32_t total = off_lds[n_chunks];
+    for (uint32_t base = 0; base < total; base += NT * U) {
+      uint2 e[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t f = base + tid + u * NT;
+        e[u] = f < total ? seg.at(f) : make_uint2(0u, 0u);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const bool valid = base + tid + u * NT < total;
+        const int b = (int)(e[u].x >> kBinShift);
+        em.put_wave(valid && b > bstar, e[u].x, (int32_t)e[u].y);
+        if (fits) list_put_wave(valid && b == bstar, e[u], lds_list, &s_ln, lcap);
+      }
     }
-  });
+  }
   __syncthreads();
   const uint64_t prefix = (uint64_t)bstar << (64 - kBinBits);
   const uint64_t mask = (uint64_t)(kBins - 1) << (64 - kBinBits);
   if (fits) {
     const uint32_t nl = s_ln < nb ? s_ln : nb;   // the list holds s_ln <= lcap entries
-    LdsSource src{lds_list, nl};
-    radix_finish<NT>(src, prefix, mask, 64 - kBinBits, need, nl, em, hist, scratch);
+    if (need < nl && nl <= 64) {
+      rank_finish64(lds_list, nl, need, em);
+    } else {
+      LdsSource src{lds_list, nl};
+      radix_finish<NT>(src, prefix, mask, 64 - kBinBits, need, nl, em, hist, scratch);
+    }
   } else {
     radix_finish<NT>(seg, prefix, mask, 64 - kBinBits, need, nb, em, hist, scratch);
   }
