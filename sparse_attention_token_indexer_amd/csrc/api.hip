@@ -89,10 +89,25 @@ hipError_t timed_pool(hipStream_t stream, F&& f) {
   return timed(DSA_KERNEL_POOL, stream, f);
 }
 
-// One selection pass: the score-and-emit kernel, then the merge kernel.
-hipError_t run_score_select(const dsa::SelArgs& a, hipStream_t stream) {
+// Most items one query can have in a pass.
+int64_t pass_items_max(const dsa::SelArgs& a) {
+  switch (a.mode) {
+    case dsa::MODE_RANGE: return a.l_max;
+    case dsa::MODE_POOLED: return a.m_max;
+    case dsa::MODE_LIST: return a.list_len;
+    default: return (int64_t)a.list_len * a.block;
+  }
+}
+
+// One selection pass: the score-and-emit kernel, then the merge kernel; or, for
+// a short pass (every query has at most kShortItems items), the scoring kernel
+// storing every item's (key, id) and the one-workgroup-per-query select.
+hipError_t run_score_select(dsa::SelArgs a, hipStream_t stream) {
+  a.store_all = pass_items_max(a) <= dsa::kShortItems ? 1 : 0;
   hipError_t e = timed(score_kind(a.mode), stream, [&] { return dsa::launch_score_emit(a, stream); });
   if (e != hipSuccess) return e;
+  if (a.store_all)
+    return timed(DSA_KERNEL_MERGE, stream, [&] { return dsa::launch_select_short(a, stream); });
   return timed(DSA_KERNEL_MERGE, stream, [&] { return dsa::launch_merge(a, stream); });
 }
 

@@ -34,6 +34,8 @@ struct SelArgs {
   int block, list_len, top_k, chunk, n_chunks;
   int f32;                     // inputs are float32
   int mode;
+  int store_all;               // short pass: every item's (key, id) to cand, no emission
+                               // (selected by the short-pass select kernel)
   // workspace
   uint2* cand;                 // [nq, n_chunks, chunk]
   uint32_t* cand_cnt;          // [nq, n_chunks]
@@ -47,6 +49,10 @@ struct SelArgs {
 // launched in that order on one stream.
 hipError_t launch_score_emit(const SelArgs& a, hipStream_t stream);
 hipError_t launch_merge(const SelArgs& a, hipStream_t stream);
+// Short passes (at most kShortItems items per query): exact top-k of one
+// query's (key, id) pairs in one workgroup.
+constexpr int kShortItems = 16384;
+hipError_t launch_select_short(const SelArgs& a, hipStream_t stream);
 constexpr int kMaxChunks = 8192;        // chunks per query in one pass
 constexpr int kMergeListCap = 12288;    // tie-bin entries resolved in LDS
 size_t score_select_lds_bytes(int chunk, int f32, int head_dim);

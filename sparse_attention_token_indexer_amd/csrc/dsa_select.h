@@ -56,8 +56,8 @@ DSA_DEVICE void list_put_wave(bool take, uint2 e, uint2* list, uint32_t* count, 
   if (take && o < cap) list[o] = e;
 }
 
-// Entries held in LDS.
-struct LdsSource {
+// (key, id) pairs at a plain pointer (LDS or device memory).
+struct PairSource {
   const uint2* e;
   uint32_t n;
   template <int NT, class F>
@@ -214,7 +214,7 @@ DSA_DEVICE void finish_bin(const uint2* list, uint32_t nl, uint32_t need, int bs
     __syncthreads();
     return;
   }
-  LdsSource src{list, nl};
+  PairSource src{list, nl};
   const uint64_t prefix = ((uint64_t)bstar << (64 - kBinBits)) | ((uint64_t)d2 << (32 + SH2));
   const uint64_t mask = ((uint64_t)((1u << (kBinBits + D2)) - 1u)) << (32 + SH2);
   radix_finish<NT>(src, prefix, mask, 32 + SH2, need2, nd2, em, hist, scratch);
@@ -455,7 +455,7 @@ DSA_DEVICE void merge_query(const uint2* cand, const uint32_t* cnt, int n_chunks
     if (need < nl && nl <= 64) {
       rank_finish64(lds_list, nl, need, em);
     } else {
-      LdsSource src{lds_list, nl};
+      PairSource src{lds_list, nl};
       radix_finish<NT>(src, prefix, mask, 64 - kBinBits, need, nl, em, hist, scratch);
     }
   } else {

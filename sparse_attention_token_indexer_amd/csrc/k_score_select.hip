@@ -219,6 +219,13 @@ __global__ __launch_bounds__(kNT) void k_score_emit(SelArgs a) {
     item_of<MODE>(a, t, r, i0 + i, id, p);
     return id;
   };
+  if (a.store_all) {           // short pass: every item, key 0 = not a valid key
+    for (int i = threadIdx.x; i < n_c; i += kNT) {
+      const uint32_t k = skey[i];
+      seg[i] = make_uint2(k, k ? (uint32_t)id_of(i) : 0u);
+    }
+    return;
+  }
   chunk_emit<kNT>(skey, n_c, a.top_k, id_of, seg, a.cand_cnt + (size_t)t * a.n_chunks + c,
                   a.ghist + (size_t)t * kBins, hist, scratch);
 }
@@ -242,6 +249,91 @@ __global__ __launch_bounds__(kMT) void k_merge(SelArgs a) {
 }
 
 constexpr size_t kMergeLds = (kBins + 64 + kMaxChunks + 2) * 4 + (size_t)kMergeListCap * 8;
+
+// Short-pass selection: one workgroup per query selects from all its (key, id)
+// pairs (key 0 = not a valid item), which the scoring kernel stored
+// contiguously per query.  The pairs stay in registers (kShortPer per
+// thread); one 12-bit histogram in LDS gives the bin b* of the k-th entry;
+// one wave-aggregated pass emits every entry above b* and collects b*, which
+// finish_bin resolves (or, when b* overflows its LDS list, the radix finish
+// over the query's pairs in memory).
+constexpr int kST = 1024;
+constexpr int kShortPer = kShortItems / kST;
+constexpr uint32_t kShortListCap = 4096;
+constexpr size_t kShortLds = (kBins + 64) * 4 + ((size_t)kShortListCap + 64) * 8;
+
+template <int MODE>
+__global__ __launch_bounds__(kST) void k_select_short(SelArgs a) {
+  extern __shared__ uint32_t smem[];
+  uint32_t* hist = smem;                                    // [kBins]
+  uint32_t* scratch = hist + kBins;                         // [64]
+  uint2* list = reinterpret_cast<uint2*>(scratch + 64);     // [kShortListCap]
+  uint2* tie = list + kShortListCap;                        // [64]
+  __shared__ uint32_t s_out, s_ln;
+  const int t = blockIdx.x, tid = (int)threadIdx.x;
+  const Row r = row_of<MODE>(a, t);
+  const int n = (int)(r.n_items < kShortItems ? r.n_items : kShortItems);
+  int32_t* out_i = a.out_idx + (size_t)t * a.top_k;
+  float* out_s = a.out_score ? a.out_score + (size_t)t * a.top_k : nullptr;
+  const uint2* row = a.cand + (size_t)t * a.n_chunks * a.chunk;
+  uint2 e[kShortPer];
+#pragma unroll
+  for (int j = 0; j < kShortPer; ++j) {
+    const int i = tid + j * kST;
+    e[j] = i < n ? row[i] : make_uint2(0u, 0u);
+  }
+  for (int i = tid; i < kBins; i += kST) hist[i] = 0;
+  if (tid == 0) { s_out = 0; s_ln = 0; }
+  __syncthreads();
+  uint32_t nv = 0;
+#pragma unroll
+  for (int j = 0; j < kShortPer; ++j)
+    if (e[j].x) {
+      atomicAdd(&hist[e[j].x >> kBinShift], 1u);
+      ++nv;
+    }
+  uint32_t n_valid;
+  (void)block_exclusive_sum<kST>(nv, scratch, &n_valid);
+  const uint32_t Kt = n_valid < (uint32_t)a.top_k ? n_valid : (uint32_t)a.top_k;
+  for (int i = (int)Kt + tid; i < a.top_k; i += kST) {
+    out_i[i] = -1;
+    if (out_s) out_s[i] = -__builtin_inff();
+  }
+  if (Kt == 0) return;
+  uint32_t above;
+  const int bstar = block_find_threshold<kST>(hist, kBins, Kt, scratch, &above);
+  const uint32_t nb = hist[bstar];
+  const uint32_t need = Kt - above;
+  const Emitter em{out_i, out_s, &s_out, Kt};
+  const bool fits = nb <= kShortListCap;
+#pragma unroll
+  for (int j = 0; j < kShortPer; ++j) {
+    const bool valid = e[j].x != 0u;
+    const int b = (int)(e[j].x >> kBinShift);
+    em.put_wave(valid && b > bstar, e[j].x, (int32_t)e[j].y);
+    if (fits) list_put_wave(valid && b == bstar, e[j], list, &s_ln, kShortListCap);
+  }
+  __syncthreads();
+  if (fits) {
+    const uint32_t nl = s_ln < nb ? s_ln : nb;
+    finish_bin<kST>(list, nl, need, bstar, em, hist, scratch, tie);
+  } else {
+    const uint64_t prefix = (uint64_t)bstar << (64 - kBinBits);
+    const uint64_t mask = (uint64_t)(kBins - 1) << (64 - kBinBits);
+    PairSource src{row, (uint32_t)n};
+    radix_finish<kST>(src, prefix, mask, 64 - kBinBits, need, nb, em, hist, scratch);
+  }
+}
+
+template <int MODE>
+hipError_t launch_select_short_t(const SelArgs& a, hipStream_t stream) {
+  auto k = k_select_short<MODE>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kShortLds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k, dim3(a.nq), dim3(kST), kShortLds, stream, a);
+  return hipGetLastError();
+}
 
 template <class SC, int MODE>
 hipError_t launch_t(const SelArgs& a, hipStream_t stream) {
@@ -283,6 +375,17 @@ size_t score_select_lds_bytes(int chunk, int f32, int head_dim) {
   size_t b = (size_t)chunk * 4 + kBins * 4 + 64 * 4;
   if (f32) b += (size_t)(64 * head_dim + 64) * 4;
   return b;
+}
+
+hipError_t launch_select_short(const SelArgs& a, hipStream_t stream) {
+  if ((int64_t)a.n_chunks * a.chunk < 1) return hipErrorInvalidValue;
+  switch (a.mode) {
+    case MODE_RANGE: return launch_select_short_t<MODE_RANGE>(a, stream);
+    case MODE_POOLED: return launch_select_short_t<MODE_POOLED>(a, stream);
+    case MODE_LIST: return launch_select_short_t<MODE_LIST>(a, stream);
+    case MODE_BLOCKS: return launch_select_short_t<MODE_BLOCKS>(a, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_merge(const SelArgs& a, hipStream_t stream) {
