@@ -58,9 +58,27 @@ def test_decode_many_chunks_ragged(dsa):
 
 
 def test_decode_small_chunks(dsa):
-    """Few queries, so the library splits each prefix into many 256-key chunks."""
-    wl = datagen.small(2, nq=4, n_seq=4, l_max=9000)
+    """Few queries with prefixes longer than a short pass (16384 items), so the
+    library splits each prefix into many 256-key chunks."""
+    wl = datagen.small(2, nq=4, n_seq=4, l_max=20000)
     _run_dense(dsa, wl)
+
+
+def test_short_pass_switch_point(dsa):
+    """16384 keys per query go through the short pass (every (key, id) stored,
+    one workgroup per query selects); 16385 through the chunked pass with the
+    merge.  Both against the oracle, with a prefix shorter than k as well."""
+    for L in (16384, 16385):
+        wl = datagen.small(2, nq=6, n_seq=6, l_max=L)
+        inp = datagen.make(wl, 7)
+        inp["q_pos"] = np.array([L - 1, L - 2, 9000, 2047, 100, 0], dtype=np.int32)
+        say(f"[dense] switch point L={L}")
+        dev = upload(inp, wl)
+        idx, val = dsa.indexer_score_topk(dev["q"], dev["w"], dev["k"], dev["q_pos"], dev["q_seq"],
+                                          top_k=2048)
+        ref, qwk = dense_ref(inp, wl, range(6), 2048)
+        errs = check_rows(idx.cpu().numpy(), val.cpu().numpy(), ref, 2048, qwk)
+        assert not errs, "\n".join(errs[:10])
 
 
 def test_short_prefixes_and_padding(dsa):
