@@ -9,8 +9,8 @@ with inputs resident in HBM.  Prints one JSON line.
 Other workloads (--workload): tiny (float32, 16 queries, L = 4096),
 dense_prefill (32768 causal rows of one 32768-key cache), misa / misa_dagger
 (h = 8 of 64 heads, B = 64, k' = 8192), hisa (32 heads, L = 1M, B = 128,
-m = 64; timed with a cold last-level cache), pool (mean pooling of the 128K
-caches).
+m = 64), pool (mean pooling of the 128K caches).  tiny and hisa touch less
+than the 256 MB last-level cache and are timed cold.
 
 The steps are timed twice: first the calls alone (ms_per_step, value), then
 the same number of calls with the library's per-launch HIP events on the
@@ -196,6 +196,8 @@ def main() -> int:
         kind = "prefill"
         kernel_bytes = None
         kernel_flops = pairs * H * d * 2
+        call_bytes = nq * H * d * eb + L * d * eb + nq * H * 4 + nq * topk * 8
+        call_flops = kernel_flops
         bound_note = "MFMA: the head contraction of every causal (query, key) pair"
     elif name in ("dense_decode", "tiny"):
         nbytes = dsa.indexer_score_topk_workspace_size(nq, H, d, wl.n_seq, L, topk,
@@ -207,6 +209,7 @@ def main() -> int:
                                    out_score=out_s, workspace=ws)
         kind = "score_tokens"
         kernel_bytes = pairs * d * eb + io_bytes
+        call_bytes, call_flops = kernel_bytes, pairs * H * d * 2
         bound_note = "HBM: every prefix key row is read once"
     elif name in ("misa", "misa_dagger"):
         kp = dsa.indexer_mean_pool_keys(k, wl.block)
@@ -223,6 +226,12 @@ def main() -> int:
         kind = "score_tokens"
         h = wl.n_active_heads
         kernel_bytes = pairs * d * eb + nq * h * d * eb + nq * h * 4 + nq * (kprime or topk) * (4 if kprime else 8)
+        M = -(-L // wl.block)
+        call_bytes = pairs * d * eb + wl.n_seq * M * d * 2 + io_bytes   # keys + pooled + q, w, out
+        call_flops = nq * H * M * d * 2 + pairs * h * d * 2               # router + routed pass
+        if kprime:
+            call_bytes += nq * kprime * (d * eb + 8)                       # gathered candidates
+            call_flops += nq * kprime * H * d * 2                          # all-head rescoring
         bound_note = "HBM: the routed pass still reads every prefix key row"
     elif name == "hisa":
         kp = dsa.indexer_mean_pool_keys(k, wl.block)
@@ -236,6 +245,9 @@ def main() -> int:
                                        out_score=out_s, workspace=ws)
         kind = "score_blocks"
         kernel_bytes = nq * wl.m_blocks * wl.block * d * eb + nq * wl.m_blocks * 4 + io_bytes
+        M = -(-L // wl.block)
+        call_bytes = wl.n_seq * M * d * 2 + nq * wl.m_blocks * wl.block * d * eb + io_bytes
+        call_flops = nq * M * H * d * 2 + nq * wl.m_blocks * wl.block * H * d * 2
         bound_note = "HBM: gathers the keys of the m surviving blocks"
     elif name == "pool":
         M = -(-L // wl.block)
@@ -245,6 +257,7 @@ def main() -> int:
             dsa.indexer_mean_pool_keys(k, wl.block, out=kp)
         kind = "pool"
         kernel_bytes = wl.n_seq * L * d * eb + wl.n_seq * M * d * 2
+        call_bytes, call_flops = kernel_bytes, wl.n_seq * L * d
         bound_note = "HBM: reads the key cache once, writes the pooled keys"
     else:
         raise ValueError(name)
@@ -252,7 +265,7 @@ def main() -> int:
     # Workloads that touch less than the 256 MB last-level cache are timed cold:
     # a 512 MiB buffer is overwritten before every step (outside its timing).
     flush = None
-    if name == "hisa":
+    if name in ("hisa", "tiny"):
         flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
 
     def timed_region() -> float:
@@ -297,6 +310,21 @@ def main() -> int:
         if r["launches"]:
             per_kernel[other] = round(r["total_ms"] / r["launches"] * 1e3, 2)
     dsa.kernel_timing(False)
+    # pass 3: every call bracketed by its own events (median and minimum)
+    per_call = []
+    for _ in range(args.steps):
+        if flush is not None:
+            flush.zero_()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        step()
+        e1.record()
+        torch.cuda.synchronize()
+        per_call.append(e0.elapsed_time(e1))
+    per_call.sort()
+    call_med_ms = per_call[len(per_call) // 2]
     k_avg_ms = kt["total_ms"] / max(kt["launches"], 1)
     per_kernel[kind] = round(k_avg_ms * 1e3, 2)
     traffic = stored_traffic(name)
@@ -336,7 +364,8 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16" if eb == 2 else "f32",
         "data": "synthetic (seeded; planted-key recipe of the workload)",
-        "config": {"workload": wl.name, "queries": nq, "l_max": L, "n_heads": H, "head_dim": d,
+        "config": {"workload": {"misa_dagger": "misa_dagger_decode_L128K_H64_h8_kp8192",
+                                "pool": "mean_pool_L128K_B64"}.get(name, wl.name), "queries": nq, "l_max": L, "n_heads": H, "head_dim": d,
                    "top_k": topk, "causal_pairs": pairs, "parallelism": "single GPU",
                    **({"block": wl.block} if wl.block else {}),
                    **({"h": wl.n_active_heads} if name.startswith("misa") else {}),
@@ -344,6 +373,13 @@ def main() -> int:
                    **({"m_blocks": wl.m_blocks} if name == "hisa" else {})},
         "topk_latency_us": ms_per_step * 1e3,
         "ms_per_step_with_kernel_events": ms_per_step_events,
+        "call": {"latency_median_us": call_med_ms * 1e3, "latency_min_us": per_call[0] * 1e3,
+                 "algorithmic_bytes": call_bytes, "algorithmic_flops": call_flops,
+                 "gb_per_s": call_bytes / (ms_per_step * 1e-3) / 1e9,
+                 "tflop_per_s": call_flops / (ms_per_step * 1e-3) / 1e12,
+                 "hbm_frac": call_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                 "pair_scores_per_s": pairs / (ms_per_step * 1e-3),
+                 "head_dots_per_s": call_flops / (2 * d) / (ms_per_step * 1e-3)},
         "cold_cache": flush is not None,
         "kernel_avg_us": per_kernel,
         "roofline": roofline,
