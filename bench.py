@@ -7,7 +7,8 @@ indexer_score_topk call (scoring and exact top-k selection of all 64 queries)
 with inputs resident in HBM.  Prints one JSON line.
 
 Other workloads (--workload): tiny (float32, 16 queries, L = 4096),
-dense_prefill (32768 causal rows of one 32768-key cache), misa / misa_dagger
+dense_prefill (32768 causal rows of one 32768-key cache), misa_prefill (the same
+rows routed to h = 8 of 64 heads over 64-key pooled blocks), misa / misa_dagger
 (h = 8 of 64 heads, B = 64, k' = 8192), hisa (32 heads, L = 1M, B = 128,
 m = 64), pool (mean pooling of the 128K caches).  tiny and hisa touch less
 than the 256 MB last-level cache and are timed cold.
@@ -34,7 +35,7 @@ CSRC = os.path.join(ROOT, "sparse_attention_token_indexer_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 WORKLOADS = {"dense_decode": 2, "tiny": 1, "dense_prefill": 3, "misa": 4, "misa_dagger": 4,
-             "hisa": 5, "pool": 4}
+             "hisa": 5, "pool": 4, "misa_prefill": 3}
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
 
 
@@ -211,6 +212,24 @@ def main() -> int:
         kernel_bytes = pairs * d * eb + io_bytes
         call_bytes, call_flops = kernel_bytes, pairs * H * d * 2
         bound_note = "HBM: every prefix key row is read once"
+    elif name == "misa_prefill":
+        h, B = 8, 64
+        kp = dsa.indexer_mean_pool_keys(k, B)
+        nbytes = dsa.misa_route_score_topk_workspace_size(nq, H, d, wl.n_seq, L, B, h, 0, topk, 1)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+
+        def step():
+            dsa.misa_route_score_topk(q, w, k, q_pos, None, block=B, n_active_heads=h,
+                                      top_k=topk, k_pooled=kp, with_heads=False, out_idx=out_i,
+                                      out_score=out_s, workspace=ws)
+        kind = "prefill_routed"
+        kernel_bytes = None
+        kernel_flops = pairs * h * d * 2
+        blocks = int(((pos_np.astype(np.int64) + B) // B).sum())      # causal pooled blocks
+        call_bytes = nq * H * d * eb + L * d * eb + -(-L // B) * d * 2 + nq * H * 4 + nq * topk * 8
+        call_flops = blocks * H * d * 2 + kernel_flops                  # router + routed pass
+        bound_note = "MFMA: the routed heads' contraction of every causal (query, key) pair"
+        extra["routing"] = {"h": h, "block": B}
     elif name in ("misa", "misa_dagger"):
         kp = dsa.indexer_mean_pool_keys(k, wl.block)
         kprime = wl.k_prime if name == "misa_dagger" else 0
@@ -365,7 +384,9 @@ def main() -> int:
         "dtype": "bf16" if eb == 2 else "f32",
         "data": "synthetic (seeded; planted-key recipe of the workload)",
         "config": {"workload": {"misa_dagger": "misa_dagger_decode_L128K_H64_h8_kp8192",
-                                "pool": "mean_pool_L128K_B64"}.get(name, wl.name), "queries": nq, "l_max": L, "n_heads": H, "head_dim": d,
+                                "pool": "mean_pool_L128K_B64",
+                                "misa_prefill": "misa_prefill_L32K_H64_h8"}.get(name, wl.name),
+                   "queries": nq, "l_max": L, "n_heads": H, "head_dim": d,
                    "top_k": topk, "causal_pairs": pairs, "parallelism": "single GPU",
                    **({"block": wl.block} if wl.block else {}),
                    **({"h": wl.n_active_heads} if name.startswith("misa") else {}),

@@ -16,7 +16,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(os.path.dirname(HERE), "_build")
 LIB = os.path.join(HERE, "libdsa_indexer.so")
-SOURCES = ["api.hip", "k_score_select.hip", "k_prefill.hip", "k_pool.hip", "k_route.hip",
+SOURCES = ["api.hip", "k_score_select.hip", "k_prefill.hip", "k_prefill_routed.hip", "k_pool.hip",
+           "k_route.hip",
            "k_iou.hip"]
 ARCH = "gfx950"
 

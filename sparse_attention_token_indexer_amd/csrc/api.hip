@@ -345,6 +345,125 @@ void fill_common(dsa::SelArgs& a, const void* q, const float* w, const void* k,
 
 }  // namespace
 
+// MISA on the prefill shape (one sequence, many bf16 rows, h <= 8, k' = 0): the
+// router, the head selection, the packed routed scoring and the row select.
+bool use_misa_prefill(int32_t dtype, int64_t nq, int n_seq, int64_t l_max, int h, int k_prime) {
+  return use_prefill(dtype, nq, n_seq, l_max) && k_prime == 0 && h <= dsa::kRoutedMaxHeads;
+}
+
+struct MisaPrefillPlan {
+  size_t part = 0, heads = 0, partial = 0, pooled = 0, scores = 0, rowmeta = 0, total = 0;
+  int splits = 1, bps = 1;
+  int64_t m_max = 0, row_stride = 0;
+};
+
+MisaPrefillPlan plan_misa_prefill(int64_t nq, int n_heads, int head_dim, int n_seq, int64_t l_max,
+                                  int block, bool pooled_given) {
+  MisaPrefillPlan p;
+  Arena A;
+  p.m_max = cdiv(l_max, block);
+  int64_t bps = 64;
+  while (nq * cdiv(p.m_max, bps) > kTargetWorkgroups && bps < p.m_max) bps *= 2;
+  p.bps = (int)bps;
+  p.splits = (int)cdiv(p.m_max, bps);
+  p.part = A.take((size_t)nq * p.splits * n_heads * 4);
+  p.heads = A.take((size_t)nq * dsa::kRoutedMaxHeads * 4);
+  p.partial = A.take((size_t)nq * head_dim * 2);
+  if (!pooled_given) p.pooled = A.take((size_t)n_seq * p.m_max * head_dim * 2);
+  p.row_stride = (l_max + 3) & ~(int64_t)3;
+  p.scores = A.take((size_t)nq * p.row_stride * 4);
+  p.rowmeta = A.take((size_t)nq * 16);
+  p.total = A.off;
+  return p;
+}
+
+int misa_prefill(const void* q, const float* w, const void* k, const void* k_pooled,
+                 const int32_t* q_seq, const int32_t* q_pos, int32_t nq, int32_t n_heads,
+                 int32_t head_dim, int32_t n_seq, int64_t l_max, int32_t block, int32_t h,
+                 int32_t top_k, int32_t* out_idx, float* out_score, int32_t* out_heads,
+                 float* out_importance, void* workspace, size_t workspace_bytes,
+                 hipStream_t stream) {
+  MisaPrefillPlan p = plan_misa_prefill(nq, n_heads, head_dim, n_seq, l_max, block,
+                                        k_pooled != nullptr);
+  int st = check_ws(workspace, workspace_bytes, p.total);
+  if (st) return st;
+  const uint16_t* pooled = reinterpret_cast<const uint16_t*>(k_pooled);
+  if (!pooled) {
+    uint16_t* dst = at<uint16_t>(workspace, p.pooled);
+    st = hip_status(timed_pool(stream, [&] { return dsa::launch_mean_pool(reinterpret_cast<const uint16_t*>(k), n_seq, l_max,
+                                          head_dim, block, dst, stream); }),
+                    "mean-pool kernel", stream);
+    if (st) return st;
+    pooled = dst;
+  }
+  uint16_t* partial = at<uint16_t>(workspace, p.partial);
+  if ((st = run_prepare(workspace, 0, k, q_seq, q_pos, nq, n_seq, head_dim, block, l_max, partial,
+                        stream)))
+    return st;
+  dsa::RouteArgs ra{};
+  ra.q = reinterpret_cast<const uint16_t*>(q);
+  ra.pooled = pooled;
+  ra.partial = partial;
+  ra.q_seq = q_seq;
+  ra.q_pos = q_pos;
+  ra.nq = nq;
+  ra.n_heads = n_heads;
+  ra.head_dim = head_dim;
+  ra.n_seq = n_seq;
+  ra.block = block;
+  ra.splits = p.splits;
+  ra.blocks_per_split = p.bps;
+  ra.l_max = l_max;
+  ra.m_max = p.m_max;
+  ra.part = at<float>(workspace, p.part);
+  if ((st = hip_status(timed(DSA_KERNEL_ROUTE, stream, [&] { return dsa::launch_route(ra, stream); }),
+                       "router kernel", stream))) return st;
+  dsa::RouteHeadsArgs rh{};
+  rh.part = ra.part;
+  rh.w = w;
+  rh.q_seq = q_seq;
+  rh.q_pos = q_pos;
+  rh.nq = nq;
+  rh.n_heads = n_heads;
+  rh.splits = p.splits;
+  rh.h_use = h;
+  rh.heads_stride = dsa::kRoutedMaxHeads;
+  rh.n_seq = n_seq;
+  rh.l_max = l_max;
+  rh.heads = at<int32_t>(workspace, p.heads);
+  rh.out_heads = out_heads;
+  rh.out_importance = out_importance;
+  if ((st = hip_status(timed(DSA_KERNEL_ROUTE_HEADS, stream,
+                             [&] { return dsa::launch_route_heads(rh, stream); }),
+                       "head selection kernel", stream))) return st;
+  dsa::PrefillArgs pa{};
+  pa.q = reinterpret_cast<const uint16_t*>(q);
+  pa.w = w;
+  pa.keys = reinterpret_cast<const uint16_t*>(k);
+  pa.q_seq = q_seq;
+  pa.q_pos = q_pos;
+  pa.nq = nq;
+  pa.n_heads = n_heads;
+  pa.head_dim = head_dim;
+  pa.top_k = top_k;
+  pa.l_max = l_max;
+  pa.row_stride = p.row_stride;
+  pa.scores = at<float>(workspace, p.scores);
+  pa.rowmeta = at<int32_t>(workspace, p.rowmeta);
+  pa.bin_bits = 10;
+  pa.heads = rh.heads;
+  pa.heads_stride = rh.heads_stride;
+  pa.h_use = h;
+  pa.out_idx = out_idx;
+  pa.out_score = out_score;
+  if ((st = hip_status(timed(DSA_KERNEL_PREFILL_ROUTED, stream,
+                             [&] { return dsa::launch_prefill_routed_score(pa, stream); }),
+                       "routed prefill scoring kernel", stream))) return st;
+  return hip_status(timed(DSA_KERNEL_ROWSELECT, stream,
+                          [&] { return dsa::launch_prefill_select(pa, stream); }),
+                    "prefill select kernel", stream);
+}
+
 extern "C" {
 
 const char* dsa_last_error(void) { return g_err.c_str(); }
@@ -429,6 +548,7 @@ int indexer_score_topk(const void* q, const float* w, const void* k, int32_t dty
     pa.row_stride = (l_max + 3) & ~(int64_t)3;
     pa.scores = at<float>(workspace, pp.scores);
     pa.rowmeta = at<int32_t>(workspace, pp.rowmeta);
+    pa.bin_bits = 12;                      // first-level bins of the dense rows
     pa.out_idx = out_idx;
     pa.out_score = out_score;
     st = hip_status(timed(DSA_KERNEL_PREFILL, stream,
@@ -476,6 +596,8 @@ size_t misa_route_score_topk_workspace_size(int32_t nq, int32_t n_heads, int32_t
                                             int32_t top_k, int32_t pooled_given) {
   (void)top_k;
   if (nq <= 0 || l_max <= 0 || block <= 0 || n_active_heads <= 0) return 0;
+  if (use_misa_prefill(DSA_DTYPE_BF16, nq, n_seq, l_max, n_active_heads, k_prime))
+    return plan_misa_prefill(nq, n_heads, head_dim, n_seq, l_max, block, pooled_given != 0).total;
   return plan_misa(nq, n_heads, head_dim, n_seq, l_max, block, n_active_heads, k_prime,
                    pooled_given != 0).total;
 }
@@ -497,6 +619,10 @@ int misa_route_score_topk(const void* q, const float* w, const void* k, const vo
     return fail(DSA_EINVAL, "k_prime must be 0 or in [top_k, %d] (got %d)", kMaxTopK, k_prime);
   if (nq == 0) return DSA_OK;
   if (k_pooled && !aligned(k_pooled, 16)) return fail(DSA_EINVAL, "k_pooled must be 16-byte aligned");
+  if (use_misa_prefill(dtype, nq, n_seq, l_max, n_active_heads, k_prime))
+    return misa_prefill(q, w, k, k_pooled, q_seq, q_pos, nq, n_heads, head_dim, n_seq, l_max, block,
+                        n_active_heads, top_k, out_idx, out_score, out_heads, out_importance,
+                        workspace, workspace_bytes, stream);
   MisaPlan p = plan_misa(nq, n_heads, head_dim, n_seq, l_max, block, n_active_heads, k_prime,
                          k_pooled != nullptr);
   if ((st = check_ws(workspace, workspace_bytes, p.total))) return st;

@@ -103,10 +103,31 @@ struct PrefillArgs {
   int64_t row_stride;          // floats per score row (l_max rounded up to 4)
   float* scores;               // [nq, row_stride] workspace (only u <= pos written)
   int32_t* rowmeta;            // [nq, 4] workspace: threshold bin, count above, count in bin
+  int bin_bits;                // first-level histogram bits (12 dense, 10 routed)
+  const int32_t* heads;        // routed pass: [nq, heads_stride] head ids (first h_use used)
+  int heads_stride, h_use;
   int32_t* out_idx;
   float* out_score;
 };
 hipError_t launch_prefill_score(const PrefillArgs& a, hipStream_t stream);
+// MISA on the prefill shape: rows scored with their h_use <= 8 routed heads,
+// four rows per 32-row MFMA tile; 10-bit per-row histograms.
+constexpr int kRoutedMaxHeads = 8;
+hipError_t launch_prefill_routed_score(const PrefillArgs& a, hipStream_t stream);
+// Top-h heads of every query from the router's per-slice sums (heads written
+// to heads[t * heads_stride + rank], optionally out_heads / out_importance).
+struct RouteHeadsArgs {
+  const float* part;           // [nq, splits, n_heads]
+  const float* w;              // [nq, n_heads]
+  const int32_t* q_seq;
+  const int32_t* q_pos;
+  int nq, n_heads, splits, h_use, heads_stride, n_seq;
+  int64_t l_max;
+  int32_t* heads;              // [nq, heads_stride]
+  int32_t* out_heads;          // [nq, h_use] or null
+  float* out_importance;       // [nq, n_heads] or null
+};
+hipError_t launch_route_heads(const RouteHeadsArgs& a, hipStream_t stream);
 hipError_t launch_prefill_select(const PrefillArgs& a, hipStream_t stream);
 
 hipError_t launch_iou(const int32_t* a, const int32_t* b, int nq, int k, float* out,

@@ -160,12 +160,12 @@ DSA_DEVICE void radix_finish(const Src& src, uint64_t prefix, uint64_t mask, int
   }
 }
 
-// Exact finish of a tied 12-bit bin held in LDS (list[0..nl), all entries share
-// the top kBinBits of their key): emit the `need` best by composite order.  One
-// 10-bit digit histogram narrows the tie to a sub-bin; if that holds at most 64
-// entries they are ranked by brute force inside one wave, otherwise the general
-// radix finish takes over.  hist needs 1024 words, tie 64 pairs of LDS.
-template <int NT>
+// Exact finish of a tied first-level bin held in LDS (list[0..nl), all entries
+// share the top FB bits of their key): emit the `need` best by composite order.
+// One 10-bit digit histogram narrows the tie to a sub-bin; if that holds at
+// most 64 entries they are ranked by brute force inside one wave, otherwise the
+// general radix finish takes over.  hist needs 1024 words, tie 64 pairs of LDS.
+template <int NT, int FB = kBinBits>
 DSA_DEVICE void finish_bin(const uint2* list, uint32_t nl, uint32_t need, int bstar,
                            const Emitter& em, uint32_t* hist, uint32_t* scratch, uint2* tie) {
   __shared__ uint32_t s_tn;
@@ -176,7 +176,7 @@ DSA_DEVICE void finish_bin(const uint2* list, uint32_t nl, uint32_t need, int bs
     return;
   }
   constexpr int D2 = 10;
-  constexpr int SH2 = 32 - kBinBits - D2;          // key bits [19:10]
+  constexpr int SH2 = 32 - FB - D2;                // the 10 key bits below the first level
   for (int i = threadIdx.x; i < (1 << D2); i += NT) hist[i] = 0;
   if (threadIdx.x == 0) s_tn = 0;
   __syncthreads();
@@ -215,8 +215,8 @@ DSA_DEVICE void finish_bin(const uint2* list, uint32_t nl, uint32_t need, int bs
     return;
   }
   PairSource src{list, nl};
-  const uint64_t prefix = ((uint64_t)bstar << (64 - kBinBits)) | ((uint64_t)d2 << (32 + SH2));
-  const uint64_t mask = ((uint64_t)((1u << (kBinBits + D2)) - 1u)) << (32 + SH2);
+  const uint64_t prefix = ((uint64_t)bstar << (64 - FB)) | ((uint64_t)d2 << (32 + SH2));
+  const uint64_t mask = ((uint64_t)((1u << (FB + D2)) - 1u)) << (32 + SH2);
   radix_finish<NT>(src, prefix, mask, 32 + SH2, need2, nd2, em, hist, scratch);
 }
 

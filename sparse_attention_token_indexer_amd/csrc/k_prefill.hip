@@ -40,14 +40,6 @@ constexpr size_t prefill_lds_bytes() {
   return 2 * (size_t)kStageKeys * (D * 2 + 16) + (size_t)ROWS * (kPBins / 2) * 4;
 }
 
-// Order-preserving score key without the -0.0 fold: the scores computed here
-// are sums w*max(0, x) started from +0.0, which can never produce -0.0, so this
-// agrees with score_to_key on every value it sees.
-DSA_DEVICE uint32_t fast_key(float f) {
-  const uint32_t b = __float_as_uint(f);
-  return b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);
-}
-
 template <int HT, int D, int ROWS>
 __global__ __launch_bounds__(64 * ROWS) void k_prefill_score(PrefillArgs a) {
   constexpr int kPT = 64 * ROWS;
@@ -288,7 +280,9 @@ struct RowSource {
   }
 };
 
+template <int FB>   // first-level bins of the rows' histograms (rowmeta)
 __global__ __launch_bounds__(kST) void k_prefill_select(PrefillArgs a) {
+  constexpr int kFBShift = 32 - FB;
   extern __shared__ __align__(16) uint8_t smem[];
   uint2* list = reinterpret_cast<uint2*>(smem);                          // [kSelListCap]
   uint2* tie = list + kSelListCap;                                        // [64]
@@ -349,7 +343,7 @@ __global__ __launch_bounds__(kST) void k_prefill_select(PrefillArgs a) {
         const uint32_t u = 4 * i4 + e;
         const bool ok = i4 < n4 && u < n;
         const uint32_t key = ok ? fast_key(v[j][e]) : 0u;
-        const int b = ok ? (int)(key >> kPBinShift) : -1;
+        const int b = ok ? (int)(key >> kFBShift) : -1;
         em.put_wave(b > bstar, key, (int32_t)u);
         if (fits) list_put_wave(b == bstar, make_uint2(key, u), list, &s_ln, kSelListCap);
       }
@@ -359,12 +353,12 @@ __global__ __launch_bounds__(kST) void k_prefill_select(PrefillArgs a) {
   const uint32_t need = Kt - above;
   if (fits) {
     const uint32_t nl = s_ln < nb ? s_ln : nb;
-    finish_bin<kST>(list, nl, need, bstar, em, hist, scratch, tie);
+    finish_bin<kST, FB>(list, nl, need, bstar, em, hist, scratch, tie);
   } else {
-    const uint64_t prefix = (uint64_t)bstar << (64 - kPBinBits);
-    const uint64_t mask = (uint64_t)(kPBins - 1) << (64 - kPBinBits);
+    const uint64_t prefix = (uint64_t)bstar << (64 - FB);
+    const uint64_t mask = (uint64_t)((1u << FB) - 1u) << (64 - FB);
     RowSource src{sc, n};
-    radix_finish<kST>(src, prefix, mask, 64 - kPBinBits, need, nb, em, hist, scratch);
+    radix_finish<kST>(src, prefix, mask, 64 - FB, need, nb, em, hist, scratch);
   }
 }
 
@@ -393,14 +387,22 @@ hipError_t launch_prefill_score(const PrefillArgs& a, hipStream_t stream) {
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_prefill_select(const PrefillArgs& a, hipStream_t stream) {
-  if (a.nq <= 0) return hipSuccess;
+template <int FB>
+hipError_t launch_select_t(const PrefillArgs& a, hipStream_t stream) {
   const size_t lds = (size_t)kSelListCap * 8 + 64 * 8 + (1024 + 64) * 4;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_prefill_select),
+  auto k = k_prefill_select<FB>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_prefill_select, dim3(a.nq), dim3(kST), lds, stream, a);
+  hipLaunchKernelGGL(k, dim3(a.nq), dim3(kST), lds, stream, a);
   return hipGetLastError();
+}
+
+hipError_t launch_prefill_select(const PrefillArgs& a, hipStream_t stream) {
+  if (a.nq <= 0) return hipSuccess;
+  if (a.bin_bits == 12) return launch_select_t<12>(a, stream);
+  if (a.bin_bits == 10) return launch_select_t<10>(a, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace dsa

@@ -116,4 +116,41 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Head selection from the router's per-slice sums, one wave per query (lane j
+// = head j): I_j = |w_j| * (sum of the slices in slice order), top h by
+// (I desc, j asc) -- the same order and arithmetic as the decode-shaped routed
+// pass, which finishes the selection inside its scoring workgroups.
+__global__ __launch_bounds__(256) void k_route_heads(RouteHeadsArgs a) {
+  const int t = (int)blockIdx.x * 4 + wave_id();
+  const int j = lane_id();
+  if (t >= a.nq) return;
+  const int seq = a.q_seq ? a.q_seq[t] : 0;
+  const int64_t pos = a.q_pos[t];
+  const bool row_ok = seq >= 0 && seq < a.n_seq && pos >= 0 && pos < a.l_max;
+  const bool head_ok = j < a.n_heads;
+  float I = 0.f;
+  if (head_ok) {
+    float tot = 0.f;
+    for (int sp = 0; sp < a.splits; ++sp) tot += a.part[((size_t)t * a.splits + sp) * a.n_heads + j];
+    I = fabsf(a.w[(size_t)t * a.n_heads + j]) * tot;
+    if (a.out_importance) a.out_importance[(size_t)t * a.n_heads + j] = row_ok ? I : 0.f;
+  }
+  int rank = 0;
+  for (int i = 0; i < a.n_heads; ++i) {
+    const float Ii = __shfl(I, i, 64);
+    rank += (Ii > I) || (Ii == I && i < j);
+  }
+  if (head_ok && rank < a.h_use) {
+    a.heads[(size_t)t * a.heads_stride + rank] = row_ok ? j : 0;
+    if (a.out_heads) a.out_heads[(size_t)t * a.h_use + rank] = row_ok ? j : -1;
+  }
+}
+
+hipError_t launch_route_heads(const RouteHeadsArgs& a, hipStream_t stream) {
+  if (a.nq <= 0) return hipSuccess;
+  if (a.n_heads > 64 || a.h_use > a.heads_stride) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_route_heads, dim3((a.nq + 3) / 4), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
 }  // namespace dsa

@@ -146,3 +146,36 @@ def test_dense_prefill_full_sampled_rows(dsa):
         r = O.dense_row(q_t, w_t, K, t, wl.top_k)
         errs += _check(gi[i], gv[i], r, wl.top_k, q_t, w_t, K, f"row {t}")
     assert not errs, "\n".join(errs[:10])
+
+
+def test_misa_prefill_full_sampled_rows(dsa):
+    """MISA on the prefill geometry at full size: the dense prefill workload's
+    32768 rows x 32768 keys, 64 heads, routed to h = 8 over 64-key pooled
+    blocks, k 2048; sampled rows, each checked on its routed heads and then on
+    the selection given the GPU's heads."""
+    wl = datagen.WORKLOADS[3]
+    h, B = 8, 64
+    say("[full] MISA prefill 32768 x 32768, h 8")
+    dev, hin = _device_inputs(wl)
+    res = dsa.misa_route_score_topk(dev["q"], dev["w"], dev["k"], dev["q_pos"], None, block=B,
+                                    n_active_heads=h, top_k=wl.top_k, with_importance=True)
+    rows = [0, 63, 64, 2047, 2048, 9999, 32767]
+    gi = res["idx"][rows].cpu().numpy()
+    gv = res["score"][rows].cpu().numpy()
+    gh = res["heads"][rows].cpu().numpy().astype(np.int64)
+    gI = res["importance"][rows].cpu().numpy().astype(np.float64)
+    K = O.to_f64(datagen.keys(wl, 0, hin["q"], hin["w"]), wl.dtype)
+    errs = []
+    for i, t in enumerate(rows):
+        q_t, w_t = O.to_f64(hin["q"][t], wl.dtype), hin["w"][t].astype(np.float64)
+        pooled = O.misa_pooled_for_query(K, B, t)
+        I = O.misa_importance(q_t, w_t, pooled)
+        Fi = np.abs(w_t) * (np.abs(q_t) @ np.abs(pooled).T).sum(axis=1)
+        bad = np.abs(gI[i] - I) > 2e-3 * I + 2.0 ** -17 * Fi
+        if bad.any():
+            errs.append(f"importance row {t}: {np.nonzero(bad)[0][:4]}")
+        errs += check_selection(gh[i], None, np.arange(wl.n_heads), I, I, h, Fi,
+                                what=f"heads row {t}")
+        r = O.misa_row(q_t, w_t, K, t, B, h, wl.top_k, heads=gh[i])
+        errs += _check(gi[i], gv[i], r, wl.top_k, q_t, w_t, K, f"misa row {t}", gh[i])
+    assert not errs, "\n".join(errs[:10])

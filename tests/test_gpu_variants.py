@@ -40,7 +40,7 @@ def _check(gi, gv, cand, s, A, k, q_t, w_t, K, what, heads=None):
     return check_selection(gi, gv, cand, s, A, k, F, what=what)
 
 
-def _misa_case(dsa, wl, h, k, kprime, seed=0, pos=None, pooled=True):
+def _misa_case(dsa, wl, h, k, kprime, seed=0, pos=None, pooled=True, rows=None):
     inp = datagen.make(wl, seed)
     if pos is not None:
         inp["q_pos"] = np.asarray(pos, dtype=np.int32)
@@ -54,7 +54,7 @@ def _misa_case(dsa, wl, h, k, kprime, seed=0, pos=None, pooled=True):
     torch.cuda.synchronize()
     out = {key: v.cpu().numpy() for key, v in res.items() if v is not None}
     errs = []
-    for t in range(wl.nq):
+    for t in (range(wl.nq) if rows is None else rows):
         q_t, w_t, K, p = _rows(inp, wl, t)
         pooled_ref = O.misa_pooled_for_query(K, wl.block, p)
         I = O.misa_importance(q_t, w_t, pooled_ref)
@@ -103,6 +103,54 @@ def test_misa_partial_blocks_and_internal_pooling(dsa):
         _misa_case(dsa, wl, h=3, k=50, kprime=0, pos=pos, pooled=pooled)
 
 
+def _misa_prefill_wl(nq, L, **kw):
+    # MISA's values on the prefill layout: row t at position t of one sequence
+    return datagen.small(4, nq=nq, n_seq=1, l_max=L, layout="prefill", plant="points",
+                         n_plant=max(8, nq // 8), **kw)
+
+
+def test_misa_prefill_rows(dsa):
+    """MISA on the prefill shape (many rows of one sequence, h <= 8): the router,
+    the head selection, the packed routed scoring and the row select.  512 rows
+    with a 64-key block: rows end inside a block (partial last blocks), rows
+    0..63 are shorter than k."""
+    wl = _misa_prefill_wl(512, 512)
+    _misa_case(dsa, wl, h=8, k=64, kprime=0)
+
+
+def test_misa_prefill_larger_and_fewer_heads(dsa):
+    wl = _misa_prefill_wl(2048, 2048)
+    rows = list(range(0, 2048, 41)) + [2047]
+    _misa_case(dsa, wl, h=8, k=300, kprime=0, seed=1, rows=rows)
+    _misa_case(dsa, wl, h=3, k=300, kprime=0, seed=2, rows=rows, pooled=False)
+    _misa_case(dsa, wl, h=1, k=100, kprime=0, seed=3, rows=rows)
+
+
+def test_misa_prefill_heads_and_dims(dsa):
+    for H, d, h in ((32, 128, 8), (64, 64, 5), (16, 128, 7)):
+        wl = _misa_prefill_wl(256, 700, n_heads=H, head_dim=d)
+        _misa_case(dsa, wl, h=h, k=100, kprime=0, seed=4)
+
+
+def test_misa_prefill_arbitrary_positions_and_invalid_rows(dsa):
+    """Positions in any order and rows that are not valid for a one-sequence call."""
+    wl = _misa_prefill_wl(100, 3000)
+    rng = np.random.default_rng(5)
+    pos = rng.integers(0, 3000, size=100)
+    pos[5], pos[6], pos[7], pos[8] = -1, 3000, 2999, 0
+    inp = datagen.make(wl, 6)
+    inp["q_pos"] = pos.astype(np.int32)
+    dev = upload(inp, wl)
+    res = dsa.misa_route_score_topk(dev["q"], dev["w"], dev["k"], dev["q_pos"], None, block=64,
+                                    n_active_heads=8, top_k=256)
+    gi = res["idx"].cpu().numpy()
+    heads = res["heads"].cpu().numpy()
+    for t in (5, 6):
+        assert np.all(gi[t] == -1) and np.all(heads[t] == -1), f"invalid row {t}"
+    valid = [t for t in range(100) if t not in (5, 6)]
+    _misa_case(dsa, wl, h=8, k=256, kprime=0, seed=6, pos=pos, rows=valid)
+
+
 def test_misa_all_heads_equals_dense(dsa):
     """h = H_I routes every head: the selection must be the dense indexer's."""
     wl = datagen.small(4, nq=4, n_seq=4, l_max=8192)
@@ -147,7 +195,7 @@ def _hisa_case(dsa, wl, m, k, seed=0, pos=None, pooled=True):
     torch.cuda.synchronize()
     out = {key: v.cpu().numpy() for key, v in res.items()}
     errs = []
-    for t in range(wl.nq):
+    for t in (range(wl.nq) if rows is None else rows):
         q_t, w_t, K, p = _rows(inp, wl, t)
         pooled_ref = O.misa_pooled_for_query(K, wl.block, p)
         bs, bA = O.hisa_block_scores(q_t, w_t, pooled_ref)
