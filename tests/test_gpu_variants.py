@@ -183,7 +183,7 @@ def test_misa_dagger_full_candidate_set_equals_dense(dsa):
     assert not errs, "\n".join(errs[:8])
 
 
-def _hisa_case(dsa, wl, m, k, seed=0, pos=None, pooled=True):
+def _hisa_case(dsa, wl, m, k, seed=0, pos=None, pooled=True, rows=None):
     inp = datagen.make(wl, seed)
     if pos is not None:
         inp["q_pos"] = np.asarray(pos, dtype=np.int32)
