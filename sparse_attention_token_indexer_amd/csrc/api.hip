@@ -352,7 +352,7 @@ bool use_misa_prefill(int32_t dtype, int64_t nq, int n_seq, int64_t l_max, int h
 }
 
 struct MisaPrefillPlan {
-  size_t part = 0, heads = 0, partial = 0, pooled = 0, scores = 0, rowmeta = 0, total = 0;
+  size_t part = 0, heads = 0, prefix = 0, pooled = 0, scores = 0, rowmeta = 0, total = 0;
   int splits = 1, bps = 1;
   int64_t m_max = 0, row_stride = 0;
 };
@@ -362,13 +362,11 @@ MisaPrefillPlan plan_misa_prefill(int64_t nq, int n_heads, int head_dim, int n_s
   MisaPrefillPlan p;
   Arena A;
   p.m_max = cdiv(l_max, block);
-  int64_t bps = 64;
-  while (nq * cdiv(p.m_max, bps) > kTargetWorkgroups && bps < p.m_max) bps *= 2;
-  p.bps = (int)bps;
-  p.splits = (int)cdiv(p.m_max, bps);
-  p.part = A.take((size_t)nq * p.splits * n_heads * 4);
+  p.bps = (int)p.m_max;                         // one slice: a wave per query
+  p.splits = 1;
+  p.part = A.take((size_t)nq * n_heads * 4);
   p.heads = A.take((size_t)nq * dsa::kRoutedMaxHeads * 4);
-  p.partial = A.take((size_t)nq * head_dim * 2);
+  p.prefix = A.take((size_t)l_max * head_dim * 2);
   if (!pooled_given) p.pooled = A.take((size_t)n_seq * p.m_max * head_dim * 2);
   p.row_stride = (l_max + 3) & ~(int64_t)3;
   p.scores = A.take((size_t)nq * p.row_stride * 4);
@@ -396,14 +394,18 @@ int misa_prefill(const void* q, const float* w, const void* k, const void* k_poo
     if (st) return st;
     pooled = dst;
   }
-  uint16_t* partial = at<uint16_t>(workspace, p.partial);
-  if ((st = run_prepare(workspace, 0, k, q_seq, q_pos, nq, n_seq, head_dim, block, l_max, partial,
-                        stream)))
+  // pooled keys of prefixes that end inside a block, by position
+  uint16_t* prefix = at<uint16_t>(workspace, p.prefix);
+  if ((st = hip_status(timed(DSA_KERNEL_PREPARE, stream, [&] {
+                         return dsa::launch_pool_prefix(reinterpret_cast<const uint16_t*>(k), l_max,
+                                                        head_dim, block, prefix, stream); }),
+                       "prefix-pool kernel", stream)))
     return st;
   dsa::RouteArgs ra{};
   ra.q = reinterpret_cast<const uint16_t*>(q);
   ra.pooled = pooled;
-  ra.partial = partial;
+  ra.partial = prefix;
+  ra.partial_by_pos = 1;
   ra.q_seq = q_seq;
   ra.q_pos = q_pos;
   ra.nq = nq;

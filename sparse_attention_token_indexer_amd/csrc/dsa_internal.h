@@ -82,13 +82,19 @@ hipError_t launch_mean_pool(const uint16_t* k, int n_seq, int64_t l_max, int hea
 struct RouteArgs {
   const uint16_t* q;           // [nq, n_heads, D]
   const uint16_t* pooled;      // [n_seq, m_max, D]
-  const uint16_t* partial;     // [nq, D] or null
+  const uint16_t* partial;     // [nq, D] (by query) or [l_max, D] (by position), or null
+  int partial_by_pos;          // partial holds the in-block prefix mean of every position
   const int32_t* q_seq;
   const int32_t* q_pos;
   int nq, n_heads, head_dim, n_seq, block, splits, blocks_per_split;
   int64_t l_max, m_max;
   float* part;                 // [nq, splits, n_heads] workspace
 };
+// out[p] = mean of the keys from the start of p's block to p, sequence 0, every
+// position p < l_max (the pooled key of a prefix that ends inside a block),
+// accumulated in float64 and rounded once to bf16 like the block means.
+hipError_t launch_pool_prefix(const uint16_t* k, int64_t l_max, int head_dim, int block,
+                              uint16_t* out, hipStream_t stream);
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream);
 
 // Prefill-shaped dense pass: all queries on sequence 0, grouped by 8 rows.

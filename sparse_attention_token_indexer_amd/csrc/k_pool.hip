@@ -99,6 +99,22 @@ __global__ __launch_bounds__(256) void k_prepare(PrepArgs a, int n_zero_blocks) 
   }
 }
 
+// In-block prefix means of every position: one workgroup per block, one
+// thread per dimension, a running float64 sum over the block's rows.
+template <int D>
+__global__ __launch_bounds__(D) void k_pool_prefix(const uint16_t* __restrict__ k, int64_t l_max,
+                                                   int block, uint16_t* __restrict__ out) {
+  const int64_t r0 = (int64_t)blockIdx.x * block;
+  const int64_t r1 = (r0 + block) < l_max ? (r0 + block) : l_max;
+  const int e = threadIdx.x;
+  double acc = 0.0;
+#pragma unroll 8
+  for (int64_t r = r0; r < r1; ++r) {
+    acc += bf16_to_f64(k[(size_t)r * D + e]);
+    out[(size_t)r * D + e] = f64_to_bf16(acc / (double)(r - r0 + 1));
+  }
+}
+
 }  // namespace
 
 hipError_t launch_mean_pool(const uint16_t* k, int n_seq, int64_t l_max, int head_dim, int block,
@@ -124,6 +140,16 @@ hipError_t launch_prepare(const PrepArgs& a, hipStream_t stream) {
   const int np = a.partial ? a.nq : 0;
   if (nz + np == 0) return hipSuccess;
   hipLaunchKernelGGL(k_prepare, dim3(nz + np), dim3(256), 0, stream, a, nz);
+  return hipGetLastError();
+}
+
+hipError_t launch_pool_prefix(const uint16_t* k, int64_t l_max, int head_dim, int block,
+                              uint16_t* out, hipStream_t stream) {
+  if (l_max <= 0) return hipSuccess;
+  const int64_t nb = (l_max + block - 1) / block;
+  if (head_dim == 128) hipLaunchKernelGGL(k_pool_prefix<128>, dim3(nb), dim3(128), 0, stream, k, l_max, block, out);
+  else if (head_dim == 64) hipLaunchKernelGGL(k_pool_prefix<64>, dim3(nb), dim3(64), 0, stream, k, l_max, block, out);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

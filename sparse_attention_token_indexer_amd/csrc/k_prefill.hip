@@ -316,10 +316,13 @@ __global__ __launch_bounds__(kST) void k_prefill_select(PrefillArgs a) {
   const int32_t* meta = a.rowmeta + (size_t)t * 4;
   const int bstar = meta[0];
   const uint32_t above = (uint32_t)meta[1], nb = (uint32_t)meta[2];
+  const bool fits = nb <= kSelListCap;
   if (threadIdx.x == 0) { s_out = 0; s_ln = 0; }
+  if (!fits)                                    // second-digit histogram of the bin
+    for (int i = threadIdx.x; i < 1024; i += kST) hist[i] = 0;
   __syncthreads();
   const Emitter em{out_i, out_s, &s_out, Kt};
-  const bool fits = nb <= kSelListCap;
+  constexpr int kSub = kFBShift - 10;          // the 10 key bits below the first level
   // one pass over the row (16-byte loads): emit every score above the bin,
   // collect the bin itself.  The loads are unconditional (clamped to the
   // row's last piece, masked afterwards) so that all of them are in flight
@@ -346,6 +349,7 @@ __global__ __launch_bounds__(kST) void k_prefill_select(PrefillArgs a) {
         const int b = ok ? (int)(key >> kFBShift) : -1;
         em.put_wave(b > bstar, key, (int32_t)u);
         if (fits) list_put_wave(b == bstar, make_uint2(key, u), list, &s_ln, kSelListCap);
+        else if (b == bstar) atomicAdd(&hist[(key >> kSub) & 1023u], 1u);
       }
     }
   }
@@ -354,11 +358,51 @@ __global__ __launch_bounds__(kST) void k_prefill_select(PrefillArgs a) {
   if (fits) {
     const uint32_t nl = s_ln < nb ? s_ln : nb;
     finish_bin<kST, FB>(list, nl, need, bstar, em, hist, scratch, tie);
+    return;
+  }
+  // The bin overflowed the list: its second-digit histogram (counted in the
+  // first pass) gives the sub-bin d2 of the k-th entry; one more pass over the
+  // row emits the bin's entries above d2 and collects d2 itself.
+  uint32_t above2;
+  const int d2 = block_find_threshold<kST>(hist, 1024, need, scratch, &above2);
+  const uint32_t nd2 = hist[d2];
+  const uint32_t need2 = need - above2;
+  if (threadIdx.x == 0) s_ln = 0;
+  __syncthreads();
+  const bool fits2 = nd2 <= kSelListCap;
+  for (uint32_t base = 0; base < n4; base += kST * U) {
+    f32x4 v[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const uint32_t i4 = base + threadIdx.x + j * kST;
+      v[j] = *reinterpret_cast<const f32x4*>(sc + 4 * (size_t)(i4 < n4 ? i4 : n4 - 1));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const uint32_t i4 = base + threadIdx.x + j * kST;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t u = 4 * i4 + e;
+        const bool ok = i4 < n4 && u < n;
+        const uint32_t key = ok ? fast_key(v[j][e]) : 0u;
+        const bool in_bin = ok && (int)(key >> kFBShift) == bstar;
+        const int sub = (int)((key >> kSub) & 1023u);
+        em.put_wave(in_bin && sub > d2, key, (int32_t)u);
+        if (fits2) list_put_wave(in_bin && sub == d2, make_uint2(key, u), list, &s_ln, kSelListCap);
+      }
+    }
+  }
+  __syncthreads();
+  const uint64_t prefix = ((uint64_t)bstar << (64 - FB)) | ((uint64_t)d2 << (64 - FB - 10));
+  const uint64_t mask = (uint64_t)((1u << (FB + 10)) - 1u) << (64 - FB - 10);
+  if (fits2) {
+    const uint32_t nl = s_ln < nd2 ? s_ln : nd2;
+    PairSource src{list, nl};
+    radix_finish<kST>(src, prefix, mask, 64 - FB - 10, need2, nl, em, hist, scratch);
   } else {
-    const uint64_t prefix = (uint64_t)bstar << (64 - FB);
-    const uint64_t mask = (uint64_t)((1u << FB) - 1u) << (64 - FB);
     RowSource src{sc, n};
-    radix_finish<kST>(src, prefix, mask, 64 - FB, need, nb, em, hist, scratch);
+    radix_finish<kST>(src, prefix, mask, 64 - FB - 10, need2, nd2, em, hist, scratch);
   }
 }
 

@@ -100,9 +100,104 @@ __global__ __launch_bounds__(kRT) void k_route(RouteArgs a) {
   }
 }
 
+// Router for many queries with one slice each (prefill shape): one wave per
+// query over all of its blocks, the next tile's pooled rows loaded while the
+// current one is multiplied; the per-head sums over the 32 block columns are
+// reduced through LDS (rows padded to 33 words: conflict-free both ways).
+// The partial last block's pooled key comes from a.partial by position
+// (prefix means of every position, a.partial_by_pos) or by query.
+template <int HT, int D>
+__global__ __launch_bounds__(256) void k_route_rows(RouteArgs a) {
+  constexpr int S = D / 16;
+  __shared__ float s_red[4][64 * 33];
+  const int wv = wave_id(), lane = lane_id(), h = lane >> 5, n = lane & 31;
+  const int t = (int)blockIdx.x * 4 + wv;
+  if (t >= a.nq) return;
+  const int seq = a.q_seq ? a.q_seq[t] : 0;
+  const int64_t pos = a.q_pos[t];
+  const bool ok = seq >= 0 && seq < a.n_seq && pos >= 0 && pos < a.l_max;
+  const int64_t M = ok ? (pos + a.block) / a.block : 0;
+  const bool partial_last = a.partial && ok && ((pos + 1) % a.block) != 0;
+  const uint16_t* partial_row =
+      partial_last ? a.partial + (size_t)(a.partial_by_pos ? pos : t) * D : nullptr;
+
+  float hsum[HT][16];
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) hsum[ht][r] = 0.f;
+  const int n_tiles = (int)((M + 31) / 32);
+  if (n_tiles > 0) {
+    bf16x8 qa[HT][S];
+    const uint16_t* q_t = a.q + (size_t)t * a.n_heads * D;
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      const int row = ht * 32 + n;
+#pragma unroll
+      for (int s = 0; s < S; ++s)
+        qa[ht][s] = row < a.n_heads ? load_bf16x8(q_t + (size_t)row * D + 8 * h + 16 * s)
+                                    : zero_bf16x8();
+    }
+    auto load = [&](bf16x8 (&kb)[S], int tile) {
+      const int64_t b = (int64_t)tile * 32 + n;
+      const int64_t bb = b < M ? b : 0;
+      const uint16_t* rowp = (partial_last && bb == M - 1)
+                                 ? partial_row
+                                 : a.pooled + ((size_t)seq * (size_t)a.m_max + (size_t)bb) * D;
+#pragma unroll
+      for (int s = 0; s < S; ++s) kb[s] = load_bf16x8(rowp + 8 * h + 16 * s);
+    };
+    bf16x8 ka[S], kn[S];
+    load(ka, 0);
+    for (int tile = 0; tile < n_tiles; ++tile) {
+      if (tile + 1 < n_tiles) load(kn, tile + 1);
+      const bool valid = (int64_t)tile * 32 + n < M;
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) {
+        f32x16 acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+        for (int s = 0; s < S; ++s)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ht][s], ka[s], acc, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) hsum[ht][r] += valid ? relu(acc[r]) : 0.f;
+      }
+#pragma unroll
+      for (int s = 0; s < S; ++s) ka[s] = kn[s];
+    }
+  }
+  // per head: the sum over the 32 block columns (lane n holds column n)
+  float* red = s_red[wv];
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[(ht * 32 + 8 * (r >> 2) + 4 * h + (r & 3)) * 33 + n] = hsum[ht][r];
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS writes are done
+  __builtin_amdgcn_wave_barrier();
+  if (lane < a.n_heads) {
+    float p = 0.f;
+    for (int c = 0; c < 32; ++c) p += red[lane * 33 + c];
+    a.part[(size_t)t * a.n_heads + lane] = p;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
+  if (a.splits == 1) {                        // one wave per query
+    const dim3 g((a.nq + 3) / 4);
+    if (a.head_dim == 128) {
+      if (a.n_heads <= 32) hipLaunchKernelGGL((k_route_rows<1, 128>), g, dim3(256), 0, stream, a);
+      else hipLaunchKernelGGL((k_route_rows<2, 128>), g, dim3(256), 0, stream, a);
+    } else if (a.head_dim == 64) {
+      if (a.n_heads <= 32) hipLaunchKernelGGL((k_route_rows<1, 64>), g, dim3(256), 0, stream, a);
+      else hipLaunchKernelGGL((k_route_rows<2, 64>), g, dim3(256), 0, stream, a);
+    } else {
+      return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   dim3 grid(a.splits, a.nq);
   if (a.head_dim == 128) {
     if (a.n_heads <= 32) hipLaunchKernelGGL((k_route<1, 128>), grid, dim3(kRT), 0, stream, a);
