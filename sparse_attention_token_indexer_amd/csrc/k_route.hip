@@ -182,9 +182,167 @@ __global__ __launch_bounds__(256) void k_route_rows(RouteArgs a) {
   }
 }
 
+// Router for many queries on ONE sequence (prefill shape): the rows share the
+// pooled keys, so 8 rows per workgroup (one wave each, heads x 32 blocks per
+// MFMA) read 128-block stages from LDS (double-buffered, rows padded to
+// 2*D + 16 bytes, as in the prefill scorers).  Each row sums max(0, q_j . kbar_b)
+// over its full blocks b < (pos + 1) / B; the partial last block (prefix mean
+// of the row's position, from a.partial by position) is one extra tile with a
+// single valid column.  Per-head sums over the 32 block columns go through a
+// padded LDS transpose; one slice per query (part[t][j]).
+constexpr int kPRStage = 128;
+constexpr int kPRRows = 8;
+
+template <int D>
+constexpr size_t prefill_route_lds() {
+  return 2 * (size_t)kPRStage * (2 * D + 16) + (size_t)kPRRows * 64 * 33 * 4;
+}
+
+template <int HT, int D>
+__global__ __launch_bounds__(64 * kPRRows) void k_route_prefill(RouteArgs a) {
+  constexpr int kT = 64 * kPRRows;
+  constexpr int S = D / 16, RB = 2 * D, NC = RB / 16, LB = RB + 16;
+  constexpr int STAGE = kPRStage * LB, PIECES = kPRStage * NC;
+  constexpr int LOADS = PIECES / kT;
+  static_assert(PIECES % kT == 0, "every thread stores whole pieces");
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint8_t* ktile = smem;                                        // [2][STAGE]
+  float* red_all = reinterpret_cast<float*>(smem + 2 * STAGE);  // [rows][64 * 33]
+  __shared__ int s_maxfull;
+  const int wv = wave_id(), lane = lane_id(), h = lane >> 5, m = lane & 31;
+  const int t = (int)blockIdx.x * kPRRows + wv;
+  int64_t pos = -1;
+  if (t < a.nq) {
+    const int seq = a.q_seq ? a.q_seq[t] : 0;
+    const int64_t p = a.q_pos[t];
+    if (seq == 0 && p >= 0 && p < a.l_max) pos = p;
+  }
+  const int nfull = pos >= 0 ? (int)((pos + 1) / a.block) : 0;   // full blocks of the row
+  if (threadIdx.x == 0) s_maxfull = 0;
+  __syncthreads();
+  if (lane == 0) atomicMax(&s_maxfull, nfull);
+  __syncthreads();
+  const int maxfull = s_maxfull;
+
+  bf16x8 qa[HT][S];
+  {
+    const uint16_t* q_t = a.q + (size_t)(pos >= 0 ? t : 0) * a.n_heads * D;
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      const int row = ht * 32 + m;
+      const bool ok = pos >= 0 && row < a.n_heads;
+#pragma unroll
+      for (int s = 0; s < S; ++s)
+        qa[ht][s] = ok ? load_bf16x8(q_t + (size_t)(ok ? row : 0) * D + 8 * h + 16 * s) : zero_bf16x8();
+    }
+  }
+  float hsum[HT][16];
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) hsum[ht][r] = 0.f;
+  auto tile_sum = [&](const bf16x8 (&b)[S], bool valid) {
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      f32x16 acc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+      for (int s = 0; s < S; ++s)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ht][s], b[s], acc, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) hsum[ht][r] += valid ? relu(acc[r]) : 0.f;
+    }
+  };
+
+  const int n_stages = (maxfull + kPRStage - 1) / kPRStage;
+  if (n_stages > 0) {
+    const uint8_t* pbase = reinterpret_cast<const uint8_t*>(a.pooled);
+    const int last = maxfull - 1;
+    u32x4 pre[LOADS];
+    auto fetch = [&](int st) {
+#pragma unroll
+      for (int j = 0; j < LOADS; ++j) {
+        const int p = threadIdx.x + j * kT;
+        const int row = min(st * kPRStage + p / NC, last);     // inside the pooled keys
+        pre[j] = *reinterpret_cast<const u32x4*>(pbase + (size_t)row * RB + (p % NC) * 16);
+      }
+    };
+    auto stash = [&](int buf) {
+#pragma unroll
+      for (int j = 0; j < LOADS; ++j) {
+        const int p = threadIdx.x + j * kT;
+        *reinterpret_cast<u32x4*>(ktile + buf * STAGE + (p / NC) * LB + (p % NC) * 16) = pre[j];
+      }
+    };
+    const uint32_t boff = (uint32_t)(m * LB + h * 16);
+    fetch(0);
+    stash(0);
+    __syncthreads();
+    for (int st = 0; st < n_stages; ++st) {
+      const bool more = st + 1 < n_stages;
+      if (more) fetch(st + 1);
+      const uint8_t* tile = ktile + (st & 1) * STAGE;
+#pragma unroll
+      for (int sub = 0; sub < kPRStage / 32; ++sub) {
+        const int b0 = st * kPRStage + sub * 32;
+        if (b0 < nfull) {                       // wave-uniform
+          bf16x8 b[S];
+#pragma unroll
+          for (int s = 0; s < S; ++s)
+            b[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(tile + boff + sub * 32 * LB + s * 32));
+          tile_sum(b, b0 + m < nfull);
+        }
+      }
+      if (more) stash((st + 1) & 1);
+      __syncthreads();
+    }
+  }
+  // the partial last block: one tile whose column 0 is the prefix mean of pos
+  if (pos >= 0 && ((pos + 1) % a.block) != 0) {
+    bf16x8 b[S];
+    const uint16_t* rowp = a.partial + (size_t)pos * D;
+#pragma unroll
+    for (int s = 0; s < S; ++s) b[s] = m == 0 ? load_bf16x8(rowp + 8 * h + 16 * s) : zero_bf16x8();
+    tile_sum(b, m == 0);
+  }
+  // per head: the sum over the 32 block columns (lane m holds column m)
+  float* red = red_all + wv * (64 * 33);
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[(ht * 32 + 8 * (r >> 2) + 4 * h + (r & 3)) * 33 + m] = hsum[ht][r];
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS writes are done
+  __builtin_amdgcn_wave_barrier();
+  if (t < a.nq && lane < a.n_heads) {
+    float p = 0.f;
+    for (int c = 0; c < 32; ++c) p += red[lane * 33 + c];
+    a.part[(size_t)t * a.n_heads + lane] = p;
+  }
+}
+
 }  // namespace
 
+template <int HT, int D>
+hipError_t launch_route_prefill_t(const RouteArgs& a, hipStream_t stream) {
+  constexpr size_t lds = prefill_route_lds<D>();
+  static_assert(lds <= 160 * 1024, "LDS");
+  auto k = k_route_prefill<HT, D>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k, dim3((a.nq + kPRRows - 1) / kPRRows), dim3(64 * kPRRows), lds, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
+  if (a.splits == 1 && a.n_seq == 1 && a.partial_by_pos) {   // rows of one sequence
+    if (a.head_dim == 128) return a.n_heads <= 32 ? launch_route_prefill_t<1, 128>(a, stream)
+                                                  : launch_route_prefill_t<2, 128>(a, stream);
+    if (a.head_dim == 64) return a.n_heads <= 32 ? launch_route_prefill_t<1, 64>(a, stream)
+                                                 : launch_route_prefill_t<2, 64>(a, stream);
+    return hipErrorInvalidValue;
+  }
   if (a.splits == 1) {                        // one wave per query
     const dim3 g((a.nq + 3) / 4);
     if (a.head_dim == 128) {
