@@ -68,6 +68,16 @@ DSA_DEVICE float fmac_rowbcast(float p, float W, float x) {
 // sum over head tiles ht and accumulator registers r of w(ht, r) * max(0, acc),
 // where W[ht] holds, in lane 16*g + r, the weight of the head that register r
 // holds in lanes of row group g (see the MFMA layouts in dsa_scorers.h).
+// W[16*(lane/16) + R] * x (the first term of a row-broadcast sum).
+template <int R>
+DSA_DEVICE float fmul_rowbcast(float W, float x) {
+  float p;
+  asm("v_mul_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+      : "=v"(p)
+      : "v"(W), "v"(x), "n"(R));
+  return p;
+}
+
 template <int HT, int... R>
 DSA_DEVICE float weighted_relu_sum(const f32x16 (&acc)[HT], const float (&W)[HT],
                                    std::integer_sequence<int, R...>) {

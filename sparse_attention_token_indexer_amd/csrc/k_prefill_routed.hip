@@ -10,7 +10,8 @@
 // key) shrink eightfold against the dense prefill kernel.  The accumulator
 // register r of a lane holds MFMA row 8*(r/4) + 4*(lane/32) + r%4, i.e. row
 // slot r/4 of the wave, so registers 4g .. 4g+3 sum into row g's partial, and
-// one lane-half swap per two rows gives 64 (row, key) scores per register.
+// one lane-half swap of two sub-tiles' partials gives row g's scores of 64
+// consecutive keys in one register.
 // Per-row histograms are 10-bit (u16 pairs, 2 KiB per row) so that 32 rows'
 // fit in LDS beside the two stages.
 #include "dsa_internal.h"
@@ -36,10 +37,16 @@ constexpr size_t routed_lds_bytes() {
 
 // per-row partial sums of one sub-tile: p[g] = sum over registers 4g..4g+3 of
 // w * max(0, acc) (weights by row broadcast, see weighted_relu_sum)
+template <int R>
+DSA_DEVICE void row_term(f32x4& p, float W, float x) {
+  if constexpr ((R & 3) == 0) p[R >> 2] = fmul_rowbcast<R>(W, x);   // first term of row R/4
+  else p[R >> 2] = fmac_rowbcast<R>(p[R >> 2], W, x);
+}
+
 template <int... R>
 DSA_DEVICE f32x4 row_partials(const f32x16& acc, float W, std::integer_sequence<int, R...>) {
-  f32x4 p = {0.f, 0.f, 0.f, 0.f};
-  ((p[R >> 2] = fmac_rowbcast<R>(p[R >> 2], W, relu(acc[R]))), ...);
+  f32x4 p;
+  (row_term<R>(p, W, relu(acc[R])), ...);
   return p;
 }
 
@@ -145,37 +152,36 @@ __global__ __launch_bounds__(kThreads) void k_prefill_routed_score(PrefillArgs a
     for (int s = 0; s < S; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], b[s], acc, 0, 0, 0);
   };
 
-  // finish of one sub-tile: lanes 0..31 take rows 0 and 2 of the wave, lanes
-  // 32..63 rows 1 and 3, each for key key0 + lane % 32
-  const int ga = lane >> 5, gb = 2 + (lane >> 5);
-  const int pa = pos_of(ga), pb = pos_of(gb);
+  // finish of two sub-tiles A (keys key0..key0+31) and B (key0+32..key0+63):
+  // for each row g of the wave, one lane-half swap of its partials puts A's
+  // key l in lane l and B's key l-32 in lane l (l >= 32), so one register
+  // holds row g's scores of 64 consecutive keys and its score row and
+  // histogram are addressed from a wave-uniform base
   const size_t rs = (size_t)a.row_stride;
-  float* srow_a = a.scores + (size_t)(t0 + ga < a.nq ? t0 + ga : 0) * rs;
-  float* srow_b = a.scores + (size_t)(t0 + gb < a.nq ? t0 + gb : 0) * rs;
-  uint32_t* hrow_a = hist + (wv * kPer + ga) * (kRBins / 2);
-  uint32_t* hrow_b = hist + (wv * kPer + gb) * (kRBins / 2);
-  auto put = [&](float* srow, uint32_t* hrow, int u, float sc) {
-    srow[u] = sc;
-    const uint32_t bin = fast_key(sc) >> kRBinShift;
-    atomicAdd(hrow + (bin >> 1), 1u << ((bin & 1u) << 4));
-  };
-  auto finish = [&](int key0, const f32x4& p) {
-    const auto s01 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0]), __float_as_uint(p[1]),
-                                                      false, false);
-    const auto s23 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[2]), __float_as_uint(p[3]),
-                                                      false, false);
-    const float sa = __uint_as_float(s01[0]) + __uint_as_float(s01[1]);
-    const float sb = __uint_as_float(s23[0]) + __uint_as_float(s23[1]);
-    const int u = key0 + (lane & 31);
-    if (u <= pa) put(srow_a, hrow_a, u, sa);
-    if (u <= pb) put(srow_b, hrow_b, u, sb);
+  auto finish_pair = [&](int key0, const f32x4& pa, const f32x4& pb) {
+    const int u = key0 + lane;
+#pragma unroll
+    for (int g = 0; g < kPer; ++g) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(pa[g]), __float_as_uint(pb[g]),
+                                                       false, false);
+      const float sc = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      const int p = pos[g];                     // wave-uniform
+      if (key0 > p) continue;
+      float* srow = a.scores + (size_t)(t0 + g) * rs;
+      uint32_t* hrow = hist + (wv * kPer + g) * (kRBins / 2);
+      if (key0 + 63 <= p || u <= p) {
+        srow[u] = sc;
+        const uint32_t bin = fast_key(sc) >> kRBinShift;
+        atomicAdd(hrow + (bin >> 1), 1u << ((bin & 1u) << 4));
+      }
+    }
   };
   auto epi = [&](const f32x16& acc) {
     return row_partials(acc, W, std::make_integer_sequence<int, 16>{});
   };
 
   // software pipeline over 32-key sub-tiles, stage barrier in sub-tile 2 (see
-  // the dense prefill kernel)
+  // the dense prefill kernel); sub-tiles are finished in pairs
 #pragma unroll
   for (int j = 0; j < LOADS; ++j) fetch_piece(j, 0);
 #pragma unroll
@@ -186,18 +192,19 @@ __global__ __launch_bounds__(kThreads) void k_prefill_routed_score(PrefillArgs a
   __syncthreads();
   bf16x8 b0[S], b1[S];
   f32x16 accx, accy;
+  f32x4 pe = {0.f, 0.f, 0.f, 0.f};
   load_b(b0, ktile, 0);
   for (int st = 0; st < n_stages; ++st) {
     const uint8_t* tile = ktile + (st & 1) * STAGE;
     const int k0 = st * kStageKeys;
     load_b(b1, tile, 1);
     mfma(accx, b0);
-    if (st > 0) finish(k0 - 32, epi(accy));
+    if (st > 0) finish_pair(k0 - 64, pe, epi(accy));
     slot(1, st + 1);
     __builtin_amdgcn_sched_barrier(0);
     load_b(b0, tile, 2);
     mfma(accy, b1);
-    finish(k0, epi(accx));
+    pe = epi(accx);
     slot(2, st + 1);
     __builtin_amdgcn_sched_barrier(0);
     load_b(b1, tile, 3);
@@ -205,15 +212,15 @@ __global__ __launch_bounds__(kThreads) void k_prefill_routed_score(PrefillArgs a
     slot(3, st + 1);
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
-    finish(k0 + 32, epi(accy));
+    finish_pair(k0, pe, epi(accy));
     load_b(b0, ktile + ((st + 1) & 1) * STAGE, 0);
     __builtin_amdgcn_sched_barrier(0);
     mfma(accy, b1);
-    finish(k0 + 64, epi(accx));
+    pe = epi(accx);
     slot(0, st + 2);
     __builtin_amdgcn_sched_barrier(0);
   }
-  finish(n_stages * kStageKeys - 32, epi(accy));
+  finish_pair(n_stages * kStageKeys - 64, pe, epi(accy));
   __syncthreads();
 
   // each row's threshold: the 10-bit bin holding its k-th score
