@@ -368,8 +368,10 @@ MisaPrefillPlan plan_misa_prefill(int64_t nq, int n_heads, int head_dim, int n_s
   p.heads = A.take((size_t)nq * dsa::kRoutedMaxHeads * 4);
   p.prefix = A.take((size_t)l_max * head_dim * 2);
   if (!pooled_given) p.pooled = A.take((size_t)n_seq * p.m_max * head_dim * 2);
-  p.row_stride = (l_max + 3) & ~(int64_t)3;
-  p.scores = A.take((size_t)nq * p.row_stride * 4);
+  // whole 128-key stages per row (the routed scorer stores every key of its
+  // last stage) plus one spare row for rows that are not scored
+  p.row_stride = (l_max + 127) & ~(int64_t)127;
+  p.scores = A.take((size_t)(nq + 1) * p.row_stride * 4);
   p.rowmeta = A.take((size_t)nq * 16);
   p.total = A.off;
   return p;
@@ -451,6 +453,7 @@ int misa_prefill(const void* q, const float* w, const void* k, const void* k_poo
   pa.l_max = l_max;
   pa.row_stride = p.row_stride;
   pa.scores = at<float>(workspace, p.scores);
+  pa.spare_row = pa.scores + (size_t)nq * p.row_stride;
   pa.rowmeta = at<int32_t>(workspace, p.rowmeta);
   pa.bin_bits = 10;
   pa.heads = rh.heads;

@@ -65,10 +65,8 @@ DSA_DEVICE float fmac_rowbcast(float p, float W, float x) {
   return p;
 }
 
-// sum over head tiles ht and accumulator registers r of w(ht, r) * max(0, acc),
-// where W[ht] holds, in lane 16*g + r, the weight of the head that register r
-// holds in lanes of row group g (see the MFMA layouts in dsa_scorers.h).
-// W[16*(lane/16) + R] * x (the first term of a row-broadcast sum).
+// W[16*(lane/16) + R] * x (the first term of a row-broadcast sum; -0.0 when W
+// is negative and x is +0.0).
 template <int R>
 DSA_DEVICE float fmul_rowbcast(float W, float x) {
   float p;
@@ -78,6 +76,9 @@ DSA_DEVICE float fmul_rowbcast(float W, float x) {
   return p;
 }
 
+// sum over head tiles ht and accumulator registers r of w(ht, r) * max(0, acc),
+// where W[ht] holds, in lane 16*g + r, the weight of the head that register r
+// holds in lanes of row group g (see the MFMA layouts in dsa_scorers.h).
 template <int HT, int... R>
 DSA_DEVICE float weighted_relu_sum(const f32x16 (&acc)[HT], const float (&W)[HT],
                                    std::integer_sequence<int, R...>) {

@@ -112,6 +112,8 @@ struct PrefillArgs {
   int bin_bits;                // first-level histogram bits (12 dense, 10 routed)
   const int32_t* heads;        // routed pass: [nq, heads_stride] head ids (first h_use used)
   int heads_stride, h_use;
+  float* spare_row;            // routed pass: [row_stride] scratch row taking the stores of
+                               // unscored rows (row_stride a multiple of 128 there)
   int32_t* out_idx;
   float* out_score;
 };

@@ -12,8 +12,9 @@
 // slot r/4 of the wave, so registers 4g .. 4g+3 sum into row g's partial, and
 // one lane-half swap of two sub-tiles' partials gives row g's scores of 64
 // consecutive keys in one register.
-// Per-row histograms are 10-bit (u16 pairs, 2 KiB per row) so that 32 rows'
-// fit in LDS beside the two stages.
+// Per-row histograms are 10-bit with 16-bit counters, two per word (bin b in
+// word b % 512), 2 KiB per row, so that 32 rows' fit in LDS beside the two
+// stages.
 #include "dsa_internal.h"
 #include "dsa_common.h"
 
@@ -36,18 +37,33 @@ constexpr size_t routed_lds_bytes() {
 }
 
 // per-row partial sums of one sub-tile: p[g] = sum over registers 4g..4g+3 of
-// w * max(0, acc) (weights by row broadcast, see weighted_relu_sum)
+// w * max(0, acc) (weights by row broadcast, see fmac_rowbcast); registers R0 ..
+// R0+N-1 at a time, so that the epilogue can be spread over MFMA steps
 template <int R>
 DSA_DEVICE void row_term(f32x4& p, float W, float x) {
   if constexpr ((R & 3) == 0) p[R >> 2] = fmul_rowbcast<R>(W, x);   // first term of row R/4
   else p[R >> 2] = fmac_rowbcast<R>(p[R >> 2], W, x);
 }
 
-template <int... R>
-DSA_DEVICE f32x4 row_partials(const f32x16& acc, float W, std::integer_sequence<int, R...>) {
-  f32x4 p;
-  (row_term<R>(p, W, relu(acc[R])), ...);
-  return p;
+template <int R0, int... R>
+DSA_DEVICE void epi_seq(f32x4& p, const f32x16& acc, float W, std::integer_sequence<int, R...>) {
+  (row_term<R0 + R>(p, W, relu(acc[R0 + R])), ...);
+}
+
+template <int R0, int N>
+DSA_DEVICE void epi_regs(f32x4& p, const f32x16& acc, float W) {
+  epi_seq<R0>(p, acc, W, std::make_integer_sequence<int, N>{});
+}
+
+template <int N, class F, int... I>
+DSA_DEVICE void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+
+// f(integral_constant<0>) .. f(integral_constant<N-1>), in order
+template <int N, class F>
+DSA_DEVICE void static_for(F&& f) {
+  static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
 }
 
 template <int D>
@@ -87,7 +103,7 @@ __global__ __launch_bounds__(kThreads) void k_prefill_routed_score(PrefillArgs a
   __syncthreads();
   if (lane == 0) atomicMax(&s_maxpos, wave_max);
   __syncthreads();
-  const int maxpos = s_maxpos;
+  const int maxpos = __builtin_amdgcn_readfirstlane(s_maxpos);
   if (maxpos < 0) return;
   const int n_stages = maxpos / kStageKeys + 1;
   auto pos_of = [&](int g) {                 // pos[g] for a per-lane g
@@ -122,10 +138,13 @@ __global__ __launch_bounds__(kThreads) void k_prefill_routed_score(PrefillArgs a
   // stage loading (as in the dense prefill kernel): four slots per stage
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.keys);
   u32x4 pre[LOADS];
+  // (a wave-uniform stage base plus a 32-bit lane offset; keys clamp to maxpos)
   auto fetch_piece = [&](int j, int st) {
     const int p = threadIdx.x + j * kThreads;
-    const int key = min(st * kStageKeys + p / NC, maxpos);   // inside the cache
-    pre[j] = *reinterpret_cast<const u32x4*>(kbase + (size_t)key * RB + (p % NC) * 16);
+    const int sk = min(st * kStageKeys, maxpos);
+    const int key = min(p / NC, maxpos - sk);
+    const uint8_t* sbase = kbase + (size_t)sk * RB;
+    pre[j] = *reinterpret_cast<const u32x4*>(sbase + (uint32_t)(key * RB + (p % NC) * 16));
   };
   auto stash_piece = [&](int j, int buf) {
     const int p = threadIdx.x + j * kThreads;
@@ -145,43 +164,48 @@ __global__ __launch_bounds__(kThreads) void k_prefill_routed_score(PrefillArgs a
       b[s] = __builtin_bit_cast(bf16x8,
                                 *reinterpret_cast<const u32x4*>(tile + boff + sub * 32 * LB + s * 32));
   };
-  auto mfma = [&](f32x16& acc, const bf16x8 (&b)[S]) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-#pragma unroll
-    for (int s = 0; s < S; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], b[s], acc, 0, 0, 0);
-  };
 
-  // finish of two sub-tiles A (keys key0..key0+31) and B (key0+32..key0+63):
-  // for each row g of the wave, one lane-half swap of its partials puts A's
-  // key l in lane l and B's key l-32 in lane l (l >= 32), so one register
-  // holds row g's scores of 64 consecutive keys and its score row and
-  // histogram are addressed from a wave-uniform base
+  // Finish of a pair of sub-tiles (keys key0 .. key0+63): for row g of the
+  // wave, one lane-half swap of the two sub-tiles' partials puts key key0 + l
+  // in lane l, so one register holds row g's 64 scores.  Branch-free: every
+  // lane stores (score rows are padded to whole stages, rows that are not
+  // scored write a spare row) and keys past the row's position add 0 to the
+  // histogram.  The +0.0 turns a -0.0 sum (all terms -0.0) into +0.0, so that
+  // score keys need no -0.0 fold.
   const size_t rs = (size_t)a.row_stride;
-  auto finish_pair = [&](int key0, const f32x4& pa, const f32x4& pb) {
-    const int u = key0 + lane;
+  const int t0u = __builtin_amdgcn_readfirstlane(t0);
+  uint8_t* srow[kPer];
 #pragma unroll
-    for (int g = 0; g < kPer; ++g) {
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(pa[g]), __float_as_uint(pb[g]),
-                                                       false, false);
-      const float sc = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-      const int p = pos[g];                     // wave-uniform
-      if (key0 > p) continue;
-      float* srow = a.scores + (size_t)(t0 + g) * rs;
-      uint32_t* hrow = hist + (wv * kPer + g) * (kRBins / 2);
-      if (key0 + 63 <= p || u <= p) {
-        srow[u] = sc;
-        const uint32_t bin = fast_key(sc) >> kRBinShift;
-        atomicAdd(hrow + (bin >> 1), 1u << ((bin & 1u) << 4));
-      }
-    }
+  for (int g = 0; g < kPer; ++g) {
+    pos[g] = __builtin_amdgcn_readfirstlane(pos[g]);
+    srow[g] = reinterpret_cast<uint8_t*>(pos[g] >= 0 ? a.scores + (size_t)(t0u + g) * rs : a.spare_row);
+  }
+  uint32_t* hwave = hist + wv * kPer * (kRBins / 2);
+  float fin_sc[2];
+  auto fin_store = [&](int i, int g, int key0, const f32x4& pa, const f32x4& pb) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(pa[g]), __float_as_uint(pb[g]),
+                                                     false, false);
+    fin_sc[i] = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) + 0.0f;
+    *reinterpret_cast<float*>(srow[g] + (uint32_t)(key0 + lane) * 4u) = fin_sc[i];
   };
-  auto epi = [&](const f32x16& acc) {
-    return row_partials(acc, W, std::make_integer_sequence<int, 16>{});
+  // bin b counts in word b % 512: low half for b < 512 (negative scores, key
+  // bit 31 clear), high half otherwise
+  auto fin_count = [&](int i, int g, int key0) {
+    const float sc = fin_sc[i];
+    const uint32_t word = (fast_key(sc) >> kRBinShift) & (kRBins / 2 - 1);
+    const uint32_t inc = key0 + lane <= pos[g] ? ((int32_t)__float_as_uint(sc) < 0 ? 1u : 0x10000u) : 0u;
+    atomicAdd(hwave + g * (kRBins / 2) + word, inc);
   };
 
-  // software pipeline over 32-key sub-tiles, stage barrier in sub-tile 2 (see
-  // the dense prefill kernel); sub-tiles are finished in pairs
+  // Software pipeline over 32-key sub-tiles c = 0..3 of each 128-key stage.
+  // The section of sub-tile c issues its S MFMAs (B operands read one section
+  // earlier), one step each, and, spread over the steps: the B reads of the
+  // next sub-tile, the ReLU-weighted epilogue of the previous sub-tile into
+  // P[c-1], two rows' finish of an earlier pair and one stage-loading slot.
+  // Pair (0,1) of a stage is finished in its section 3 (rows 0, 1) and the
+  // next stage's section 0 (rows 2, 3); pair (2,3) in the next stage's
+  // sections 1 and 2.  The stage barrier closes section 2.  Steps are fenced
+  // so that the interleave is kept as written.
 #pragma unroll
   for (int j = 0; j < LOADS; ++j) fetch_piece(j, 0);
 #pragma unroll
@@ -190,37 +214,72 @@ __global__ __launch_bounds__(kThreads) void k_prefill_routed_score(PrefillArgs a
   for (int j = 0; j < LOADS; ++j) fetch_piece(j, 1);
   slot(0, 1);
   __syncthreads();
-  bf16x8 b0[S], b1[S];
-  f32x16 accx, accy;
-  f32x4 pe = {0.f, 0.f, 0.f, 0.f};
-  load_b(b0, ktile, 0);
-  for (int st = 0; st < n_stages; ++st) {
+  bf16x8 bb[2][S];
+  f32x16 acc[2];
+  f32x4 P[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) P[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  load_b(bb[0], ktile, 0);
+  constexpr int EPR = 16 / S;                 // epilogue registers per step
+  // step s of section c in stage st (c, s compile-time; st runtime)
+  auto step = [&](auto C, auto SS, int st, bool live) {
+    constexpr int c = decltype(C)::value, s = decltype(SS)::value;
     const uint8_t* tile = ktile + (st & 1) * STAGE;
-    const int k0 = st * kStageKeys;
-    load_b(b1, tile, 1);
-    mfma(accx, b0);
-    if (st > 0) finish_pair(k0 - 64, pe, epi(accy));
-    slot(1, st + 1);
+    f32x16& ac = acc[c & 1];
+    if constexpr (s == 0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ac[r] = 0.f;
+    }
+    ac = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], bb[c & 1][s], ac, 0, 0, 0);
+    // B of the next sub-tile
+    {
+      const uint8_t* nt = c == 3 ? ktile + ((st + 1) & 1) * STAGE : tile;
+      constexpr int nsub = (c + 1) & 3;
+      bb[(c + 1) & 1][s] = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4*>(nt + boff + nsub * 32 * LB + s * 32));
+    }
+    // epilogue of the previous sub-tile (c - 1, or sub-tile 3 of the previous stage)
+    if (c != 0 || live) {
+      const f32x16& ap = acc[(c + 1) & 1];
+      f32x4& pp = P[(c + 3) & 3];
+      epi_regs<s * EPR, EPR>(pp, ap, W);
+    }
+    // finish: two rows of a pair
+    // (store and count of a row one step apart when there are 8 steps)
+    constexpr int fa = 1, fb = S >= 8 ? 4 : 2, lag = S >= 8 ? 1 : 0;
+    constexpr bool prev_pair = c != 3;                          // pair of the previous stage
+    const int pk0 = c == 0 ? (st - 1) * kStageKeys : c == 3 ? st * kStageKeys : (st - 1) * kStageKeys + 64;
+    constexpr int pi = (c == 0 || c == 3) ? 0 : 2;              // first sub-tile of the pair
+    constexpr int g0 = (c == 0 || c == 2) ? 2 : 0;              // first row
+    if (!prev_pair || live) {
+      if constexpr (s == fa) fin_store(0, g0, pk0, P[pi], P[pi + 1]);
+      if constexpr (s == fa + lag) fin_count(0, g0, pk0);
+      if constexpr (s == fb) fin_store(1, g0 + 1, pk0, P[pi], P[pi + 1]);
+      if constexpr (s == fb + lag) fin_count(1, g0 + 1, pk0);
+    }
+    if constexpr (s == S - 2) slot((c + 1) & 3, c == 3 ? st + 2 : st + 1);
+    if constexpr (c == 2 && s == S - 1) __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
-    load_b(b0, tile, 2);
-    mfma(accy, b1);
-    pe = epi(accx);
-    slot(2, st + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    load_b(b1, tile, 3);
-    mfma(accx, b0);
-    slot(3, st + 1);
-    __syncthreads();
-    __builtin_amdgcn_sched_barrier(0);
-    finish_pair(k0, pe, epi(accy));
-    load_b(b0, ktile + ((st + 1) & 1) * STAGE, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma(accy, b1);
-    pe = epi(accx);
-    slot(0, st + 2);
-    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto section = [&](auto C, int st, bool live) {
+    static_for<S>([&](auto SS) { step(C, SS, st, live); });
+  };
+  for (int st = 0; st < n_stages; ++st) {
+    const bool live = st > 0;
+    section(std::integral_constant<int, 0>{}, st, live);
+    section(std::integral_constant<int, 1>{}, st, live);
+    section(std::integral_constant<int, 2>{}, st, live);
+    section(std::integral_constant<int, 3>{}, st, live);
   }
-  finish_pair(n_stages * kStageKeys - 64, pe, epi(accy));
+  // drain: epilogue of the last sub-tile, rows 2, 3 of pair (0,1), pair (2,3)
+  {
+    const int k0 = (n_stages - 1) * kStageKeys;
+    epi_regs<0, 16>(P[3], acc[1], W);
+    fin_store(0, 2, k0, P[0], P[1]); fin_count(0, 2, k0);
+    fin_store(1, 3, k0, P[0], P[1]); fin_count(1, 3, k0);
+#pragma unroll
+    for (int g = 0; g < kPer; ++g) { fin_store(0, g, k0 + 64, P[2], P[3]); fin_count(0, g, k0 + 64); }
+  }
   __syncthreads();
 
   // each row's threshold: the 10-bit bin holding its k-th score
@@ -236,11 +295,10 @@ __global__ __launch_bounds__(kThreads) void k_prefill_routed_score(PrefillArgs a
     }
     const uint32_t* hrow = hist + (wv * kPer + g) * (kRBins / 2);
     const int b_hi = kRBins - PERB * lane;   // lane owns bins [b_hi - PERB, b_hi)
+    const int sh = 16 * ((b_hi - 1) / (kRBins / 2));   // all in one half of the words
+    const int w0 = (b_hi - PERB) & (kRBins / 2 - 1);
     uint32_t mine = 0;
-    for (int wd = (b_hi - PERB) / 2; wd < b_hi / 2; ++wd) {
-      const uint32_t v = hrow[wd];
-      mine += (v & 0xFFFFu) + (v >> 16);
-    }
+    for (int i = 0; i < PERB; ++i) mine += (hrow[w0 + i] >> sh) & 0xFFFFu;
     uint32_t incl = mine;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -251,7 +309,7 @@ __global__ __launch_bounds__(kThreads) void k_prefill_routed_score(PrefillArgs a
     if (before < need && incl >= need) {
       uint32_t accum = before;
       for (int b = b_hi - 1; b >= b_hi - PERB; --b) {
-        const uint32_t c = (hrow[b >> 1] >> ((b & 1) * 16)) & 0xFFFFu;
+        const uint32_t c = (hrow[b & (kRBins / 2 - 1)] >> sh) & 0xFFFFu;
         if (accum + c >= need) {
           meta[0] = b;
           meta[1] = (int32_t)accum;
@@ -282,6 +340,8 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
 hipError_t launch_prefill_routed_score(const PrefillArgs& a, hipStream_t stream) {
   if (a.nq <= 0) return hipSuccess;
   if (a.h_use < 1 || a.h_use > kRoutedMaxHeads || a.bin_bits != kRBinBits) return hipErrorInvalidValue;
+  // every key of a row's last stage is stored: rows span whole stages
+  if (a.row_stride % kStageKeys != 0 || a.row_stride < a.l_max || !a.spare_row) return hipErrorInvalidValue;
   if (a.head_dim == 128) return launch_t<128>(a, stream);
   if (a.head_dim == 64) return launch_t<64>(a, stream);
   return hipErrorInvalidValue;
