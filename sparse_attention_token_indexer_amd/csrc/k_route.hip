@@ -183,34 +183,54 @@ __global__ __launch_bounds__(256) void k_route_rows(RouteArgs a) {
 }
 
 // Router for many queries on ONE sequence (prefill shape): the rows share the
-// pooled keys, so 8 rows per workgroup (one wave each, heads x 32 blocks per
-// MFMA) read 128-block stages from LDS (double-buffered, rows padded to
+// pooled keys, so 4 rows per workgroup (one wave each, heads x 32 blocks per
+// MFMA) read 64-block stages from LDS (double-buffered, rows padded to
 // 2*D + 16 bytes, as in the prefill scorers).  Each row sums max(0, q_j . kbar_b)
 // over its full blocks b < (pos + 1) / B; the partial last block (prefix mean
 // of the row's position, from a.partial by position) is one extra tile with a
 // single valid column.  Per-head sums over the 32 block columns go through a
-// padded LDS transpose; one slice per query (part[t][j]).
-constexpr int kPRStage = 128;
-constexpr int kPRRows = 8;
+// padded LDS transpose in the stage buffers; one slice per query (part[t][j]).
+// The router streams every row's q (all heads) from HBM once: small
+// workgroups (35 KB of LDS at D = 128) let two share a CU, so one's q loads
+// overlap the other's MFMAs.
+constexpr int kPRStage = 64;
+constexpr int kPRRows = 4;
 
+// the two stages, or the column transpose that reuses them if larger
 template <int D>
 constexpr size_t prefill_route_lds() {
-  return 2 * (size_t)kPRStage * (2 * D + 16) + (size_t)kPRRows * 64 * 33 * 4;
+  constexpr size_t stages = 2 * (size_t)kPRStage * (2 * D + 16);
+  constexpr size_t red = (size_t)kPRRows * 64 * 33 * 4;
+  return stages > red ? stages : red;
+}
+
+template <int N, class F, int... I>
+DSA_DEVICE void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+
+// f(integral_constant<0>) .. f(integral_constant<N-1>), in order
+template <int N, class F>
+DSA_DEVICE void static_for(F&& f) {
+  static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
 }
 
 template <int HT, int D>
-__global__ __launch_bounds__(64 * kPRRows) void k_route_prefill(RouteArgs a) {
+// (two workgroups per CU: at most 256 registers per lane)
+__global__ __launch_bounds__(64 * kPRRows) __attribute__((amdgpu_waves_per_eu(2)))
+void k_route_prefill(RouteArgs a) {
   constexpr int kT = 64 * kPRRows;
   constexpr int S = D / 16, RB = 2 * D, NC = RB / 16, LB = RB + 16;
   constexpr int STAGE = kPRStage * LB, PIECES = kPRStage * NC;
   constexpr int LOADS = PIECES / kT;
   static_assert(PIECES % kT == 0, "every thread stores whole pieces");
+  constexpr int NSUB = kPRStage / 32;                    // sub-tiles per stage
+  constexpr int PER_SLOT = (LOADS + NSUB - 1) / NSUB;
   extern __shared__ __align__(16) uint8_t smem[];
   uint8_t* ktile = smem;                                        // [2][STAGE]
-  float* red_all = reinterpret_cast<float*>(smem + 2 * STAGE);  // [rows][64 * 33]
   __shared__ int s_maxfull;
   const int wv = wave_id(), lane = lane_id(), h = lane >> 5, m = lane & 31;
-  const int t = (int)blockIdx.x * kPRRows + wv;
+  const int t = ((int)gridDim.x - 1 - (int)blockIdx.x) * kPRRows + wv;   // longest rows first
   int64_t pos = -1;
   if (t < a.nq) {
     const int seq = a.q_seq ? a.q_seq[t] : 0;
@@ -222,7 +242,7 @@ __global__ __launch_bounds__(64 * kPRRows) void k_route_prefill(RouteArgs a) {
   __syncthreads();
   if (lane == 0) atomicMax(&s_maxfull, nfull);
   __syncthreads();
-  const int maxfull = s_maxfull;
+  const int maxfull = __builtin_amdgcn_readfirstlane(s_maxfull);
 
   bf16x8 qa[HT][S];
   {
@@ -236,12 +256,110 @@ __global__ __launch_bounds__(64 * kPRRows) void k_route_prefill(RouteArgs a) {
         qa[ht][s] = ok ? load_bf16x8(q_t + (size_t)(ok ? row : 0) * D + 8 * h + 16 * s) : zero_bf16x8();
     }
   }
+  // hsum[ht][r] += max(0, x) for block columns the row counts: med3(x, 0, cap)
+  // with cap = +inf for a counted column and 0 otherwise
   float hsum[HT][16];
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
     for (int r = 0; r < 16; ++r) hsum[ht][r] = 0.f;
-  auto tile_sum = [&](const bf16x8 (&b)[S], bool valid) {
+  auto cap_of = [&](int b0) { return b0 + m < nfull ? __builtin_inff() : 0.f; };
+
+  const int n_stages = (maxfull + kPRStage - 1) / kPRStage;
+  if (n_stages > 0) {
+    const uint8_t* pbase = reinterpret_cast<const uint8_t*>(a.pooled);
+    const uint32_t boff = (uint32_t)(m * LB + h * 16);
+    const int last = maxfull - 1;
+    u32x4 pre[LOADS];
+    auto fetch_piece = [&](int j, int st) {
+      const int p = threadIdx.x + j * kT;
+      const int row = min(st * kPRStage + p / NC, last);     // inside the pooled keys
+      pre[j] = *reinterpret_cast<const u32x4*>(pbase + (size_t)row * RB + (p % NC) * 16);
+    };
+    auto stash_piece = [&](int j, int buf) {
+      const int p = threadIdx.x + j * kT;
+      *reinterpret_cast<u32x4*>(ktile + buf * STAGE + (p / NC) * LB + (p % NC) * 16) = pre[j];
+    };
+    auto slot = [&](int q, int st) {
+#pragma unroll
+      for (int j = q * PER_SLOT; j < (q + 1) * PER_SLOT && j < LOADS; ++j) {
+        stash_piece(j, st & 1);
+        fetch_piece(j, st + 1);
+      }
+    };
+    // Software pipeline over units (sub-tile c of a stage, head tile u), as in
+    // the routed prefill scorer: step s of a unit issues its MFMA for k-step s
+    // and adds 16 / S accumulator
+    // registers of the previous unit into hsum; the last head tile of a
+    // sub-tile also reads the next sub-tile's B operand for k-step s.  Units
+    // alternate between two accumulators.  One stage-loading slot per
+    // sub-tile; the stage barrier closes the second-to-last sub-tile.
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) fetch_piece(j, 0);
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) stash_piece(j, 0);
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) fetch_piece(j, 1);
+    slot(0, 1);
+    __syncthreads();
+    bf16x8 bb[S];
+    f32x16 acc[2];
+    // (zero accumulators and cap 0 make the first unit's epilogue add +0)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[0][r] = acc[1][r] = 0.f;
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+      bb[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ktile + boff + s * 32));
+    constexpr int EPR = 16 / S;
+    float cap_prev = 0.f;
+    auto step = [&](auto C, auto U, auto SS, int st, float cap_p) {
+      constexpr int c = decltype(C)::value, u = decltype(U)::value, s = decltype(SS)::value;
+      constexpr int par = (c * HT + u) & 1, pu = u == 0 ? HT - 1 : u - 1;
+      if constexpr (s == 0) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[par][r] = 0.f;
+      }
+      acc[par] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[u][s], bb[s], acc[par], 0, 0, 0);
+      if constexpr (u == HT - 1) {
+        const uint8_t* nt = ktile + ((c == NSUB - 1 ? st + 1 : st) & 1) * STAGE;
+        constexpr int nsub = (c + 1) % NSUB;
+        bb[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(nt + boff + nsub * 32 * LB + s * 32));
+      }
+#pragma unroll
+      for (int r = s * EPR; r < (s + 1) * EPR; ++r)
+        hsum[pu][r] += __builtin_amdgcn_fmed3f(acc[par ^ 1][r], 0.f, cap_p);
+      if constexpr (u == HT - 1 && s == S - 2) slot((c + 1) % NSUB, c == NSUB - 1 ? st + 2 : st + 1);
+      if constexpr (c == NSUB - 2 && u == HT - 1 && s == S - 1) __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto unit = [&](auto C, auto U, int st, float cap_p) {
+      static_for<S>([&](auto SS) { step(C, U, SS, st, cap_p); });
+    };
+    // all units of sub-tile C; cap_in is the cap of the unit before them
+    auto subtile = [&](auto C, int st, float cap_in, float cap_c) {
+      unit(C, std::integral_constant<int, 0>{}, st, cap_in);
+      if constexpr (HT > 1) unit(C, std::integral_constant<int, 1>{}, st, cap_c);
+    };
+    static_assert(NSUB == 2, "two sub-tiles per stage");
+    for (int st = 0; st < n_stages; ++st) {
+      const int k0 = st * kPRStage;
+      const float c0 = cap_of(k0), c1 = cap_of(k0 + 32);
+      subtile(std::integral_constant<int, 0>{}, st, cap_prev, c0);
+      subtile(std::integral_constant<int, 1>{}, st, c0, c1);
+      cap_prev = c1;
+    }
+    // the last unit (sub-tile NSUB - 1, head tile HT - 1)
+    constexpr int last_par = ((NSUB - 1) * HT + HT - 1) & 1;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) hsum[HT - 1][r] += __builtin_amdgcn_fmed3f(acc[last_par][r], 0.f, cap_prev);
+  }
+  // the partial last block: one tile whose column 0 is the prefix mean of pos
+  if (pos >= 0 && ((pos + 1) % a.block) != 0) {
+    bf16x8 b[S];
+    const uint16_t* rowp = a.partial + (size_t)pos * D;
+#pragma unroll
+    for (int s = 0; s < S; ++s) b[s] = m == 0 ? load_bf16x8(rowp + 8 * h + 16 * s) : zero_bf16x8();
+    const float cap = m == 0 ? __builtin_inff() : 0.f;
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
       f32x16 acc;
@@ -251,63 +369,13 @@ __global__ __launch_bounds__(64 * kPRRows) void k_route_prefill(RouteArgs a) {
       for (int s = 0; s < S; ++s)
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ht][s], b[s], acc, 0, 0, 0);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) hsum[ht][r] += valid ? relu(acc[r]) : 0.f;
-    }
-  };
-
-  const int n_stages = (maxfull + kPRStage - 1) / kPRStage;
-  if (n_stages > 0) {
-    const uint8_t* pbase = reinterpret_cast<const uint8_t*>(a.pooled);
-    const int last = maxfull - 1;
-    u32x4 pre[LOADS];
-    auto fetch = [&](int st) {
-#pragma unroll
-      for (int j = 0; j < LOADS; ++j) {
-        const int p = threadIdx.x + j * kT;
-        const int row = min(st * kPRStage + p / NC, last);     // inside the pooled keys
-        pre[j] = *reinterpret_cast<const u32x4*>(pbase + (size_t)row * RB + (p % NC) * 16);
-      }
-    };
-    auto stash = [&](int buf) {
-#pragma unroll
-      for (int j = 0; j < LOADS; ++j) {
-        const int p = threadIdx.x + j * kT;
-        *reinterpret_cast<u32x4*>(ktile + buf * STAGE + (p / NC) * LB + (p % NC) * 16) = pre[j];
-      }
-    };
-    const uint32_t boff = (uint32_t)(m * LB + h * 16);
-    fetch(0);
-    stash(0);
-    __syncthreads();
-    for (int st = 0; st < n_stages; ++st) {
-      const bool more = st + 1 < n_stages;
-      if (more) fetch(st + 1);
-      const uint8_t* tile = ktile + (st & 1) * STAGE;
-#pragma unroll
-      for (int sub = 0; sub < kPRStage / 32; ++sub) {
-        const int b0 = st * kPRStage + sub * 32;
-        if (b0 < nfull) {                       // wave-uniform
-          bf16x8 b[S];
-#pragma unroll
-          for (int s = 0; s < S; ++s)
-            b[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(tile + boff + sub * 32 * LB + s * 32));
-          tile_sum(b, b0 + m < nfull);
-        }
-      }
-      if (more) stash((st + 1) & 1);
-      __syncthreads();
+      for (int r = 0; r < 16; ++r) hsum[ht][r] += __builtin_amdgcn_fmed3f(acc[r], 0.f, cap);
     }
   }
-  // the partial last block: one tile whose column 0 is the prefix mean of pos
-  if (pos >= 0 && ((pos + 1) % a.block) != 0) {
-    bf16x8 b[S];
-    const uint16_t* rowp = a.partial + (size_t)pos * D;
-#pragma unroll
-    for (int s = 0; s < S; ++s) b[s] = m == 0 ? load_bf16x8(rowp + 8 * h + 16 * s) : zero_bf16x8();
-    tile_sum(b, m == 0);
-  }
-  // per head: the sum over the 32 block columns (lane m holds column m)
-  float* red = red_all + wv * (64 * 33);
+  // per head: the sum over the 32 block columns (lane m holds column m), in
+  // the stage buffers once every wave is done with them
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem) + wv * (64 * 33);
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
