@@ -39,9 +39,18 @@ WORKLOADS = {"dense_decode": 2, "tiny": 1, "dense_prefill": 3, "misa": 4, "misa_
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
 
 
-def kernel_source_hash() -> str:
+# source file of each workload's dominant kernel (its hash, with every shared
+# header's, identifies the build that traffic counters were taken on)
+KERNEL_SOURCE = {"dense_decode": "k_score_select.hip", "tiny": "k_score_select.hip",
+                 "misa": "k_score_select.hip", "misa_dagger": "k_score_select.hip",
+                 "hisa": "k_score_select.hip", "dense_prefill": "k_prefill.hip",
+                 "misa_prefill": "k_prefill_routed.hip", "pool": "k_pool.hip"}
+
+
+def kernel_source_hash(workload: str) -> str:
     h = hashlib.sha256()
-    for f in sorted(os.listdir(CSRC)):
+    files = [f for f in sorted(os.listdir(CSRC)) if f.endswith(".h")] + [KERNEL_SOURCE[workload]]
+    for f in files:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -49,14 +58,15 @@ def kernel_source_hash() -> str:
 
 def stored_traffic(workload: str):
     """HBM bytes per launch of the dominant kernel from rocprofv3 counters, if they
-    were taken on the current kernel sources (else None)."""
+    were taken on the current source of that kernel and the shared headers
+    (else None)."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
     e = t.get(workload)
-    if not e or e.get("kernel_hash") != kernel_source_hash():
+    if not e or e.get("kernel_hash") != kernel_source_hash(workload):
         return None
     return e.get("bytes_per_launch")
 
@@ -147,6 +157,8 @@ def main() -> int:
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flush", default="read", choices=("read", "write"),
+                    help="how cold-timed workloads evict the caches before each step")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device copy (for HBM counter calibration)")
     args = ap.parse_args()
@@ -282,10 +294,17 @@ def main() -> int:
         raise ValueError(name)
 
     # Workloads that touch less than the 256 MB last-level cache are timed cold:
-    # a 512 MiB buffer is overwritten before every step (outside its timing).
+    # before every step (outside its timing) a 512 MiB buffer is read through
+    # (--flush read: the caches end up holding its clean lines) or overwritten
+    # (--flush write: they end up holding dirty lines, whose write-back then
+    # competes with the step's own reads).
     flush = None
     if name in ("hisa", "tiny"):
-        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        flush_buf = torch.zeros(128 << 20, dtype=torch.float32, device=dev)
+        if args.flush == "write":
+            flush = lambda: flush_buf.zero_()
+        else:
+            flush = lambda: flush_buf.amax()
 
     def timed_region() -> float:
         """ms per step over args.steps steps (barrier + synchronize around)."""
@@ -301,7 +320,7 @@ def main() -> int:
             return t_start.elapsed_time(t_end) / args.steps
         total = 0.0
         for _ in range(args.steps):
-            flush.zero_()
+            flush()
             t_start = torch.cuda.Event(enable_timing=True)
             t_end = torch.cuda.Event(enable_timing=True)
             t_start.record()
@@ -333,7 +352,7 @@ def main() -> int:
     per_call = []
     for _ in range(args.steps):
         if flush is not None:
-            flush.zero_()
+            flush()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -401,7 +420,7 @@ def main() -> int:
                  "hbm_frac": call_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
                  "pair_scores_per_s": pairs / (ms_per_step * 1e-3),
                  "head_dots_per_s": call_flops / (2 * d) / (ms_per_step * 1e-3)},
-        "cold_cache": flush is not None,
+        "cold_cache": (args.flush + " 512 MiB") if flush is not None else False,
         "kernel_avg_us": per_kernel,
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -33,26 +33,28 @@ struct ScorerMfma32 {
 
   DSA_DEVICE static int row_key(int) { return lane_id() & 31; }
 
+  // (both head-list reads come first, then the weight and query loads with no
+  // wait between them)
   DSA_DEVICE void init(const uint16_t* q_t, const float* w_t, const int32_t* heads_t,
                        int h_use, float*) {
     const int lane = lane_id(), m = lane & 31, h = lane >> 5;
+    int wsel[HT], qsel[HT];
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
-      int slot = ht * 32 + m;
-      if (slot < h_use) {
-        int head = heads_t ? heads_t[slot] : slot;
-        const uint16_t* src = q_t + (size_t)head * D + 8 * h;
-#pragma unroll
-        for (int s = 0; s < S; ++s) qa[ht][s] = load_bf16x8(src + 16 * s);
-      } else {
-#pragma unroll
-        for (int s = 0; s < S; ++s) qa[ht][s] = zero_bf16x8();
-      }
       // lane 16*g + r: the head slot that accumulator register r holds in
       // lanes of row group g (lane half g/2 = h)
       const int r = lane & 15;
       const int rs = ht * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-      W[ht] = rs < h_use ? w_t[heads_t ? heads_t[rs] : rs] : 0.f;
+      const int slot = ht * 32 + m;
+      wsel[ht] = rs < h_use ? (heads_t ? heads_t[rs] : rs) : -1;
+      qsel[ht] = slot < h_use ? (heads_t ? heads_t[slot] : slot) : -1;
+    }
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      W[ht] = wsel[ht] >= 0 ? w_t[wsel[ht]] : 0.f;
+      const uint16_t* src = q_t + (size_t)(qsel[ht] >= 0 ? qsel[ht] : 0) * D + 8 * h;
+#pragma unroll
+      for (int s = 0; s < S; ++s) qa[ht][s] = qsel[ht] >= 0 ? load_bf16x8(src + 16 * s) : zero_bf16x8();
     }
   }
 
@@ -98,20 +100,19 @@ struct ScorerMfma16 {
   DSA_DEVICE void init(const uint16_t* q_t, const float* w_t, const int32_t* heads_t,
                        int h_use, float*) {
     const int lane = lane_id(), m = lane & 15, g = lane >> 4;
-    if (m < h_use) {
-      int head = heads_t ? heads_t[m] : m;
-      const uint16_t* src = q_t + (size_t)head * D + 8 * g;
-#pragma unroll
-      for (int s = 0; s < S; ++s) qa[s] = load_bf16x8(src + 32 * s);
-    } else {
-#pragma unroll
-      for (int s = 0; s < S; ++s) qa[s] = zero_bf16x8();
-    }
+    // head-list reads first, then the loads (see ScorerMfma32::init)
+    int wsel[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       int rs = 4 * g + r;
-      wr[r] = rs < h_use ? w_t[heads_t ? heads_t[rs] : rs] : 0.f;
+      wsel[r] = rs < h_use ? (heads_t ? heads_t[rs] : rs) : -1;
     }
+    const int qsel = m < h_use ? (heads_t ? heads_t[m] : m) : -1;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) wr[r] = wsel[r] >= 0 ? w_t[wsel[r]] : 0.f;
+    const uint16_t* src = q_t + (size_t)(qsel >= 0 ? qsel : 0) * D + 8 * g;
+#pragma unroll
+    for (int s = 0; s < S; ++s) qa[s] = qsel >= 0 ? load_bf16x8(src + 32 * s) : zero_bf16x8();
   }
 
   DSA_DEVICE static void load(Frag& b, const uint16_t* const* rows) {

@@ -183,20 +183,21 @@ __global__ __launch_bounds__(kNT) void k_score_emit(SelArgs a) {
   }
   SC sc;
   sc.init(q_t, w_t, heads_t, a.h_use, sc_lds);
-  for (int i = threadIdx.x; i < kBins; i += kNT) hist[i] = 0;   // counted after the loop
-  __syncthreads();
-
   const int64_t i0 = (int64_t)c * a.chunk;
   const int n_c = (int)((r.n_items - i0) < a.chunk ? (r.n_items - i0) : a.chunk);
   const int n_tiles = (n_c + 31) / 32;
   const int wv = wave_id();
   {
     // three tile fragments in rotation: while one tile is scored, the wave's
-    // next two tiles are in flight
+    // next two tiles are in flight.  The first two are requested before the
+    // histogram clear and the barrier (they read no LDS), so their latency
+    // overlaps the query loads'.
     typename SC::Frag fa, fb, fc;
     int tile = wv;
     if (tile < n_tiles) load_tile<SC, MODE>(a, t, r, i0, n_c, tile, fa);
     if (tile + kNW < n_tiles) load_tile<SC, MODE>(a, t, r, i0, n_c, tile + kNW, fb);
+    for (int i = threadIdx.x; i < kBins; i += kNT) hist[i] = 0;   // counted after the loop
+    __syncthreads();
     for (; tile < n_tiles; tile += 3 * kNW) {
       const int t1 = tile + kNW, t2 = tile + 2 * kNW, t3 = tile + 3 * kNW, t4 = tile + 4 * kNW;
       if (t2 < n_tiles) load_tile<SC, MODE>(a, t, r, i0, n_c, t2, fc);
