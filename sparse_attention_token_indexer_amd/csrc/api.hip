@@ -223,10 +223,14 @@ struct PrefillPlan {
   size_t scores = 0, rowmeta = 0, total = 0;
 };
 
+// score rows span whole 128-key stages (the scorers store every key of a
+// row's last stage); one spare row takes the stores of rows that are not scored
+int64_t prefill_row_stride(int64_t l_max) { return (l_max + 127) & ~(int64_t)127; }
+
 PrefillPlan plan_prefill(int64_t nq, int64_t l_max) {
   PrefillPlan p;
   Arena A;
-  p.scores = A.take((size_t)nq * ((l_max + 3) & ~(int64_t)3) * 4);
+  p.scores = A.take((size_t)(nq + 1) * prefill_row_stride(l_max) * 4);
   p.rowmeta = A.take((size_t)nq * 16);
   p.total = A.off;
   return p;
@@ -368,9 +372,7 @@ MisaPrefillPlan plan_misa_prefill(int64_t nq, int n_heads, int head_dim, int n_s
   p.heads = A.take((size_t)nq * dsa::kRoutedMaxHeads * 4);
   p.prefix = A.take((size_t)l_max * head_dim * 2);
   if (!pooled_given) p.pooled = A.take((size_t)n_seq * p.m_max * head_dim * 2);
-  // whole 128-key stages per row (the routed scorer stores every key of its
-  // last stage) plus one spare row for rows that are not scored
-  p.row_stride = (l_max + 127) & ~(int64_t)127;
+  p.row_stride = prefill_row_stride(l_max);
   p.scores = A.take((size_t)(nq + 1) * p.row_stride * 4);
   p.rowmeta = A.take((size_t)nq * 16);
   p.total = A.off;
@@ -550,8 +552,9 @@ int indexer_score_topk(const void* q, const float* w, const void* k, int32_t dty
     pa.head_dim = head_dim;
     pa.top_k = top_k;
     pa.l_max = l_max;
-    pa.row_stride = (l_max + 3) & ~(int64_t)3;
+    pa.row_stride = prefill_row_stride(l_max);
     pa.scores = at<float>(workspace, pp.scores);
+    pa.spare_row = pa.scores + (size_t)nq * pa.row_stride;
     pa.rowmeta = at<int32_t>(workspace, pp.rowmeta);
     pa.bin_bits = 12;                      // first-level bins of the dense rows
     pa.out_idx = out_idx;

@@ -88,6 +88,18 @@ DSA_DEVICE float weighted_relu_sum(const f32x16 (&acc)[HT], const float (&W)[HT]
   return p;
 }
 
+template <int N, class F, int... I>
+DSA_DEVICE void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+
+// f(integral_constant<0>) .. f(integral_constant<N-1>), in order (unrolled
+// steps whose register indices must be compile-time constants)
+template <int N, class F>
+DSA_DEVICE void static_for(F&& f) {
+  static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
+}
+
 // Wave-wide sum / exchange helpers (wave64).
 DSA_DEVICE float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
 

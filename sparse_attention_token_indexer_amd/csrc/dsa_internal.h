@@ -106,14 +106,14 @@ struct PrefillArgs {
   const int32_t* q_pos;        // [nq]
   int nq, n_heads, head_dim, top_k;
   int64_t l_max;
-  int64_t row_stride;          // floats per score row (l_max rounded up to 4)
+  int64_t row_stride;          // floats per score row (l_max rounded up to 128)
   float* scores;               // [nq, row_stride] workspace (only u <= pos written)
   int32_t* rowmeta;            // [nq, 4] workspace: threshold bin, count above, count in bin
   int bin_bits;                // first-level histogram bits (12 dense, 10 routed)
   const int32_t* heads;        // routed pass: [nq, heads_stride] head ids (first h_use used)
   int heads_stride, h_use;
-  float* spare_row;            // routed pass: [row_stride] scratch row taking the stores of
-                               // unscored rows (row_stride a multiple of 128 there)
+  float* spare_row;            // [row_stride] scratch row taking the stores of rows that are
+                               // not scored
   int32_t* out_idx;
   float* out_score;
 };

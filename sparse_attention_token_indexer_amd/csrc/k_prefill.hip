@@ -130,60 +130,45 @@ __global__ __launch_bounds__(64 * ROWS) void k_prefill_score(PrefillArgs a) {
       fetch_piece(j, st + 1);
     }
   };
-  // B operands of the sub-tile at `sub` of a stage
-  auto load_b = [&](bf16x8 (&b)[S], const uint8_t* tile, int sub) {
-#pragma unroll
-    for (int s = 0; s < S; ++s)
-      b[s] = __builtin_bit_cast(bf16x8,
-                                *reinterpret_cast<const u32x4*>(tile + boff + sub * 32 * LB + s * 32));
-  };
-  auto mfma = [&](f32x16 (&acc)[HT], const bf16x8 (&b)[S]) {
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[ht][r] = 0.f;
-#pragma unroll
-    for (int s = 0; s < S; ++s)
-#pragma unroll
-      for (int ht = 0; ht < HT; ++ht)
-        acc[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ht][s], b[s], acc[ht], 0, 0, 0);
-  };
-  // partial score of this lane's heads for key column m
-  auto epi = [&](const f32x16 (&acc)[HT]) {
-    return weighted_relu_sum<HT>(acc, W, std::make_integer_sequence<int, 16>{});
-  };
-  float* srow = a.scores + (size_t)(t < a.nq ? t : 0) * (size_t)a.row_stride;
+  // Finish of a pair of 32-key sub-tiles (keys key0 .. key0+63): one lane-half
+  // swap of the two sub-tiles' partials puts key key0 + l in lane l, and the
+  // two lane halves' partials of a key meet in one add.  Branch-free: every
+  // lane stores (score rows span whole stages; a row that is not scored writes
+  // the spare row) and keys past the row's position add 0 to the histogram.
+  // Histogram bin b counts in word b % 2048: low half for b < 2048 (negative
+  // scores, key bit 31 clear), high half otherwise.
+  const int pos_u = __builtin_amdgcn_readfirstlane(pos);
+  uint8_t* srow = reinterpret_cast<uint8_t*>(
+      pos_u >= 0 ? a.scores + (size_t)__builtin_amdgcn_readfirstlane(t) * (size_t)a.row_stride
+                 : a.spare_row);
   uint32_t* hrow = hist + wv * (kPBins / 2);
-  // sub-tiles A = keys key0..key0+31 and B = key0+32..key0+63: lanes 0..31 get
-  // A's key l, lanes 32..63 B's key l-32, and the two lane halves' partials of
-  // one key meet in one add.  The score is counted in the row's histogram here
-  // and stored later (see below).
-  auto score_pair = [&](int key0, float pa, float pb) {
+  float fin_sc = 0.f;
+  auto fin_store = [&](int key0, float pa, float pb) {
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(pa), __float_as_uint(pb),
                                                      false, false);
-    const float sc = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    if (key0 + lane <= pos) {
-      const uint32_t bin = fast_key(sc) >> kPBinShift;
-      atomicAdd(hrow + (bin >> 1), 1u << ((bin & 1u) * 16));
-    }
-    return sc;
+    fin_sc = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    *reinterpret_cast<float*>(srow + (uint32_t)(key0 + lane) * 4u) = fin_sc;
   };
-  auto store_pair = [&](int key0, float sc) {
-    if (key0 + lane <= pos) srow[key0 + lane] = sc;
+  auto fin_count = [&](int key0) {
+    const uint32_t word = (fast_key(fin_sc) >> kPBinShift) & (kPBins / 2 - 1);
+    const uint32_t inc =
+        key0 + lane <= pos_u ? ((int32_t)__float_as_uint(fin_sc) < 0 ? 1u : 0x10000u) : 0u;
+    atomicAdd(hrow + word, inc);
   };
 
-  // Software pipeline over the workgroup's 32-key sub-tiles (the same count for
-  // every wave; keys past a row's position are computed and dropped): sub-tile
-  // j's operands are read one sub-tile ahead, and its epilogue runs under the
-  // MFMAs of sub-tile j+1.  The barrier that publishes stage st+1 sits in
-  // sub-tile 2 of stage st, after every wave has read its last operands of
-  // stage st-1 (whose buffer stage st+1 reuses), so sub-tile 3 can already
-  // read stage st+1.  Stage st+1 is stored in four slots spread over the
-  // sub-tiles before that barrier (sub-tile 3 of stage st-1, sub-tiles 0-2 of
-  // stage st), each slot a full stage after the global loads it stores.
-  // Loads and stores share one completion counter, so a store-slot wait also
-  // covers every score store issued before it: both pairs' score stores go
-  // out together right after the barrier.
+  // Software pipeline over 32-key sub-tiles c = 0..3 of each 128-key stage
+  // (the same count for every wave; keys past a row's position are computed
+  // and dropped).  The sub-tile's S k-steps are S fenced steps; step s issues
+  // both head tiles' MFMAs for k-step s (B operands read one sub-tile
+  // earlier), reads the next sub-tile's B operand for k-step s, and adds 32 / S
+  // accumulator registers of the previous sub-tile to its partial pe[c - 1].
+  // Pair (0,1) of a stage is finished in its sub-tile 3, pair (2,3) in the next
+  // stage's sub-tile 1 (store in one step, count in the next).  One
+  // stage-loading slot per sub-tile; the barrier that publishes stage st+1
+  // closes sub-tile 2 of stage st, after every wave has read its last operands
+  // of stage st (whose buffer stage st+2 reuses), so sub-tile 3 can already
+  // read stage st+1.  Each slot stores its pieces a full stage after their
+  // global loads.
 #pragma unroll
   for (int j = 0; j < LOADS; ++j) fetch_piece(j, 0);
 #pragma unroll
@@ -192,45 +177,65 @@ __global__ __launch_bounds__(64 * ROWS) void k_prefill_score(PrefillArgs a) {
   for (int j = 0; j < LOADS; ++j) fetch_piece(j, 1);
   slot(0, 1);
   __syncthreads();
-  bf16x8 b0[S], b1[S];
-  f32x16 accx[HT], accy[HT];
-  float pe = 0.f, sc_prev = 0.f;
-  load_b(b0, ktile, 0);
-  for (int st = 0; st < n_stages; ++st) {
-    const uint8_t* tile = ktile + (st & 1) * STAGE;
-    const int k0 = st * kStageKeys;
-    // (the scheduling fences keep each step's loads, MFMAs and epilogue
-    // together, so no operand set is loaded more than one step ahead)
-    load_b(b1, tile, 1);
-    mfma(accx, b0);
-    if (st > 0) sc_prev = score_pair(k0 - 64, pe, epi(accy));
-    slot(1, st + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    load_b(b0, tile, 2);
-    mfma(accy, b1);
-    pe = epi(accx);
-    slot(2, st + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    load_b(b1, tile, 3);
-    mfma(accx, b0);
-    slot(3, st + 1);
-    __syncthreads();
-    __builtin_amdgcn_sched_barrier(0);
-    {
-      const float sc = score_pair(k0, pe, epi(accy));
-      if (st > 0) store_pair(k0 - 64, sc_prev);
-      store_pair(k0, sc);
+  bf16x8 bb[S];
+  f32x16 acc[2][HT];
+  float pe[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+    bb[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ktile + boff + s * 32));
+  constexpr int EPR = 16 * HT / S;             // epilogue registers per step
+  auto step = [&](auto C, auto SS, int st, bool live) {
+    constexpr int c = decltype(C)::value, s = decltype(SS)::value;
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      if constexpr (s == 0) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[c & 1][ht][r] = 0.f;
+      }
+      acc[c & 1][ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ht][s], bb[s], acc[c & 1][ht], 0, 0, 0);
     }
-    load_b(b0, ktile + ((st + 1) & 1) * STAGE, 0);
+    {
+      const uint8_t* nt = ktile + ((c == 3 ? st + 1 : st) & 1) * STAGE;
+      constexpr int nsub = (c + 1) & 3;
+      bb[s] = __builtin_bit_cast(bf16x8,
+                                 *reinterpret_cast<const u32x4*>(nt + boff + nsub * 32 * LB + s * 32));
+    }
+    if (c != 0 || live) {
+      float& p = pe[(c + 3) & 3];
+      if constexpr (s == 0) p = 0.f;
+      static_for<EPR>([&](auto I) {
+        constexpr int i = s * EPR + decltype(I)::value;
+        p = fmac_rowbcast<i & 15>(p, W[i >> 4], relu(acc[(c + 1) & 1][i >> 4][i & 15]));
+      });
+    }
+    constexpr int fs = 1, fc = S >= 8 ? 2 : 1;   // steps of the finish's store and count
+    if constexpr (c == 3) {
+      if constexpr (s == fs) fin_store(st * kStageKeys, pe[0], pe[1]);
+      if constexpr (s == fc) fin_count(st * kStageKeys);
+    }
+    if constexpr (c == 1) {
+      if (live) {
+        if constexpr (s == fs) fin_store((st - 1) * kStageKeys + 64, pe[2], pe[3]);
+        if constexpr (s == fc) fin_count((st - 1) * kStageKeys + 64);
+      }
+    }
+    if constexpr (s == S - 2) slot((c + 1) & 3, c == 3 ? st + 2 : st + 1);
+    if constexpr (c == 2 && s == S - 1) __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
-    mfma(accy, b1);
-    pe = epi(accx);
-    slot(0, st + 2);
-    __builtin_amdgcn_sched_barrier(0);
+  };
+  for (int st = 0; st < n_stages; ++st) {
+    const bool live = st > 0;
+    static_for<S>([&](auto SS) { step(std::integral_constant<int, 0>{}, SS, st, live); });
+    static_for<S>([&](auto SS) { step(std::integral_constant<int, 1>{}, SS, st, live); });
+    static_for<S>([&](auto SS) { step(std::integral_constant<int, 2>{}, SS, st, live); });
+    static_for<S>([&](auto SS) { step(std::integral_constant<int, 3>{}, SS, st, live); });
   }
+  // drain: the last sub-tile's epilogue, then pair (2,3) of the last stage
   {
-    const int k_last = n_stages * kStageKeys - 64;
-    store_pair(k_last, score_pair(k_last, pe, epi(accy)));
+    pe[3] = weighted_relu_sum<HT>(acc[1], W, std::make_integer_sequence<int, 16>{});
+    const int k_last = (n_stages - 1) * kStageKeys + 64;
+    fin_store(k_last, pe[2], pe[3]);
+    fin_count(k_last);
   }
 
   // this row's threshold: the 12-bit bin holding its k-th score
@@ -243,11 +248,10 @@ __global__ __launch_bounds__(64 * ROWS) void k_prefill_score(PrefillArgs a) {
   // lane l owns bins [kPBins - PER (l + 1), kPBins - PER l), counted from the top
   constexpr int PER = kPBins / 64;
   const int b_hi = kPBins - PER * lane;         // exclusive
+  const int sh = 16 * ((b_hi - 1) / (kPBins / 2));   // all in one half of the words
+  const int w0 = (b_hi - PER) & (kPBins / 2 - 1);
   uint32_t mine = 0;
-  for (int wd = (b_hi - PER) / 2; wd < b_hi / 2; ++wd) {
-    const uint32_t v = hrow[wd];
-    mine += (v & 0xFFFFu) + (v >> 16);
-  }
+  for (int i = 0; i < PER; ++i) mine += (hrow[w0 + i] >> sh) & 0xFFFFu;
   uint32_t incl = mine;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -258,7 +262,7 @@ __global__ __launch_bounds__(64 * ROWS) void k_prefill_score(PrefillArgs a) {
   if (before < need && incl >= need) {
     uint32_t accum = before;
     for (int b = b_hi - 1; b >= b_hi - PER; --b) {
-      const uint32_t c = (hrow[b >> 1] >> ((b & 1) * 16)) & 0xFFFFu;
+      const uint32_t c = (hrow[b & (kPBins / 2 - 1)] >> sh) & 0xFFFFu;
       if (accum + c >= need) {
         meta[0] = b;
         meta[1] = (int32_t)accum;
@@ -424,6 +428,8 @@ hipError_t launch_score_t(const PrefillArgs& a, hipStream_t stream) {
 
 hipError_t launch_prefill_score(const PrefillArgs& a, hipStream_t stream) {
   if (a.nq <= 0) return hipSuccess;
+  // every key of a row's last stage is stored: rows span whole stages
+  if (a.row_stride % kStageKeys != 0 || a.row_stride < a.l_max || !a.spare_row) return hipErrorInvalidValue;
   if (a.head_dim == 128) return a.n_heads <= 32 ? launch_score_t<1, 128>(a, stream)
                                                 : launch_score_t<2, 128>(a, stream);
   if (a.head_dim == 64) return a.n_heads <= 32 ? launch_score_t<1, 64>(a, stream)

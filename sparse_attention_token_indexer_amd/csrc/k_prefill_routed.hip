@@ -55,17 +55,6 @@ DSA_DEVICE void epi_regs(f32x4& p, const f32x16& acc, float W) {
   epi_seq<R0>(p, acc, W, std::make_integer_sequence<int, N>{});
 }
 
-template <int N, class F, int... I>
-DSA_DEVICE void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-
-// f(integral_constant<0>) .. f(integral_constant<N-1>), in order
-template <int N, class F>
-DSA_DEVICE void static_for(F&& f) {
-  static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
-}
-
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_prefill_routed_score(PrefillArgs a) {
   constexpr int S = D / 16;

@@ -204,17 +204,6 @@ constexpr size_t prefill_route_lds() {
   return stages > red ? stages : red;
 }
 
-template <int N, class F, int... I>
-DSA_DEVICE void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-
-// f(integral_constant<0>) .. f(integral_constant<N-1>), in order
-template <int N, class F>
-DSA_DEVICE void static_for(F&& f) {
-  static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
-}
-
 template <int HT, int D>
 // (two workgroups per CU: at most 256 registers per lane)
 __global__ __launch_bounds__(64 * kPRRows) __attribute__((amdgpu_waves_per_eu(2)))
