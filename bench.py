@@ -35,7 +35,7 @@ CSRC = os.path.join(ROOT, "sparse_attention_token_indexer_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 WORKLOADS = {"dense_decode": 2, "tiny": 1, "dense_prefill": 3, "misa": 4, "misa_dagger": 4,
-             "hisa": 5, "pool": 4, "misa_prefill": 3}
+             "hisa": 5, "pool": 4, "misa_prefill": 3, "hisa_prefill": 3}
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
 
 
@@ -44,7 +44,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
 KERNEL_SOURCE = {"dense_decode": "k_score_select.hip", "tiny": "k_score_select.hip",
                  "misa": "k_score_select.hip", "misa_dagger": "k_score_select.hip",
                  "hisa": "k_score_select.hip", "dense_prefill": "k_prefill.hip",
-                 "misa_prefill": "k_prefill_routed.hip", "pool": "k_pool.hip"}
+                 "misa_prefill": "k_prefill_routed.hip", "pool": "k_pool.hip",
+                 "hisa_prefill": "k_score_select.hip"}
 
 
 def kernel_source_hash(workload: str) -> str:
@@ -117,7 +118,7 @@ def cpu_baseline(wl, seed, seconds: float, mode: str):
     done_pairs, spent, nq_done = 0, 0.0, 0
     order = range(wl.nq)
     cache = {}
-    if mode == "dense_prefill":   # rows spread over the causal triangle
+    if mode in ("dense_prefill", "misa_prefill", "hisa_prefill"):   # rows spread over the triangle
         order = np.random.default_rng(seed).permutation(wl.nq)
     for t in order:
         s_id = int(q_seq[t])
@@ -135,6 +136,10 @@ def cpu_baseline(wl, seed, seconds: float, mode: str):
             O.misa_dagger_row(q_t, w_t, K, p, wl.block, wl.n_active_heads, wl.k_prime, wl.top_k)
         elif mode == "hisa":
             O.hisa_row(q_t, w_t, K, p, wl.block, wl.m_blocks, wl.top_k)
+        elif mode == "misa_prefill":
+            O.misa_row(q_t, w_t, K, p, 64, 8, wl.top_k)
+        elif mode == "hisa_prefill":
+            O.hisa_row(q_t, w_t, K, p, 128, 64, wl.top_k)
         else:
             O.dense_row(q_t, w_t, K, p, wl.top_k)
         spent += time.perf_counter() - t0
@@ -280,6 +285,27 @@ def main() -> int:
         call_bytes = wl.n_seq * M * d * 2 + nq * wl.m_blocks * wl.block * d * eb + io_bytes
         call_flops = nq * M * H * d * 2 + nq * wl.m_blocks * wl.block * H * d * 2
         bound_note = "HBM: gathers the keys of the m surviving blocks"
+    elif name == "hisa_prefill":
+        B, m = 128, 64
+        kp = dsa.indexer_mean_pool_keys(k, B)
+        nbytes = dsa.hisa_block_filter_topk_workspace_size(nq, H, d, wl.n_seq, L, B, m, topk, 1)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+
+        def step():
+            dsa.hisa_block_filter_topk(q, w, k, q_pos, None, block=B, m_blocks=m, top_k=topk,
+                                       k_pooled=kp, with_blocks=False, out_idx=out_i,
+                                       out_score=out_s, workspace=ws)
+        kind = "score_blocks"
+        kernel_bytes = None
+        p1 = pos_np.astype(np.int64) + 1
+        tokens = int(np.minimum(p1, m * B).sum())          # candidate tokens (at most m blocks)
+        blocks = int(((p1 + B - 1) // B).sum())             # causal pooled blocks
+        kernel_flops = tokens * H * d * 2
+        call_bytes = nq * H * d * eb + L * d * eb + -(-L // B) * d * 2 + nq * H * 4 + nq * topk * 8
+        call_flops = blocks * H * d * 2 + kernel_flops
+        bound_note = ("MFMA: the head contraction over each row's m surviving blocks (keys "
+                      "re-gathered per row from L2 and the last-level cache)")
+        extra["filter"] = {"block": B, "m_blocks": m}
     elif name == "pool":
         M = -(-L // wl.block)
         kp = torch.empty((wl.n_seq, M, d), dtype=torch.bfloat16, device=dev)
@@ -404,7 +430,8 @@ def main() -> int:
         "data": "synthetic (seeded; planted-key recipe of the workload)",
         "config": {"workload": {"misa_dagger": "misa_dagger_decode_L128K_H64_h8_kp8192",
                                 "pool": "mean_pool_L128K_B64",
-                                "misa_prefill": "misa_prefill_L32K_H64_h8"}.get(name, wl.name),
+                                "misa_prefill": "misa_prefill_L32K_H64_h8",
+                                "hisa_prefill": "hisa_prefill_L32K_H64_B128_m64"}.get(name, wl.name),
                    "queries": nq, "l_max": L, "n_heads": H, "head_dim": d,
                    "top_k": topk, "causal_pairs": pairs, "parallelism": "single GPU",
                    **({"block": wl.block} if wl.block else {}),

@@ -221,6 +221,18 @@ def test_hisa_partial_blocks_and_internal_pooling(dsa):
         _hisa_case(dsa, wl, m=8, k=200, pos=pos, pooled=pooled)
 
 
+def test_hisa_prefill_rows(dsa):
+    """HISA on the prefill layout: many rows of one sequence at positions
+    0..nq-1, so early rows keep every block (fewer than m), rows end inside a
+    block (partial last block pooled over the row's tokens), and rows with
+    fewer than k candidate tokens are padded."""
+    wl = datagen.small(5, nq=1024, n_seq=1, l_max=1024, layout="prefill", plant="points",
+                       n_plant=128, block=64)
+    rows = list(range(0, 1024, 37)) + [63, 64, 65, 1023]
+    _hisa_case(dsa, wl, m=6, k=200, rows=rows)
+    _hisa_case(dsa, wl, m=3, k=64, seed=1, rows=rows, pooled=False)
+
+
 def test_hisa_all_blocks_equals_dense_and_iou(dsa):
     """m >= M keeps every block, so HISA equals dense; with m < M the IoU kernel
     agrees with the oracle's IoU of the same two selections."""
