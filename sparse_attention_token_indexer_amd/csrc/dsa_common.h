@@ -100,6 +100,21 @@ DSA_DEVICE void static_for(F&& f) {
   static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave by DPP: shifts by 1, 2, 4
+// and 8 lanes within each 16-lane row, then row 0's total added into row 1 and
+// row 2's into row 3 (row_bcast:15), then rows 0-1's into rows 2-3
+// (row_bcast:31).  Lanes whose source is outside the row read 0.
+DSA_DEVICE uint32_t wave_incl_scan(uint32_t x) {
+  int v = (int)x;
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15, rows 1 and 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31, rows 2 and 3
+  return (uint32_t)v;
+}
+
 // Wave-wide sum / exchange helpers (wave64).
 DSA_DEVICE float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
 

@@ -327,36 +327,90 @@ __global__ __launch_bounds__(kST) void k_prefill_select(PrefillArgs a) {
   __syncthreads();
   const Emitter em{out_i, out_s, &s_out, Kt};
   constexpr int kSub = kFBShift - 10;          // the 10 key bits below the first level
-  // one pass over the row (16-byte loads): emit every score above the bin,
-  // collect the bin itself.  The loads are unconditional (clamped to the
-  // row's last piece, masked afterwards) so that all of them are in flight
-  // together.  Keys are formed as in the scoring kernel's histogram (the
-  // stored scores are never -0.0).
+  const int lane = lane_id();
+  // Passes over the row (16-byte loads, U per thread in flight): the loads are
+  // unconditional (clamped to the row's last piece, masked afterwards) so that
+  // all of them are in flight together.  Keys are formed as in the scoring
+  // kernel's histogram (the stored scores are never -0.0).  Each thread flags
+  // its 4U scores of an iteration in two masks (emitted now / kept in the LDS
+  // list); one wave scan of the packed counts and one LDS atomic per wave
+  // reserve consecutive slots, and each lane writes its flagged scores there.
   constexpr int U = 4;
   const uint32_t n4 = (n + 3) / 4;
-  for (uint32_t base = 0; base < n4; base += kST * U) {
-    f32x4 v[U];
+  auto load_iter = [&](uint32_t base, f32x4 (&v)[U]) {
 #pragma unroll
     for (int j = 0; j < U; ++j) {
       const uint32_t i4 = base + threadIdx.x + j * kST;
       v[j] = *reinterpret_cast<const f32x4*>(sc + 4 * (size_t)(i4 < n4 ? i4 : n4 - 1));
     }
     __builtin_amdgcn_sched_barrier(0);             // issue every load first
+  };
+  auto append = [&](uint32_t base, const f32x4 (&v)[U], uint32_t take_m, uint32_t keep_m,
+                    uint32_t kcap) {
+    const uint32_t packed = (uint32_t)__builtin_popcount(take_m) |
+                            ((uint32_t)__builtin_popcount(keep_m) << 16);
+    const uint32_t incl = wave_incl_scan(packed);
+    const uint32_t tot = __builtin_amdgcn_readlane(incl, 63);
+    if (tot == 0) return;                          // wave-uniform
+    uint32_t bt = 0, bk = 0;
+    if (lane == 63) {
+      if (tot & 0xFFFFu) bt = atomicAdd(&s_out, tot & 0xFFFFu);
+      if (tot >> 16) bk = atomicAdd(&s_ln, tot >> 16);
+    }
+    const uint32_t excl = incl - packed;
+    uint32_t o = __builtin_amdgcn_readlane(bt, 63) + (excl & 0xFFFFu);
+    uint32_t l = __builtin_amdgcn_readlane(bk, 63) + (excl >> 16);
 #pragma unroll
     for (int j = 0; j < U; ++j) {
-      const uint32_t i4 = base + threadIdx.x + j * kST;
+      const uint32_t u0 = 4 * (base + threadIdx.x + j * kST);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint32_t u = 4 * i4 + e;
-        const bool ok = i4 < n4 && u < n;
-        const uint32_t key = ok ? fast_key(v[j][e]) : 0u;
-        const int b = ok ? (int)(key >> kFBShift) : -1;
-        em.put_wave(b > bstar, key, (int32_t)u);
-        if (fits) list_put_wave(b == bstar, make_uint2(key, u), list, &s_ln, kSelListCap);
-        else if (b == bstar) atomicAdd(&hist[(key >> kSub) & 1023u], 1u);
+        const int bit = 4 * j + e;
+        if ((take_m >> bit) & 1u) {
+          if (o < Kt) {
+            out_i[o] = (int32_t)(u0 + e);
+            if (out_s) out_s[o] = v[j][e];
+          }
+          ++o;
+        }
+        if ((keep_m >> bit) & 1u) {
+          if (l < kcap) list[l] = make_uint2(fast_key(v[j][e]), u0 + e);
+          ++l;
+        }
       }
     }
-  }
+  };
+  // first pass: emit every score above the bin, collect the bin (or, when it
+  // overflows the list, count its next 10-bit digit).  Iterations wholly
+  // inside the row skip the end-of-row masks; the path is fixed per row.
+  const uint32_t n_whole = n / (4 * kST * U) * (kST * U);   // in 16-byte pieces
+  auto pass1_iter = [&](uint32_t base, auto MASKED, auto FITS) {
+    constexpr bool kMasked = decltype(MASKED)::value, kFits = decltype(FITS)::value;
+    f32x4 v[U];
+    load_iter(base, v);
+    uint32_t take_m = 0, keep_m = 0;
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t u = 4 * (base + threadIdx.x + j * kST) + e;
+        const bool ok = !kMasked || u < n;
+        const uint32_t key = fast_key(v[j][e]);
+        const int b = (int)(key >> kFBShift);
+        take_m |= (uint32_t)(ok && b > bstar) << (4 * j + e);
+        if constexpr (kFits) keep_m |= (uint32_t)(ok && b == bstar) << (4 * j + e);
+        else if (ok && b == bstar) atomicAdd(&hist[(key >> kSub) & 1023u], 1u);
+      }
+    }
+    append(base, v, take_m, keep_m, kSelListCap);
+  };
+  auto pass1 = [&](auto FITS) {
+    uint32_t base = 0;
+    for (; base < n_whole; base += kST * U) pass1_iter(base, std::false_type{}, FITS);
+    for (; base < n4; base += kST * U) pass1_iter(base, std::true_type{}, FITS);
+  };
+  if (fits) pass1(std::true_type{});
+  else pass1(std::false_type{});
   __syncthreads();
   const uint32_t need = Kt - above;
   if (fits) {
@@ -376,12 +430,8 @@ __global__ __launch_bounds__(kST) void k_prefill_select(PrefillArgs a) {
   const bool fits2 = nd2 <= kSelListCap;
   for (uint32_t base = 0; base < n4; base += kST * U) {
     f32x4 v[U];
-#pragma unroll
-    for (int j = 0; j < U; ++j) {
-      const uint32_t i4 = base + threadIdx.x + j * kST;
-      v[j] = *reinterpret_cast<const f32x4*>(sc + 4 * (size_t)(i4 < n4 ? i4 : n4 - 1));
-    }
-    __builtin_amdgcn_sched_barrier(0);
+    load_iter(base, v);
+    uint32_t take_m = 0, keep_m = 0;
 #pragma unroll
     for (int j = 0; j < U; ++j) {
       const uint32_t i4 = base + threadIdx.x + j * kST;
@@ -392,10 +442,11 @@ __global__ __launch_bounds__(kST) void k_prefill_select(PrefillArgs a) {
         const uint32_t key = ok ? fast_key(v[j][e]) : 0u;
         const bool in_bin = ok && (int)(key >> kFBShift) == bstar;
         const int sub = (int)((key >> kSub) & 1023u);
-        em.put_wave(in_bin && sub > d2, key, (int32_t)u);
-        if (fits2) list_put_wave(in_bin && sub == d2, make_uint2(key, u), list, &s_ln, kSelListCap);
+        take_m |= (uint32_t)(in_bin && sub > d2) << (4 * j + e);
+        if (fits2) keep_m |= (uint32_t)(in_bin && sub == d2) << (4 * j + e);
       }
     }
+    append(base, v, take_m, keep_m, kSelListCap);
   }
   __syncthreads();
   const uint64_t prefix = ((uint64_t)bstar << (64 - FB)) | ((uint64_t)d2 << (64 - FB - 10));
