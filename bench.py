@@ -43,9 +43,9 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
 # header's, identifies the build that traffic counters were taken on)
 KERNEL_SOURCE = {"dense_decode": "k_score_select.hip", "tiny": "k_score_select.hip",
                  "misa": "k_score_select.hip", "misa_dagger": "k_score_select.hip",
-                 "hisa": "k_score_select.hip", "dense_prefill": "k_prefill.hip",
+                 "hisa": "k_hisa.hip", "dense_prefill": "k_prefill.hip",
                  "misa_prefill": "k_prefill_routed.hip", "pool": "k_pool.hip",
-                 "hisa_prefill": "k_score_select.hip"}
+                 "hisa_prefill": "k_hisa.hip"}
 
 
 def kernel_source_hash(workload: str) -> str:
@@ -279,12 +279,13 @@ def main() -> int:
             dsa.hisa_block_filter_topk(q, w, k, q_pos, q_seq, block=wl.block, m_blocks=wl.m_blocks,
                                        top_k=topk, k_pooled=kp, with_blocks=False, out_idx=out_i,
                                        out_score=out_s, workspace=ws)
-        kind = "score_blocks"
-        kernel_bytes = nq * wl.m_blocks * wl.block * d * eb + nq * wl.m_blocks * 4 + io_bytes
+        kind = "hisa"
         M = -(-L // wl.block)
         call_bytes = wl.n_seq * M * d * 2 + nq * wl.m_blocks * wl.block * d * eb + io_bytes
         call_flops = nq * M * H * d * 2 + nq * wl.m_blocks * wl.block * H * d * 2
-        bound_note = "HBM: gathers the keys of the m surviving blocks"
+        kernel_bytes = call_bytes          # one kernel: block pass, top-m, token pass, top-k
+        bound_note = ("HBM: the pooled keys once and the keys of the m surviving blocks, in one "
+                      "kernel (block pass, top-m, token pass, top-k)")
     elif name == "hisa_prefill":
         B, m = 128, 64
         kp = dsa.indexer_mean_pool_keys(k, B)
@@ -295,16 +296,16 @@ def main() -> int:
             dsa.hisa_block_filter_topk(q, w, k, q_pos, None, block=B, m_blocks=m, top_k=topk,
                                        k_pooled=kp, with_blocks=False, out_idx=out_i,
                                        out_score=out_s, workspace=ws)
-        kind = "score_blocks"
+        kind = "hisa"
         kernel_bytes = None
         p1 = pos_np.astype(np.int64) + 1
         tokens = int(np.minimum(p1, m * B).sum())          # candidate tokens (at most m blocks)
         blocks = int(((p1 + B - 1) // B).sum())             # causal pooled blocks
-        kernel_flops = tokens * H * d * 2
         call_bytes = nq * H * d * eb + L * d * eb + -(-L // B) * d * 2 + nq * H * 4 + nq * topk * 8
-        call_flops = blocks * H * d * 2 + kernel_flops
-        bound_note = ("MFMA: the head contraction over each row's m surviving blocks (keys "
-                      "re-gathered per row from L2 and the last-level cache)")
+        call_flops = blocks * H * d * 2 + tokens * H * d * 2
+        kernel_flops = call_flops          # one kernel: block pass, top-m, token pass, top-k
+        bound_note = ("MFMA: the head contraction over each row's pooled blocks and then its m "
+                      "surviving blocks (keys re-gathered per row from L2 and the last-level cache)")
         extra["filter"] = {"block": B, "m_blocks": m}
     elif name == "pool":
         M = -(-L // wl.block)

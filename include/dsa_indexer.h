@@ -195,7 +195,8 @@ int indexer_selection_iou(const int32_t* a, const int32_t* b, int32_t nq, int32_
 #define DSA_KERNEL_MERGE 10       /* exact top-k merge after a score-and-emit kernel */
 #define DSA_KERNEL_ROUTE_HEADS 11 /* MISA head selection (prefill shape) */
 #define DSA_KERNEL_PREFILL_ROUTED 12 /* MISA routed scoring on the prefill shape */
-#define DSA_KERNEL_KINDS 13
+#define DSA_KERNEL_HISA 13        /* HISA in one kernel: blocks, top-m, tokens, top-k */
+#define DSA_KERNEL_KINDS 14
 int dsa_kernel_timing(int enable);
 int dsa_kernel_timing_read(int32_t kind, int64_t* launches, double* total_ms, double* min_ms,
                            double* max_ms);

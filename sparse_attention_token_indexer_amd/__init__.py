@@ -55,7 +55,7 @@ _SIGS = {
 KERNEL_KINDS = {
     "prepare": 0, "score_tokens": 1, "score_pooled": 2, "score_list": 3, "score_blocks": 4,
     "route": 5, "pool": 6, "iou": 7, "prefill": 8, "rowselect": 9, "merge": 10,
-    "route_heads": 11, "prefill_routed": 12,
+    "route_heads": 11, "prefill_routed": 12, "hisa": 13,
 }
 
 _lib: Optional[ctypes.CDLL] = None

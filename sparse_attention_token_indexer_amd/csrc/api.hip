@@ -312,6 +312,49 @@ HisaPlan plan_hisa(int64_t nq, int head_dim, int n_seq, int64_t l_max, int block
   return p;
 }
 
+// One-kernel HISA: G workgroups per query (about kTargetWorkgroups in all),
+// each taking ch1 pooled blocks and ch2 token items (both at most
+// kHisaMaxChunk, multiples of the 32-item tile).  The sync words and the
+// kept-block flags come first: the prepare kernel clears them.
+struct HisaFusedPlan {
+  bool ok = false;
+  int groups = 0, ch1 = 0, ch2 = 0, sblk_n = 0;
+  int64_t m_max = 0;
+  size_t zero_bytes = 0, sync = 0, bflag = 0, cand1 = 0, cnt1 = 0, keys2 = 0, blocks = 0;
+  size_t partial = 0, pooled = 0, total = 0;
+};
+
+HisaFusedPlan plan_hisa_fused(int64_t nq, int head_dim, int n_seq, int64_t l_max, int block, int m,
+                              bool pooled_given) {
+  HisaFusedPlan p;
+  p.m_max = cdiv(l_max, block);
+  const int64_t items = (int64_t)m * block;
+  int64_t g = cdiv(kTargetWorkgroups, nq);
+  if (g > dsa::kHisaMaxGroups) g = dsa::kHisaMaxGroups;
+  while (g < dsa::kHisaMaxGroups &&
+         (cdiv(p.m_max, g) > dsa::kHisaMaxChunk || cdiv(items, g) > dsa::kHisaMaxChunk))
+    g *= 2;
+  if (g > dsa::kHisaMaxGroups) g = dsa::kHisaMaxGroups;
+  p.ok = nq <= 65535 && m <= dsa::kHisaMaxBlocks && items <= dsa::kHisaRegKeys &&
+         cdiv(p.m_max, g) <= dsa::kHisaMaxChunk && cdiv(items, g) <= dsa::kHisaMaxChunk;
+  p.groups = (int)g;
+  p.ch1 = (int)(cdiv(cdiv(p.m_max, g), 32) * 32);
+  p.ch2 = (int)(cdiv(cdiv(items, g), 32) * 32);
+  p.sblk_n = p.ch2 / block + 2;
+  Arena A;
+  p.sync = A.take((size_t)nq * dsa::kHisaSyncWords * 4);
+  p.bflag = A.take((size_t)nq * m * 4);
+  p.zero_bytes = A.off;
+  p.cand1 = A.take((size_t)nq * g * p.ch1 * 8);
+  p.cnt1 = A.take((size_t)nq * g * 4);
+  p.keys2 = A.take((size_t)nq * g * p.ch2 * 4);
+  p.blocks = A.take((size_t)nq * m * 4);
+  p.partial = A.take((size_t)nq * head_dim * 2);
+  if (!pooled_given) p.pooled = A.take((size_t)n_seq * p.m_max * head_dim * 2);
+  p.total = A.off;
+  return p;
+}
+
 int run_prepare(void* ws, size_t zero_bytes, const void* k, const int32_t* q_seq,
                 const int32_t* q_pos, int nq, int n_seq, int head_dim, int block, int64_t l_max,
                 uint16_t* partial, hipStream_t stream) {
@@ -705,6 +748,8 @@ size_t hisa_block_filter_topk_workspace_size(int32_t nq, int32_t n_heads, int32_
                                              int32_t pooled_given) {
   (void)n_heads; (void)top_k;
   if (nq <= 0 || l_max <= 0 || block <= 0 || m_blocks <= 0) return 0;
+  HisaFusedPlan f = plan_hisa_fused(nq, head_dim, n_seq, l_max, block, m_blocks, pooled_given != 0);
+  if (f.ok) return f.total;
   return plan_hisa(nq, head_dim, n_seq, l_max, block, m_blocks, pooled_given != 0).total;
 }
 
@@ -722,6 +767,55 @@ int hisa_block_filter_topk(const void* q, const float* w, const void* k, const v
   if ((int64_t)m_blocks * block > 0x7FFFFFFF) return fail(DSA_EINVAL, "m_blocks * block too large");
   if (nq == 0) return DSA_OK;
   if (k_pooled && !aligned(k_pooled, 16)) return fail(DSA_EINVAL, "k_pooled must be 16-byte aligned");
+  HisaFusedPlan f = plan_hisa_fused(nq, head_dim, n_seq, l_max, block, m_blocks, k_pooled != nullptr);
+  if (f.ok) {
+    if ((st = check_ws(workspace, workspace_bytes, f.total))) return st;
+    const uint16_t* pooled = reinterpret_cast<const uint16_t*>(k_pooled);
+    if (!pooled) {
+      uint16_t* dst = at<uint16_t>(workspace, f.pooled);
+      st = hip_status(timed_pool(stream, [&] { return dsa::launch_mean_pool(reinterpret_cast<const uint16_t*>(k), n_seq, l_max,
+                                            head_dim, block, dst, stream); }),
+                      "mean-pool kernel", stream);
+      if (st) return st;
+      pooled = dst;
+    }
+    uint16_t* partial = at<uint16_t>(workspace, f.partial);
+    if ((st = run_prepare(workspace, f.zero_bytes, k, q_seq, q_pos, nq, n_seq, head_dim, block,
+                          l_max, partial, stream)))
+      return st;
+    dsa::HisaArgs h{};
+    h.q = reinterpret_cast<const uint16_t*>(q);
+    h.w = w;
+    h.keys = reinterpret_cast<const uint16_t*>(k);
+    h.pooled = pooled;
+    h.partial = partial;
+    h.q_seq = q_seq;
+    h.q_pos = q_pos;
+    h.nq = nq;
+    h.n_heads = n_heads;
+    h.head_dim = head_dim;
+    h.n_seq = n_seq;
+    h.block = block;
+    h.m_blocks = m_blocks;
+    h.top_k = top_k;
+    h.l_max = l_max;
+    h.m_max = f.m_max;
+    h.groups = f.groups;
+    h.ch1 = f.ch1;
+    h.ch2 = f.ch2;
+    h.sblk_n = f.sblk_n;
+    h.sync = at<uint32_t>(workspace, f.sync);
+    h.bflag = at<int32_t>(workspace, f.bflag);
+    h.cand1 = at<uint2>(workspace, f.cand1);
+    h.cnt1 = at<uint32_t>(workspace, f.cnt1);
+    h.keys2 = at<uint32_t>(workspace, f.keys2);
+    h.blocks = out_blocks ? out_blocks : at<int32_t>(workspace, f.blocks);
+    h.out_idx = out_idx;
+    h.out_score = out_score;
+    h.out_block_score = out_block_score;
+    return hip_status(timed(DSA_KERNEL_HISA, stream, [&] { return dsa::launch_hisa(h, stream); }),
+                      "HISA kernel", stream);
+  }
   HisaPlan p = plan_hisa(nq, head_dim, n_seq, l_max, block, m_blocks, k_pooled != nullptr);
   if ((st = check_ws(workspace, workspace_bytes, p.total))) return st;
   const uint16_t* pooled = reinterpret_cast<const uint16_t*>(k_pooled);
