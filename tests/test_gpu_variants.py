@@ -233,6 +233,43 @@ def test_hisa_prefill_rows(dsa):
     _hisa_case(dsa, wl, m=3, k=64, seed=1, rows=rows, pooled=False)
 
 
+def test_hisa_exact_ties_take_lowest_ids(dsa):
+    """Zero queries make every block and token score exactly 0.0, so both
+    selections are decided by the tie-break alone (lower index first): the
+    kept blocks are 0..m-1 and the tokens the k lowest of theirs.  With 4096
+    blocks per query (every block a candidate) and a tie bin holding every
+    token item, this runs the selection paths for candidate lists and tie
+    bins that do not fit in LDS; one query ends inside a block."""
+    n_seq, L, H, D, B, m, k = 4, 262144, 32, 128, 64, 64, 1000
+    pos = np.array([L - 1, L - 18, 100000, 5000], dtype=np.int32)
+    say(f"[hisa ties] nq={n_seq} L={L} H={H} B={B} m={m} k={k}")
+    g = torch.Generator(device="cuda").manual_seed(3)
+    q = torch.zeros((n_seq, H, D), dtype=torch.bfloat16, device="cuda")
+    w = torch.randn((n_seq, H), device="cuda", generator=g)
+    keys = torch.randn((n_seq, L, D), device="cuda", generator=g).to(torch.bfloat16)
+    res = dsa.hisa_block_filter_topk(q, w, keys, torch.from_numpy(pos).cuda(),
+                                     torch.arange(n_seq, dtype=torch.int32, device="cuda"),
+                                     block=B, m_blocks=m, top_k=k)
+    torch.cuda.synchronize()
+    out = {key: v.cpu().numpy() for key, v in res.items()}
+    errs = []
+    for t in range(n_seq):
+        M = (int(pos[t]) + B) // B
+        mb = min(m, M)
+        if sorted(out["blocks"][t][:mb].tolist()) != list(range(mb)):
+            errs.append(f"q{t}: blocks {sorted(out['blocks'][t][:mb].tolist())[:8]}...")
+        if np.any(out["block_score"][t][:mb] != 0.0):
+            errs.append(f"q{t}: block scores not all zero")
+        toks = np.arange(mb * B)
+        toks = toks[toks <= pos[t]]
+        kt = min(k, toks.size)
+        if sorted(out["idx"][t][:kt].tolist()) != toks[:kt].tolist():
+            errs.append(f"q{t}: tokens {sorted(out['idx'][t][:kt].tolist())[:8]}...")
+        if np.any(out["score"][t][:kt] != 0.0) or np.any(out["idx"][t][kt:] != -1):
+            errs.append(f"q{t}: token scores not zero or padding wrong")
+    assert not errs, "\n".join(errs)
+
+
 def test_hisa_all_blocks_equals_dense_and_iou(dsa):
     """m >= M keeps every block, so HISA equals dense; with m < M the IoU kernel
     agrees with the oracle's IoU of the same two selections."""
