@@ -48,10 +48,25 @@ KERNEL_SOURCE = {"dense_decode": "k_score_select.hip", "tiny": "k_score_select.h
                  "hisa_prefill": "k_hisa.hip"}
 
 
+def _local_sources(name: str) -> list:
+    """The source file and every header under csrc/ it includes, transitively."""
+    seen, todo = [], [name]
+    while todo:
+        f = todo.pop()
+        if f in seen or not os.path.exists(os.path.join(CSRC, f)):
+            continue
+        seen.append(f)
+        with open(os.path.join(CSRC, f)) as fh:
+            for line in fh:
+                line = line.strip()
+                if line.startswith('#include "'):
+                    todo.append(line.split('"')[1])
+    return sorted(seen)
+
+
 def kernel_source_hash(workload: str) -> str:
     h = hashlib.sha256()
-    files = [f for f in sorted(os.listdir(CSRC)) if f.endswith(".h")] + [KERNEL_SOURCE[workload]]
-    for f in files:
+    for f in _local_sources(KERNEL_SOURCE[workload]):
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]

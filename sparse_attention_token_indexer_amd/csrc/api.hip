@@ -9,6 +9,7 @@
 #include <string>
 #include <vector>
 
+#include "dsa_hisa.h"
 #include "dsa_internal.h"
 
 namespace {

@@ -27,6 +27,7 @@
 // fastest), so the query groups dispatched first can always finish and free
 // room for the rest.  The waits are also bounded in time: a query whose wait
 // times out is marked in its sync words and left incomplete.
+#include "dsa_hisa.h"
 #include "dsa_internal.h"
 #include "dsa_scorers.h"
 #include "dsa_select.h"
