@@ -2,6 +2,7 @@
 // Declarations and the contract of every entry point are in include/dsa_indexer.h.
 #include "../../include/dsa_indexer.h"
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -313,42 +314,60 @@ HisaPlan plan_hisa(int64_t nq, int head_dim, int n_seq, int64_t l_max, int block
   return p;
 }
 
-// One-kernel HISA: G workgroups per query (about kTargetWorkgroups in all),
-// each taking ch1 pooled blocks and ch2 token items (both at most
-// kHisaMaxChunk, multiples of the 32-item tile).  The sync words and the
-// kept-block flags come first: the prepare kernel clears them.
+// HISA kernels.  When one grid of G workgroups per query (about
+// kTargetWorkgroups in all) fits the chip at once, every workgroup takes part
+// in both passes: ch1 pooled blocks, then ch2 token items.  Otherwise (many
+// queries: prefill rows) the grid is split into block-pass items, all
+// dispatched first, and token-pass items, so that no workgroup waits for a
+// selection while occupying a slot that block-pass work still needs.  Chunks
+// are at most kHisaMaxChunk and multiples of the 32-item tile.  The sync
+// words and the kept-block flags come first: the prepare kernel clears them.
 struct HisaFusedPlan {
   bool ok = false;
-  int groups = 0, ch1 = 0, ch2 = 0, sblk_n = 0;
+  int split = 0, groups = 0, groups1 = 0, groups2 = 0, ch1 = 0, ch2 = 0, sblk_n = 0;
   int64_t m_max = 0;
   size_t zero_bytes = 0, sync = 0, bflag = 0, cand1 = 0, cnt1 = 0, keys2 = 0, blocks = 0;
   size_t partial = 0, pooled = 0, total = 0;
 };
+
+// workgroups per query for `items` items: about kTargetWorkgroups over the
+// call, more when a chunk would exceed kHisaMaxChunk
+int64_t hisa_groups(int64_t nq, int64_t items) {
+  int64_t g = cdiv(kTargetWorkgroups, nq);
+  if (g > dsa::kHisaMaxGroups) g = dsa::kHisaMaxGroups;
+  while (g < dsa::kHisaMaxGroups && cdiv(items, g) > dsa::kHisaMaxChunk) g *= 2;
+  return g > dsa::kHisaMaxGroups ? dsa::kHisaMaxGroups : g;
+}
+
+int hisa_chunk(int64_t items, int64_t g) { return (int)(cdiv(cdiv(items, g), 32) * 32); }
 
 HisaFusedPlan plan_hisa_fused(int64_t nq, int head_dim, int n_seq, int64_t l_max, int block, int m,
                               bool pooled_given) {
   HisaFusedPlan p;
   p.m_max = cdiv(l_max, block);
   const int64_t items = (int64_t)m * block;
-  int64_t g = cdiv(kTargetWorkgroups, nq);
-  if (g > dsa::kHisaMaxGroups) g = dsa::kHisaMaxGroups;
-  while (g < dsa::kHisaMaxGroups &&
-         (cdiv(p.m_max, g) > dsa::kHisaMaxChunk || cdiv(items, g) > dsa::kHisaMaxChunk))
-    g *= 2;
-  if (g > dsa::kHisaMaxGroups) g = dsa::kHisaMaxGroups;
+  const int64_t g = std::max(hisa_groups(nq, p.m_max), hisa_groups(nq, items));
+  p.split = nq * g > kTargetWorkgroups ? 1 : 0;
+  int64_t g1 = g, g2 = g;
+  if (p.split) {
+    g1 = hisa_groups(nq, p.m_max);
+    g2 = hisa_groups(nq, items);
+  }
   p.ok = nq <= 65535 && m <= dsa::kHisaMaxBlocks && items <= dsa::kHisaRegKeys &&
-         cdiv(p.m_max, g) <= dsa::kHisaMaxChunk && cdiv(items, g) <= dsa::kHisaMaxChunk;
+         cdiv(p.m_max, g1) <= dsa::kHisaMaxChunk && cdiv(items, g2) <= dsa::kHisaMaxChunk;
   p.groups = (int)g;
-  p.ch1 = (int)(cdiv(cdiv(p.m_max, g), 32) * 32);
-  p.ch2 = (int)(cdiv(cdiv(items, g), 32) * 32);
+  p.groups1 = (int)g1;
+  p.groups2 = (int)g2;
+  p.ch1 = hisa_chunk(p.m_max, g1);
+  p.ch2 = hisa_chunk(items, g2);
   p.sblk_n = p.ch2 / block + 2;
   Arena A;
   p.sync = A.take((size_t)nq * dsa::kHisaSyncWords * 4);
   p.bflag = A.take((size_t)nq * m * 4);
   p.zero_bytes = A.off;
-  p.cand1 = A.take((size_t)nq * g * p.ch1 * 8);
-  p.cnt1 = A.take((size_t)nq * g * 4);
-  p.keys2 = A.take((size_t)nq * g * p.ch2 * 4);
+  p.cand1 = A.take((size_t)nq * g1 * p.ch1 * 8);
+  p.cnt1 = A.take((size_t)nq * g1 * 4);
+  p.keys2 = A.take((size_t)nq * g2 * p.ch2 * 4);
   p.blocks = A.take((size_t)nq * m * 4);
   p.partial = A.take((size_t)nq * head_dim * 2);
   if (!pooled_given) p.pooled = A.take((size_t)n_seq * p.m_max * head_dim * 2);
@@ -802,6 +821,9 @@ int hisa_block_filter_topk(const void* q, const float* w, const void* k, const v
     h.l_max = l_max;
     h.m_max = f.m_max;
     h.groups = f.groups;
+    h.split = f.split;
+    h.groups1 = f.groups1;
+    h.groups2 = f.groups2;
     h.ch1 = f.ch1;
     h.ch2 = f.ch2;
     h.sblk_n = f.sblk_n;

@@ -6,9 +6,11 @@
 
 namespace dsa {
 
-// HISA for decode-shaped calls: `groups` workgroups per query score ch1
-// pooled blocks and then ch2 token items each, then one workgroup per query
-// selects the top-k (see k_hisa.hip).
+// HISA: per query, block-pass workgroups score ch1 pooled blocks each and
+// token-pass workgroups ch2 token items each (in one grid of `groups`
+// workgroups per query that do both, or, with `split`, groups1 block-pass
+// items then groups2 token-pass items), then one workgroup per query selects
+// the top-k (see k_hisa.hip).
 struct HisaArgs {
   const uint16_t* q;           // [nq, n_heads, D] bf16
   const float* w;              // [nq, n_heads]
@@ -19,14 +21,16 @@ struct HisaArgs {
   const int32_t* q_pos;        // [nq]
   int nq, n_heads, head_dim, n_seq, block, m_blocks, top_k;
   int64_t l_max, m_max;
-  int groups, ch1, ch2;        // ch1, ch2: multiples of 32, <= kHisaMaxChunk
+  int groups;                  // workgroups per query (both passes), or
+  int split, groups1, groups2; // with split: block-pass / token-pass items per query
+  int ch1, ch2;                // multiples of 32, <= kHisaMaxChunk
   int sblk_n;                  // LDS slots for block ids (>= ch2 / block + 2)
   // workspace
   uint32_t* sync;              // [nq, kHisaSyncWords]  (zeroed before the launch)
   int32_t* bflag;              // [nq, m_blocks] kept block + 1 (zeroed before the launch)
-  uint2* cand1;                // [nq, groups, ch1] block candidates
-  uint32_t* cnt1;              // [nq, groups]
-  uint32_t* keys2;             // [nq, groups * ch2] token-pass score keys
+  uint2* cand1;                // [nq, g1, ch1] block candidates (g1 = groups, or groups1)
+  uint32_t* cnt1;              // [nq, g1]
+  uint32_t* keys2;             // [nq, g2 * ch2] token-pass score keys (g2 = groups, or groups2)
   int32_t* blocks;             // [nq, m_blocks] kept blocks (workspace or the caller's)
   // outputs
   int32_t* out_idx;            // [nq, top_k]
@@ -43,13 +47,14 @@ constexpr int kHisaMaxBlocks = 1024;      // m_blocks of the one-kernel path
 constexpr int kHisaRegKeys = 8192;        // token items per query (selected in LDS)
 // LDS of one workgroup: keys [max(ch1, ch2)], histogram [bins + bins / 16],
 // scan scratch [64],
-// candidate offsets [groups + 2] and counts [groups], block ids [sblk_n], the kept blocks and
+// candidate offsets [g1 + 2] and counts [g1], block ids [sblk_n], the kept blocks and
 // their scores [2 * m_blocks], then (8-byte aligned) the tie list
 // [kHisaListCap], the brute-force tie slots [64] and the block candidates
 // [kHisaCandCap] (pairs).
 inline __host__ __device__ int hisa_list_offset_words(const HisaArgs& a) {
-  const int w = (a.ch1 > a.ch2 ? a.ch1 : a.ch2) + kHisaBins + kHisaBins / 16 + 64 + 2 * a.groups + 2 + a.sblk_n +
-                2 * a.m_blocks;
+  const int g1 = a.split ? a.groups1 : a.groups;
+  const int w = (a.ch1 > a.ch2 ? a.ch1 : a.ch2) + kHisaBins + kHisaBins / 16 + 64 + 2 * g1 + 2 +
+                a.sblk_n + 2 * a.m_blocks;
   return (w + 1) & ~1;
 }
 inline size_t hisa_lds_bytes(const HisaArgs& a) {

@@ -57,6 +57,7 @@ constexpr int kHistWords = Hist<kHT>::kWords;
 DSA_DEVICE int hpad(int b) { return Hist<kHT>::at(b); }
 constexpr uint64_t kSpinTicks = 1ull << 26;     // ~0.67 s of the 100 MHz wall clock
 constexpr int kSU = 8;                          // entries per thread per pass step
+constexpr int kHisaSegRead = 96;                // candidate slots read per segment up front
 
 enum SyncWord {
   S_ARRIVE1 = 0,   // block-pass workgroups done
@@ -429,9 +430,10 @@ __global__ __launch_bounds__(kHT) __attribute__((amdgpu_waves_per_eu(2))) void k
   uint32_t* skey = smem;                                        // [chmax]
   uint32_t* hist = skey + chmax;                                // [kHistWords]
   uint32_t* scratch = hist + kHistWords;                        // [64]
-  uint32_t* off = scratch + 64;                                 // [groups + 2]
-  uint32_t* scnt = off + a.groups + 2;                          // [groups]
-  int32_t* sblk = reinterpret_cast<int32_t*>(scnt + a.groups);  // [sblk_n]
+  const int g1 = a.split ? a.groups1 : a.groups, g2 = a.split ? a.groups2 : a.groups;
+  uint32_t* off = scratch + 64;                                 // [g1 + 2]
+  uint32_t* scnt = off + g1 + 2;                                // [g1]
+  int32_t* sblk = reinterpret_cast<int32_t*>(scnt + g1);        // [sblk_n]
   int32_t* sbid = sblk + a.sblk_n;                              // [m_blocks] kept blocks
   float* sbsc = reinterpret_cast<float*>(sbid + a.m_blocks);    // [m_blocks] their scores
   uint2* list = reinterpret_cast<uint2*>(smem + hisa_list_offset_words(a));   // [kHisaListCap]
@@ -440,7 +442,25 @@ __global__ __launch_bounds__(kHT) __attribute__((amdgpu_waves_per_eu(2))) void k
   __shared__ uint32_t s_cnt, s_ln, s_out, s_sel, s_go, s_above, s_nb;
   __shared__ int s_b;
 
-  const int g = blockIdx.x, t = blockIdx.y, tid = (int)threadIdx.x, lane = lane_id();
+  // grid: (groups, nq), each workgroup taking part in both passes; or, with
+  // split, a 1-D grid of the block-pass items of every query followed by the
+  // token-pass items (each query's items consecutive)
+  int t, g;
+  bool pass1, pass2;
+  if (a.split) {
+    const int nb1 = a.nq * g1;
+    pass1 = (int)blockIdx.x < nb1;
+    pass2 = !pass1;
+    const int bid = pass1 ? (int)blockIdx.x : (int)blockIdx.x - nb1;
+    const int gq = pass1 ? g1 : g2;
+    t = bid / gq;
+    g = bid - t * gq;
+  } else {
+    g = blockIdx.x;
+    t = blockIdx.y;
+    pass1 = pass2 = true;
+  }
+  const int tid = (int)threadIdx.x, lane = lane_id();
   const int seq = a.q_seq ? a.q_seq[t] : 0;
   const int64_t pos = a.q_pos[t];
   int32_t* out_i = a.out_idx + (size_t)t * a.top_k;
@@ -448,11 +468,7 @@ __global__ __launch_bounds__(kHT) __attribute__((amdgpu_waves_per_eu(2))) void k
   int32_t* blocks = a.blocks + (size_t)t * a.m_blocks;
   float* bscore = a.out_block_score ? a.out_block_score + (size_t)t * a.m_blocks : nullptr;
   if (!(seq >= 0 && seq < a.n_seq && pos >= 0 && pos < a.l_max)) {   // no keys: padding only
-    if (g == 0) {
-      for (int i = tid; i < a.top_k; i += kHT) {
-        out_i[i] = -1;
-        if (out_s) out_s[i] = -__builtin_inff();
-      }
+    if (pass1 && g == 0) {                       // (k_hisa_topk pads the top-k row)
       for (int i = tid; i < a.m_blocks; i += kHT) {
         blocks[i] = -1;
         if (bscore) bscore[i] = -__builtin_inff();
@@ -465,19 +481,20 @@ __global__ __launch_bounds__(kHT) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int n1 = (M + a.ch1 - 1) / a.ch1;                       // block-pass workgroups
   const int items2 = m1 * a.block;                              // token items (list slots)
   const int n2 = (items2 + a.ch2 - 1) / a.ch2;                  // token-pass workgroups
-  if (g >= n1 && g >= n2) return;
+  pass1 = pass1 && g < n1;
+  pass2 = pass2 && g < n2;
+  if (!pass1 && !pass2) return;
   uint32_t* sy = a.sync + (size_t)t * kHisaSyncWords;
   int32_t* bflag = a.bflag + (size_t)t * a.m_blocks;            // kept block + 1 (0: not yet)
 
   SC sc;
   sc.init(a.q + (size_t)t * a.n_heads * D, a.w + (size_t)t * a.n_heads, nullptr, a.n_heads,
           nullptr);
-  for (int i = tid; i < kHistWords; i += kHT) hist[i] = 0;
-  if (tid == 0) s_cnt = 0;
-  __syncthreads();
-
   // ---- 1. block pass
-  if (g < n1) {
+  if (pass1) {
+    for (int i = tid; i < kHistWords; i += kHT) hist[i] = 0;
+    if (tid == 0) s_cnt = 0;
+    __syncthreads();
     const int i0 = g * a.ch1;
     const int nc = (M - i0) < a.ch1 ? (M - i0) : a.ch1;
     const bool part = ((pos + 1) % a.block) != 0;
@@ -494,7 +511,7 @@ __global__ __launch_bounds__(kHT) __attribute__((amdgpu_waves_per_eu(2))) void k
     // candidates: every block of a bin >= bl, at consecutive slots (per wave
     // one LDS atomic, then ballots: each store instruction writes consecutive
     // slots)
-    uint2* seg = a.cand1 + ((size_t)t * a.groups + g) * a.ch1;
+    uint2* seg = a.cand1 + ((size_t)t * g1 + g) * a.ch1;
     const int rounds = (nc + kHT - 1) / kHT;
     uint32_t cw = 0;
     for (int r = 0; r < rounds; ++r) {
@@ -515,7 +532,7 @@ __global__ __launch_bounds__(kHT) __attribute__((amdgpu_waves_per_eu(2))) void k
       wb += (uint32_t)__popcll(m);
     }
     __syncthreads();
-    if (tid == 0) st_dev(&a.cnt1[(size_t)t * a.groups + g], s_cnt);
+    if (tid == 0) st_dev(&a.cnt1[(size_t)t * g1 + g], s_cnt);
     drain();
     __syncthreads();
     if (tid == 0) s_sel = atomicAdd(&sy[S_ARRIVE1], 1u) == (uint32_t)(n1 - 1) ? 1u : 0u;
@@ -524,11 +541,12 @@ __global__ __launch_bounds__(kHT) __attribute__((amdgpu_waves_per_eu(2))) void k
       // The exact top-m1 of all candidates.  The segment counts and the first
       // S entries of every segment are loaded in one round (entries past a
       // segment's count are dropped); longer segments are completed after.
-      const uint2* cbase = a.cand1 + (size_t)t * a.groups * a.ch1;
-      const int S = (int)kHisaCandCap / n1 < a.ch1 ? (int)kHisaCandCap / n1 : a.ch1;
+      const uint2* cbase = a.cand1 + (size_t)t * g1 * a.ch1;
+      int S = (int)kHisaCandCap / n1 < a.ch1 ? (int)kHisaCandCap / n1 : a.ch1;
+      if (S > kHisaSegRead) S = kHisaSegRead;         // a segment holds about m1
       constexpr int U = kHisaCandCap / kHT;
       uint32_t c = 0;
-      if (tid < n1) c = ld_dev(&a.cnt1[(size_t)t * a.groups + tid]);
+      if (tid < n1) c = ld_dev(&a.cnt1[(size_t)t * g1 + tid]);
       uint2 v[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -570,7 +588,7 @@ __global__ __launch_bounds__(kHT) __attribute__((amdgpu_waves_per_eu(2))) void k
       }
     }
   }
-  if (g >= n2) return;
+  if (!pass2) return;
 
   // ---- 2. token pass: wait for this workgroup's block ids, score, store keys
   const int j0 = g * a.ch2;
@@ -599,7 +617,7 @@ __global__ __launch_bounds__(kHT) __attribute__((amdgpu_waves_per_eu(2))) void k
   __syncthreads();
   // the keys go to the query's key array; the selection kernel that follows
   // in stream order reads them
-  uint32_t* keys_t = a.keys2 + (size_t)t * a.groups * a.ch2;
+  uint32_t* keys_t = a.keys2 + (size_t)t * g2 * a.ch2;
   for (int j = tid; j < nc2; j += kHT) keys_t[j0 + j] = skey[j];
 }
 
@@ -638,7 +656,7 @@ __global__ __launch_bounds__(kTT) void k_hisa_topk(HisaArgs a) {
   // (key, token id) of every item into LDS: item i = tid + j * kTT is token
   // list[i / block] * block + i % block; list index and offset advance by kTT
   // per step without a division
-  const uint32_t* keys_t = a.keys2 + (size_t)t * a.groups * a.ch2;
+  const uint32_t* keys_t = a.keys2 + (size_t)t * (a.split ? a.groups2 : a.groups) * a.ch2;
   const int blk = a.block, step = kTT / blk, rem = kTT % blk;
   int li = tid / blk, r = tid % blk;
   for (int base = 0; base < items2; base += kSU * kTT) {
@@ -672,7 +690,10 @@ hipError_t launch_hisa_t(const HisaArgs& a, hipStream_t stream) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k, dim3(a.groups, a.nq), dim3(kHT), lds, stream, a);
+  if (a.split)
+    hipLaunchKernelGGL(k, dim3(a.nq * (a.groups1 + a.groups2)), dim3(kHT), lds, stream, a);
+  else
+    hipLaunchKernelGGL(k, dim3(a.groups, a.nq), dim3(kHT), lds, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const size_t lds2 = hisa_topk_lds_bytes(a);
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_hisa_topk),
@@ -685,7 +706,10 @@ hipError_t launch_hisa_t(const HisaArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_hisa(const HisaArgs& a, hipStream_t stream) {
-  if (a.groups < 1 || a.groups > kHisaMaxGroups || a.ch1 < 32 || a.ch2 < 32 ||
+  const int gmax = a.split ? (a.groups1 > a.groups2 ? a.groups1 : a.groups2) : a.groups;
+  const int gmin = a.split ? (a.groups1 < a.groups2 ? a.groups1 : a.groups2) : a.groups;
+  if (gmin < 1 || gmax > kHisaMaxGroups || a.ch1 < 32 || a.ch2 < 32 ||
+      (a.split && (int64_t)a.nq * (a.groups1 + a.groups2) > 0x7FFFFFFF) ||
       a.ch1 > kHisaMaxChunk || a.ch2 > kHisaMaxChunk || a.ch1 % 32 || a.ch2 % 32 ||
       a.sblk_n < a.ch2 / a.block + 2 || a.nq < 1 || a.nq > 65535 || a.m_blocks < 1 ||
       a.m_blocks > kHisaMaxBlocks || (int64_t)a.m_blocks * a.block > kHisaRegKeys)
