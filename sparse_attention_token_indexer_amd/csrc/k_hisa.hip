@@ -3,12 +3,16 @@
 // the surviving blocks scored with the full indexer and the exact top-k among
 // them) in two kernels.
 //
-// k_hisa, grid (G, nq): the G workgroups of query t share its work:
+// k_hisa: per query, block-pass and token-pass workgroups share its work.
+// When the grid fits the chip at once it is (G, nq) and every workgroup takes
+// part in both passes; otherwise (many queries) it is 1-D, every query's
+// block-pass items first and the token-pass items after, so that no
+// workgroup waits for a selection on a slot that block-pass work still needs.
 //  1. block pass: workgroup g scores pooled blocks [g*ch1, (g+1)*ch1) into LDS
 //     and writes those whose 12-bit bin is at or above its local top-m bin (a
 //     superset of its part of the query's top-m).  The last of the query's
-//     workgroups to arrive selects the exact top-m from these candidates and
-//     publishes each kept block as id + 1 in a cleared array.
+//     block-pass workgroups to arrive selects the exact top-m from these
+//     candidates and publishes each kept block as id + 1 in a cleared array.
 //  2. token pass: workgroup g waits for the entries of that array its items
 //     need, scores token items [g*ch2, (g+1)*ch2) of the block list (item i =
 //     token list[i / block] * block + i % block) and stores their keys.
@@ -22,11 +26,13 @@
 // before it bumps the arrival counter, so the workgroup that sees the final
 // count sees the data.  (A device-scope fence would instead write back and
 // invalidate the whole L2 at every step, which costs far more than the work.)
-// Only the token pass waits, and only for its query's block selection; a
-// query's workgroups are consecutive in dispatch order (blockIdx.x runs
-// fastest), so the query groups dispatched first can always finish and free
-// room for the rest.  The waits are also bounded in time: a query whose wait
-// times out is marked in its sync words and left incomplete.
+// Only the token pass waits, and only for its query's block selection, which
+// block-pass work that never waits produces: in the (G, nq) grid a query's
+// workgroups are consecutive in dispatch order (blockIdx.x runs fastest), so
+// the query groups dispatched first can always finish and free room for the
+// rest; in the 1-D grid every block-pass item precedes every token-pass
+// item.  The waits are also bounded in time: a query whose wait times out is
+// marked in its sync words and left incomplete.
 #include "dsa_hisa.h"
 #include "dsa_internal.h"
 #include "dsa_scorers.h"
