@@ -116,6 +116,13 @@ def hisa(q_t, w_t, K, pos: int, B: int, m: int, k: int) -> Tuple[List[int], List
     return blocks, select([(score(q_t, w_t, K[u]), u) for u in cand], k)
 
 
+def misa_hisa(q_t, w_t, K, pos: int, B: int, h: int, m: int, k: int):
+    I = importance(q_t, w_t, pool(K, B, pos + 1))
+    heads = select([(I[j], j) for j in range(len(I))], h)
+    blocks, idx = hisa([q_t[j] for j in heads], [w_t[j] for j in heads], K, pos, B, m, k)
+    return heads, blocks, idx
+
+
 def iou(a: Sequence[int], b: Sequence[int]) -> float:
     sa = {x for x in a if x >= 0}
     sb = {x for x in b if x >= 0}

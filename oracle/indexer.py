@@ -35,7 +35,10 @@ Readings where the pages are silent (each also listed with the design notes):
   score = the indexer formula with all heads applied to the pooled keys;
   R9 no forced sink/local blocks; R10 MISA dagger ranks candidates by the
   routed score and returns full H_I-head scores; R11 ties go to the lower
-  index, output is a set padded with (-1, -inf), -0.0 equals +0.0.
+  index, output is a set padded with (-1, -inf), -0.0 equals +0.0; R13 the
+  composition of the two (MISA summary, "method": the head axis; HISA review,
+  section 3: the token axis) routes h heads with MISA's router and runs both
+  HISA stages with only those heads, original weights kept.
 
 Pins (what checks each function against something other than itself; the
 tests live in tests/test_oracle_*.py):
@@ -55,6 +58,9 @@ tests live in tests/test_oracle_*.py):
   hisa             m = M equals dense; B = 1 with m >= k equals dense;
                    hand-worked example.  The block-score formula (R8) is
                    "parity unpinned".
+  misa_hisa        h = H_I equals HISA; m = M equals MISA; pure-Python brute
+                   force.  The composition itself (R13) is a reading of the
+                   pages, which name the combination but give no steps.
   iou              hand-computed cases, IoU(A, A) = 1, disjoint = 0
 """
 from __future__ import annotations
@@ -269,6 +275,26 @@ def hisa_row(q_t, w_t, K_seq, pos: int, B: int, m: int, k: int,
     fine = rescore_row(q_t, w_t, K_seq, cand, k)
     fine.update({"bs": bs, "bA": bA, "blocks": np.asarray(blocks), "pooled": pooled})
     return fine
+
+
+# -------------------------------------------------------------- MISA∘HISA ---
+
+def misa_hisa_row(q_t, w_t, K_seq, pos: int, B: int, h: int, m: int, k: int,
+                  heads: Optional[np.ndarray] = None,
+                  blocks: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """MISA∘HISA (R13): route to h heads from the pooled keys as MISA does,
+    then run HISA with only those heads (original weights kept) in both of its
+    stages: block scores over the pooled keys and token scores inside the kept
+    blocks.  ``heads`` / ``blocks`` skip the routing / block stage (for
+    stage-conditional checks)."""
+    pooled = misa_pooled_for_query(K_seq, B, pos)
+    I = misa_importance(q_t, w_t, pooled)
+    if heads is None:
+        heads = route_heads(I, h)
+    hs = np.asarray(heads, dtype=np.int64)
+    r = hisa_row(q_t[hs], w_t[hs], K_seq, pos, B, m, k, blocks=blocks)
+    r.update({"I": I, "heads": hs})
+    return r
 
 
 # -------------------------------------------------------------------- IoU ---

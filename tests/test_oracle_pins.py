@@ -249,6 +249,34 @@ def test_misa_hisa_match_brute_exact():
         assert sorted(rh["idx"].tolist()) == sorted(bi)
 
 
+def test_misa_hisa_matches_brute_and_reduces():
+    """MISA∘HISA against the pure-Python composition on tiny integer inputs;
+    with every head routed it is HISA, with every block kept it is MISA."""
+    rng = np.random.default_rng(21)
+    for _ in range(40):
+        H = int(rng.integers(1, 5)); d = int(rng.integers(1, 7)); L = int(rng.integers(2, 65))
+        q, w, K = _int_inputs(rng, H, d, L)
+        K = O.round_bf16(K)
+        pos = int(rng.integers(0, L)); k = int(rng.integers(1, 20)); B = int(rng.integers(1, 9))
+        h = int(rng.integers(1, H + 1)); m = int(rng.integers(1, 6))
+        r = O.misa_hisa_row(q, w, K, pos, B, h, m, k)
+        bh, bb, bi = brute.misa_hisa(q.tolist(), w.tolist(), K.tolist(), pos, B, h, m, k)
+        assert r["heads"].tolist() == bh
+        assert r["blocks"].tolist() == bb
+        assert sorted(r["idx"].tolist()) == sorted(bi)
+        # every head routed: HISA (the head order does not change the sums'
+        # exact integer values here)
+        ra = O.misa_hisa_row(q, w, K, pos, B, H, m, k)
+        rh = O.hisa_row(q, w, K, pos, B, m, k)
+        assert sorted(ra["blocks"].tolist()) == sorted(rh["blocks"].tolist())
+        assert sorted(ra["idx"].tolist()) == sorted(rh["idx"].tolist())
+        # every block kept: MISA
+        M = (pos + B) // B
+        rm = O.misa_hisa_row(q, w, K, pos, B, h, M, k)
+        mm = O.misa_row(q, w, K, pos, B, h, k)
+        assert sorted(rm["idx"].tolist()) == sorted(mm["idx"].tolist())
+
+
 def test_router_choice_maximises_importance():
     """Exhaustive search over all h-subsets of heads: the routed set attains the
     largest summed importance."""
