@@ -10,8 +10,9 @@ Other workloads (--workload): tiny (float32, 16 queries, L = 4096),
 dense_prefill (32768 causal rows of one 32768-key cache), misa_prefill (the same
 rows routed to h = 8 of 64 heads over 64-key pooled blocks), misa / misa_dagger
 (h = 8 of 64 heads, B = 64, k' = 8192), hisa (32 heads, L = 1M, B = 128,
-m = 64), pool (mean pooling of the 128K caches).  tiny and hisa touch less
-than the 256 MB last-level cache and are timed cold.
+m = 64), misa_hisa (the same with the router's h = 8 heads), pool (mean
+pooling of the 128K caches).  tiny, hisa and misa_hisa touch less than the
+256 MB last-level cache and are timed cold.
 
 The steps are timed twice: first the calls alone (ms_per_step, value), then
 the same number of calls with the library's per-launch HIP events on the
@@ -35,7 +36,7 @@ CSRC = os.path.join(ROOT, "sparse_attention_token_indexer_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 WORKLOADS = {"dense_decode": 2, "tiny": 1, "dense_prefill": 3, "misa": 4, "misa_dagger": 4,
-             "hisa": 5, "pool": 4, "misa_prefill": 3, "hisa_prefill": 3}
+             "hisa": 5, "pool": 4, "misa_prefill": 3, "hisa_prefill": 3, "misa_hisa": 5}
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
 
 
@@ -45,7 +46,7 @@ KERNEL_SOURCE = {"dense_decode": "k_score_select.hip", "tiny": "k_score_select.h
                  "misa": "k_score_select.hip", "misa_dagger": "k_score_select.hip",
                  "hisa": "k_hisa.hip", "dense_prefill": "k_prefill.hip",
                  "misa_prefill": "k_prefill_routed.hip", "pool": "k_pool.hip",
-                 "hisa_prefill": "k_hisa.hip"}
+                 "hisa_prefill": "k_hisa.hip", "misa_hisa": "k_hisa.hip"}
 
 
 def _local_sources(name: str) -> list:
@@ -155,6 +156,8 @@ def cpu_baseline(wl, seed, seconds: float, mode: str):
             O.misa_row(q_t, w_t, K, p, 64, 8, wl.top_k)
         elif mode == "hisa_prefill":
             O.hisa_row(q_t, w_t, K, p, 128, 64, wl.top_k)
+        elif mode == "misa_hisa":
+            O.misa_hisa_row(q_t, w_t, K, p, wl.block, 8, wl.m_blocks, wl.top_k)
         else:
             O.dense_row(q_t, w_t, K, p, wl.top_k)
         spent += time.perf_counter() - t0
@@ -301,6 +304,29 @@ def main() -> int:
         kernel_bytes = call_bytes          # one kernel: block pass, top-m, token pass, top-k
         bound_note = ("HBM: the pooled keys once and the keys of the m surviving blocks, in one "
                       "kernel (block pass, top-m, token pass, top-k)")
+    elif name == "misa_hisa":
+        h = 8
+        kp = dsa.indexer_mean_pool_keys(k, wl.block)
+        nbytes = dsa.misa_hisa_topk_workspace_size(nq, H, d, wl.n_seq, L, wl.block, h,
+                                                   wl.m_blocks, topk, 1)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+
+        def step():
+            dsa.misa_hisa_topk(q, w, k, q_pos, q_seq, block=wl.block, n_active_heads=h,
+                               m_blocks=wl.m_blocks, top_k=topk, k_pooled=kp, with_heads=False,
+                               with_blocks=False, out_idx=out_i, out_score=out_s, workspace=ws)
+        kind = "hisa"
+        M = -(-L // wl.block)
+        pooled_bytes = wl.n_seq * M * d * 2
+        gathered = nq * wl.m_blocks * wl.block * d * eb
+        # the routed heads' q and w, the pooled keys, the kept blocks' keys, the outputs
+        kernel_bytes = pooled_bytes + gathered + nq * h * (d * eb + 4) + nq * topk * 8
+        call_bytes = pooled_bytes + gathered + io_bytes   # the router reads every head's q
+        call_flops = (nq * M * H * d * 2 + nq * M * h * d * 2      # router + block pass
+                      + nq * wl.m_blocks * wl.block * h * d * 2)  # token pass
+        bound_note = ("HBM: the pooled keys once and the keys of the m surviving blocks, in one "
+                      "kernel over the routed heads (block pass, top-m, token pass, top-k)")
+        extra["routing"] = {"h": h, "block": wl.block, "m_blocks": wl.m_blocks}
     elif name == "hisa_prefill":
         B, m = 128, 64
         kp = dsa.indexer_mean_pool_keys(k, B)
@@ -341,7 +367,7 @@ def main() -> int:
     # (--flush write: they end up holding dirty lines, whose write-back then
     # competes with the step's own reads).
     flush = None
-    if name in ("hisa", "tiny"):
+    if name in ("hisa", "misa_hisa", "tiny"):
         flush_buf = torch.zeros(128 << 20, dtype=torch.float32, device=dev)
         if args.flush == "write":
             flush = lambda: flush_buf.zero_()
@@ -447,13 +473,15 @@ def main() -> int:
         "config": {"workload": {"misa_dagger": "misa_dagger_decode_L128K_H64_h8_kp8192",
                                 "pool": "mean_pool_L128K_B64",
                                 "misa_prefill": "misa_prefill_L32K_H64_h8",
-                                "hisa_prefill": "hisa_prefill_L32K_H64_B128_m64"}.get(name, wl.name),
+                                "hisa_prefill": "hisa_prefill_L32K_H64_B128_m64",
+                                "misa_hisa": "misa_hisa_decode_L1M_H32_h8"}.get(name, wl.name),
                    "queries": nq, "l_max": L, "n_heads": H, "head_dim": d,
                    "top_k": topk, "causal_pairs": pairs, "parallelism": "single GPU",
                    **({"block": wl.block} if wl.block else {}),
-                   **({"h": wl.n_active_heads} if name.startswith("misa") else {}),
+                   **({"h": 8 if name == "misa_hisa" else wl.n_active_heads}
+                      if name.startswith("misa") else {}),
                    **({"k_prime": wl.k_prime} if name == "misa_dagger" else {}),
-                   **({"m_blocks": wl.m_blocks} if name == "hisa" else {})},
+                   **({"m_blocks": wl.m_blocks} if name in ("hisa", "misa_hisa") else {})},
         "topk_latency_us": ms_per_step * 1e3,
         "ms_per_step_with_kernel_events": ms_per_step_events,
         "call": {"latency_median_us": call_med_ms * 1e3, "latency_min_us": per_call[0] * 1e3,

@@ -164,6 +164,33 @@ int hisa_block_filter_topk(const void* q, const float* w, const void* k, const v
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * MISA then HISA (MISA summary, "method": the head axis; HISA review,
+ * section 3: the token axis; the composition, which the pages name but do
+ * not spell out, routes first): the n_active_heads = h most important heads
+ * of every query are chosen by MISA's router (importance as for
+ * misa_route_score_topk), and both HISA stages use only them, original
+ * weights kept: block scores
+ *   bs[t, b] = sum_{j in heads_t} w[t, j] * max(0, q[t, j] . kbar[b]),
+ * the m_blocks best blocks, then token scores with the same heads inside the
+ * surviving blocks and the top_k.  Outputs as for hisa_block_filter_topk,
+ * plus out_heads [nq, h] (most important first) and out_importance
+ * [nq, n_heads], each optional.
+ * Only DSA_DTYPE_BF16; 1 <= h <= n_heads; 1 <= block; 1 <= m_blocks <= 1024
+ * and m_blocks * block <= 8192 (DSA_EUNSUPPORTED otherwise); nq <= 65535.
+ */
+size_t misa_hisa_topk_workspace_size(int32_t nq, int32_t n_heads, int32_t head_dim,
+                                     int32_t n_seq, int64_t l_max, int32_t block,
+                                     int32_t n_active_heads, int32_t m_blocks, int32_t top_k,
+                                     int32_t pooled_given);
+int misa_hisa_topk(const void* q, const float* w, const void* k, const void* k_pooled,
+                   int32_t dtype, const int32_t* q_seq, const int32_t* q_pos, int32_t nq,
+                   int32_t n_heads, int32_t head_dim, int32_t n_seq, int64_t l_max, int32_t block,
+                   int32_t n_active_heads, int32_t m_blocks, int32_t top_k, int32_t* out_idx,
+                   float* out_score, int32_t* out_heads, float* out_importance,
+                   int32_t* out_blocks, float* out_block_score, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Selection agreement (MISA summary, "results"; HISA review, section 3): per
  * query IoU = |A & B| / |A | B| over the non-negative entries of a[t, :] and
  * b[t, :] (two empty rows give 1).  Rows must hold no duplicate indices.

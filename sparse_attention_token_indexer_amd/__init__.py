@@ -44,6 +44,11 @@ _SIGS = {
     "hisa_block_filter_topk": ([_c_p, _c_p, _c_p, _c_p, _i32, _c_p, _c_p, _i32, _i32, _i32, _i32,
                                 _i64, _i32, _i32, _i32, _c_p, _c_p, _c_p, _c_p, _c_p, _sz, _c_p],
                                ctypes.c_int),
+    "misa_hisa_topk_workspace_size": ([_i32, _i32, _i32, _i32, _i64, _i32, _i32, _i32, _i32,
+                                       _i32], _sz),
+    "misa_hisa_topk": ([_c_p, _c_p, _c_p, _c_p, _i32, _c_p, _c_p, _i32, _i32, _i32, _i32, _i64,
+                        _i32, _i32, _i32, _i32, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _sz,
+                        _c_p], ctypes.c_int),
     "indexer_selection_iou": ([_c_p, _c_p, _i32, _i32, _c_p, _c_p], ctypes.c_int),
     "dsa_kernel_timing": ([ctypes.c_int], ctypes.c_int),
     "dsa_kernel_timing_read": ([_i32, ctypes.POINTER(_i64), ctypes.POINTER(ctypes.c_double),
@@ -280,6 +285,54 @@ def hisa_block_filter_topk(q, w, k, q_pos, q_seq=None, *, block: int, m_blocks: 
                                       _ptr(blocks), _ptr(bscore), _ptr(ws), nbytes, _stream(dev))
     _check(st, "hisa_block_filter_topk")
     out = {"idx": out_idx, "score": out_score}
+    if blocks is not None:
+        out["blocks"] = blocks
+        out["block_score"] = bscore
+    return out
+
+
+def misa_hisa_topk_workspace_size(nq, n_heads, head_dim, n_seq, l_max, block, n_active_heads,
+                                  m_blocks, top_k, pooled_given) -> int:
+    return int(lib().misa_hisa_topk_workspace_size(nq, n_heads, head_dim, n_seq, l_max, block,
+                                                   n_active_heads, m_blocks, top_k,
+                                                   int(bool(pooled_given))))
+
+
+def misa_hisa_topk(q, w, k, q_pos, q_seq=None, *, block: int, n_active_heads: int,
+                   m_blocks: int, top_k: int, k_pooled=None, with_scores=True, with_heads=True,
+                   with_importance=False, with_blocks=True, out_idx=None, out_score=None,
+                   workspace=None) -> Dict[str, torch.Tensor]:
+    """MISA then HISA: h routed heads, then the top-m pooled blocks and the
+    top_k tokens inside them, both scored with those heads.  Returns a dict
+    with "idx", "score" and, if asked, "heads", "importance", "blocks" and
+    "block_score"."""
+    dev, nq, H, d, n_seq, l_max = _common(q, w, k, q_pos, q_seq)
+    if q.dtype != torch.bfloat16:
+        raise TypeError("MISA-HISA takes bf16 inputs")
+    if k_pooled is not None:
+        _need(k_pooled, "k_pooled", torch.bfloat16, 3, dev)
+        if tuple(k_pooled.shape) != (n_seq, -(-l_max // block), d):
+            raise ValueError("k_pooled must be [n_seq, ceil(l_max/block), d]")
+    out_idx, out_score = _outputs(dev, nq, top_k, out_idx, out_score, with_scores)
+    h = n_active_heads
+    heads = torch.empty((nq, h), dtype=torch.int32, device=dev) if with_heads else None
+    imp = torch.empty((nq, H), dtype=torch.float32, device=dev) if with_importance else None
+    blocks = torch.empty((nq, m_blocks), dtype=torch.int32, device=dev) if with_blocks else None
+    bscore = torch.empty((nq, m_blocks), dtype=torch.float32, device=dev) if with_blocks else None
+    nbytes = misa_hisa_topk_workspace_size(nq, H, d, n_seq, l_max, block, h, m_blocks, top_k,
+                                           k_pooled is not None)
+    ws = _workspace(nbytes, dev, workspace)
+    st = lib().misa_hisa_topk(_ptr(q), _ptr(w), _ptr(k), _ptr(k_pooled), DSA_DTYPE_BF16,
+                              _ptr(q_seq), _ptr(q_pos), nq, H, d, n_seq, l_max, block, h,
+                              m_blocks, top_k, _ptr(out_idx), _ptr(out_score), _ptr(heads),
+                              _ptr(imp), _ptr(blocks), _ptr(bscore), _ptr(ws), nbytes,
+                              _stream(dev))
+    _check(st, "misa_hisa_topk")
+    out = {"idx": out_idx, "score": out_score}
+    if heads is not None:
+        out["heads"] = heads
+    if imp is not None:
+        out["importance"] = imp
     if blocks is not None:
         out["blocks"] = blocks
         out["block_score"] = bscore

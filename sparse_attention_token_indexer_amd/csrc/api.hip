@@ -273,7 +273,7 @@ MisaPlan plan_misa(int64_t nq, int n_heads, int head_dim, int n_seq, int64_t l_m
   p.zero_bytes = A.off;
   // router: about kTargetWorkgroups workgroups, at least 64 blocks each
   int64_t bps = 64;
-  while (nq * cdiv(p.m_max, bps) > kTargetWorkgroups) bps *= 2;
+  while (bps < p.m_max && nq * cdiv(p.m_max, bps) > kTargetWorkgroups) bps *= 2;
   p.bps = (int)bps;
   p.splits = (int)cdiv(p.m_max, bps);
   p.part = A.take((size_t)nq * p.splits * n_heads * 4);
@@ -392,6 +392,105 @@ int run_prepare(void* ws, size_t zero_bytes, const void* k, const int32_t* q_seq
   pa.partial = partial;
   return hip_status(timed(DSA_KERNEL_PREPARE, stream, [&] { return dsa::launch_prepare(pa, stream); }),
                     "prepare kernel", stream);
+}
+
+// The HISA kernels' common set-up: pooled keys (the caller's, or pooled into
+// the workspace) and the prepare kernel (sync words, kept-block flags,
+// partial last blocks).
+int hisa_setup(const HisaFusedPlan& f, const void* k, const void* k_pooled, const int32_t* q_seq,
+               const int32_t* q_pos, int nq, int n_seq, int head_dim, int64_t l_max, int block,
+               void* workspace, hipStream_t stream, const uint16_t** pooled_out,
+               uint16_t** partial_out) {
+  int st;
+  const uint16_t* pooled = reinterpret_cast<const uint16_t*>(k_pooled);
+  if (!pooled) {
+    uint16_t* dst = at<uint16_t>(workspace, f.pooled);
+    st = hip_status(timed_pool(stream, [&] { return dsa::launch_mean_pool(reinterpret_cast<const uint16_t*>(k), n_seq, l_max,
+                                          head_dim, block, dst, stream); }),
+                    "mean-pool kernel", stream);
+    if (st) return st;
+    pooled = dst;
+  }
+  uint16_t* partial = at<uint16_t>(workspace, f.partial);
+  if ((st = run_prepare(workspace, f.zero_bytes, k, q_seq, q_pos, nq, n_seq, head_dim, block,
+                        l_max, partial, stream)))
+    return st;
+  *pooled_out = pooled;
+  *partial_out = partial;
+  return DSA_OK;
+}
+
+// k_hisa and k_hisa_topk over the plan; heads (stride heads_stride, first
+// h_use) restricts both passes to routed heads, null uses all n_heads.
+int run_hisa_kernels(const HisaFusedPlan& f, const void* q, const float* w, const void* k,
+                     const uint16_t* pooled, const uint16_t* partial, const int32_t* q_seq,
+                     const int32_t* q_pos, const int32_t* heads, int heads_stride, int h_use,
+                     int nq, int n_heads, int head_dim, int n_seq, int64_t l_max, int block,
+                     int m_blocks, int top_k, int32_t* out_idx, float* out_score,
+                     int32_t* out_blocks, float* out_block_score, void* workspace,
+                     hipStream_t stream) {
+  dsa::HisaArgs h{};
+  h.q = reinterpret_cast<const uint16_t*>(q);
+  h.w = w;
+  h.keys = reinterpret_cast<const uint16_t*>(k);
+  h.pooled = pooled;
+  h.partial = partial;
+  h.q_seq = q_seq;
+  h.q_pos = q_pos;
+  h.heads = heads;
+  h.heads_stride = heads_stride;
+  h.h_use = h_use;
+  h.nq = nq;
+  h.n_heads = n_heads;
+  h.head_dim = head_dim;
+  h.n_seq = n_seq;
+  h.block = block;
+  h.m_blocks = m_blocks;
+  h.top_k = top_k;
+  h.l_max = l_max;
+  h.m_max = f.m_max;
+  h.groups = f.groups;
+  h.split = f.split;
+  h.groups1 = f.groups1;
+  h.groups2 = f.groups2;
+  h.ch1 = f.ch1;
+  h.ch2 = f.ch2;
+  h.sblk_n = f.sblk_n;
+  h.sync = at<uint32_t>(workspace, f.sync);
+  h.bflag = at<int32_t>(workspace, f.bflag);
+  h.cand1 = at<uint2>(workspace, f.cand1);
+  h.cnt1 = at<uint32_t>(workspace, f.cnt1);
+  h.keys2 = at<uint32_t>(workspace, f.keys2);
+  h.blocks = out_blocks ? out_blocks : at<int32_t>(workspace, f.blocks);
+  h.out_idx = out_idx;
+  h.out_score = out_score;
+  h.out_block_score = out_block_score;
+  return hip_status(timed(DSA_KERNEL_HISA, stream, [&] { return dsa::launch_hisa(h, stream); }),
+                    "HISA kernel", stream);
+}
+
+// MISA∘HISA: the HISA plan, then the router's per-slice sums and the routed
+// heads.
+struct MisaHisaPlan {
+  HisaFusedPlan h;
+  size_t part = 0, heads = 0, total = 0;
+  int splits = 1, bps = 1;
+};
+
+MisaHisaPlan plan_misa_hisa(int64_t nq, int n_heads, int head_dim, int n_seq, int64_t l_max,
+                            int block, int h_act, int m, bool pooled_given) {
+  MisaHisaPlan p;
+  p.h = plan_hisa_fused(nq, head_dim, n_seq, l_max, block, m, pooled_given);
+  int64_t bps = 64;
+  while (bps < p.h.m_max && nq * cdiv(p.h.m_max, bps) > kTargetWorkgroups) bps *= 2;
+  p.bps = (int)bps;
+  p.splits = (int)cdiv(p.h.m_max, bps);
+  Arena A;
+  A.off = p.h.total;
+  p.part = A.take((size_t)nq * p.splits * n_heads * 4);
+  p.heads = A.take((size_t)nq * h_act * 4);
+  p.total = A.off;
+  return p;
 }
 
 void fill_common(dsa::SelArgs& a, const void* q, const float* w, const void* k,
@@ -790,54 +889,14 @@ int hisa_block_filter_topk(const void* q, const float* w, const void* k, const v
   HisaFusedPlan f = plan_hisa_fused(nq, head_dim, n_seq, l_max, block, m_blocks, k_pooled != nullptr);
   if (f.ok) {
     if ((st = check_ws(workspace, workspace_bytes, f.total))) return st;
-    const uint16_t* pooled = reinterpret_cast<const uint16_t*>(k_pooled);
-    if (!pooled) {
-      uint16_t* dst = at<uint16_t>(workspace, f.pooled);
-      st = hip_status(timed_pool(stream, [&] { return dsa::launch_mean_pool(reinterpret_cast<const uint16_t*>(k), n_seq, l_max,
-                                            head_dim, block, dst, stream); }),
-                      "mean-pool kernel", stream);
-      if (st) return st;
-      pooled = dst;
-    }
-    uint16_t* partial = at<uint16_t>(workspace, f.partial);
-    if ((st = run_prepare(workspace, f.zero_bytes, k, q_seq, q_pos, nq, n_seq, head_dim, block,
-                          l_max, partial, stream)))
+    const uint16_t* pooled = nullptr;
+    uint16_t* partial = nullptr;
+    if ((st = hisa_setup(f, k, k_pooled, q_seq, q_pos, nq, n_seq, head_dim, l_max, block, workspace,
+                         stream, &pooled, &partial)))
       return st;
-    dsa::HisaArgs h{};
-    h.q = reinterpret_cast<const uint16_t*>(q);
-    h.w = w;
-    h.keys = reinterpret_cast<const uint16_t*>(k);
-    h.pooled = pooled;
-    h.partial = partial;
-    h.q_seq = q_seq;
-    h.q_pos = q_pos;
-    h.nq = nq;
-    h.n_heads = n_heads;
-    h.head_dim = head_dim;
-    h.n_seq = n_seq;
-    h.block = block;
-    h.m_blocks = m_blocks;
-    h.top_k = top_k;
-    h.l_max = l_max;
-    h.m_max = f.m_max;
-    h.groups = f.groups;
-    h.split = f.split;
-    h.groups1 = f.groups1;
-    h.groups2 = f.groups2;
-    h.ch1 = f.ch1;
-    h.ch2 = f.ch2;
-    h.sblk_n = f.sblk_n;
-    h.sync = at<uint32_t>(workspace, f.sync);
-    h.bflag = at<int32_t>(workspace, f.bflag);
-    h.cand1 = at<uint2>(workspace, f.cand1);
-    h.cnt1 = at<uint32_t>(workspace, f.cnt1);
-    h.keys2 = at<uint32_t>(workspace, f.keys2);
-    h.blocks = out_blocks ? out_blocks : at<int32_t>(workspace, f.blocks);
-    h.out_idx = out_idx;
-    h.out_score = out_score;
-    h.out_block_score = out_block_score;
-    return hip_status(timed(DSA_KERNEL_HISA, stream, [&] { return dsa::launch_hisa(h, stream); }),
-                      "HISA kernel", stream);
+    return run_hisa_kernels(f, q, w, k, pooled, partial, q_seq, q_pos, nullptr, 0, n_heads, nq,
+                            n_heads, head_dim, n_seq, l_max, block, m_blocks, top_k, out_idx,
+                            out_score, out_blocks, out_block_score, workspace, stream);
   }
   HisaPlan p = plan_hisa(nq, head_dim, n_seq, l_max, block, m_blocks, k_pooled != nullptr);
   if ((st = check_ws(workspace, workspace_bytes, p.total))) return st;
@@ -879,6 +938,89 @@ int hisa_block_filter_topk(const void* q, const float* w, const void* k, const v
   b.out_idx = out_idx;
   b.out_score = out_score;
   return hip_status(run_score_select(b, stream), "refine score/select kernel", stream);
+}
+
+size_t misa_hisa_topk_workspace_size(int32_t nq, int32_t n_heads, int32_t head_dim,
+                                     int32_t n_seq, int64_t l_max, int32_t block,
+                                     int32_t n_active_heads, int32_t m_blocks, int32_t top_k,
+                                     int32_t pooled_given) {
+  (void)top_k;
+  if (nq <= 0 || l_max <= 0 || block <= 0 || m_blocks <= 0 || n_active_heads <= 0 || n_heads <= 0)
+    return 0;
+  return plan_misa_hisa(nq, n_heads, head_dim, n_seq, l_max, block, n_active_heads, m_blocks,
+                        pooled_given != 0).total;
+}
+
+int misa_hisa_topk(const void* q, const float* w, const void* k, const void* k_pooled,
+                   int32_t dtype, const int32_t* q_seq, const int32_t* q_pos, int32_t nq,
+                   int32_t n_heads, int32_t head_dim, int32_t n_seq, int64_t l_max, int32_t block,
+                   int32_t n_active_heads, int32_t m_blocks, int32_t top_k, int32_t* out_idx,
+                   float* out_score, int32_t* out_heads, float* out_importance,
+                   int32_t* out_blocks, float* out_block_score, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream) {
+  int st = check_common(q, w, k, dtype, q_pos, nq, n_heads, head_dim, n_seq, l_max, top_k, out_idx);
+  if (st) return st;
+  if (dtype != DSA_DTYPE_BF16) return fail(DSA_EUNSUPPORTED, "MISA-HISA supports bf16 inputs only");
+  if (block < 1) return fail(DSA_EINVAL, "block must be >= 1 (got %d)", block);
+  if (n_active_heads < 1 || n_active_heads > n_heads)
+    return fail(DSA_EINVAL, "n_active_heads must be in [1, n_heads] (got %d)", n_active_heads);
+  if (m_blocks < 1) return fail(DSA_EINVAL, "m_blocks must be >= 1 (got %d)", m_blocks);
+  if (nq == 0) return DSA_OK;
+  if (k_pooled && !aligned(k_pooled, 16)) return fail(DSA_EINVAL, "k_pooled must be 16-byte aligned");
+  MisaHisaPlan p = plan_misa_hisa(nq, n_heads, head_dim, n_seq, l_max, block, n_active_heads,
+                                  m_blocks, k_pooled != nullptr);
+  if (!p.h.ok)
+    return fail(DSA_EUNSUPPORTED, "MISA-HISA needs m_blocks <= %d, m_blocks * block <= %d and "
+                "nq <= 65535", dsa::kHisaMaxBlocks, dsa::kHisaRegKeys);
+  if ((st = check_ws(workspace, workspace_bytes, p.total))) return st;
+  const uint16_t* pooled = nullptr;
+  uint16_t* partial = nullptr;
+  if ((st = hisa_setup(p.h, k, k_pooled, q_seq, q_pos, nq, n_seq, head_dim, l_max, block,
+                       workspace, stream, &pooled, &partial)))
+    return st;
+  // router: per-slice sums of max(0, q_j . kbar_b) over the pooled blocks
+  dsa::RouteArgs ra{};
+  ra.q = reinterpret_cast<const uint16_t*>(q);
+  ra.pooled = pooled;
+  ra.partial = partial;
+  ra.q_seq = q_seq;
+  ra.q_pos = q_pos;
+  ra.nq = nq;
+  ra.n_heads = n_heads;
+  ra.head_dim = head_dim;
+  ra.n_seq = n_seq;
+  ra.block = block;
+  ra.splits = p.splits;
+  ra.blocks_per_split = p.bps;
+  ra.l_max = l_max;
+  ra.m_max = p.h.m_max;
+  ra.part = at<float>(workspace, p.part);
+  if ((st = hip_status(timed(DSA_KERNEL_ROUTE, stream, [&] { return dsa::launch_route(ra, stream); }),
+                       "router kernel", stream))) return st;
+  // the h most important heads of every query
+  dsa::RouteHeadsArgs rh{};
+  rh.part = ra.part;
+  rh.w = w;
+  rh.q_seq = q_seq;
+  rh.q_pos = q_pos;
+  rh.nq = nq;
+  rh.n_heads = n_heads;
+  rh.splits = p.splits;
+  rh.h_use = n_active_heads;
+  rh.heads_stride = n_active_heads;
+  rh.n_seq = n_seq;
+  rh.l_max = l_max;
+  rh.heads = at<int32_t>(workspace, p.heads);
+  rh.out_heads = out_heads;
+  rh.out_importance = out_importance;
+  if ((st = hip_status(timed(DSA_KERNEL_ROUTE_HEADS, stream,
+                             [&] { return dsa::launch_route_heads(rh, stream); }),
+                       "head selection kernel", stream))) return st;
+  // HISA with the routed heads
+  return run_hisa_kernels(p.h, q, w, k, pooled, partial, q_seq, q_pos, rh.heads, n_active_heads,
+                          n_active_heads, nq, n_heads, head_dim, n_seq, l_max, block, m_blocks,
+                          top_k, out_idx, out_score, out_blocks, out_block_score, workspace,
+                          stream);
 }
 
 int indexer_selection_iou(const int32_t* a, const int32_t* b, int32_t nq, int32_t k,

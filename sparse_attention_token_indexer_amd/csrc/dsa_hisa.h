@@ -19,6 +19,8 @@ struct HisaArgs {
   const uint16_t* partial;     // [nq, D] pooled partial last block (prepare kernel)
   const int32_t* q_seq;        // [nq] or null
   const int32_t* q_pos;        // [nq]
+  const int32_t* heads;        // [nq, heads_stride] routed heads (first h_use), or null: all
+  int heads_stride, h_use;     // h_use = n_heads without routing
   int nq, n_heads, head_dim, n_seq, block, m_blocks, top_k;
   int64_t l_max, m_max;
   int groups;                  // workgroups per query (both passes), or

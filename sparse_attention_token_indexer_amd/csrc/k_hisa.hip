@@ -494,8 +494,8 @@ __global__ __launch_bounds__(kHT) __attribute__((amdgpu_waves_per_eu(2))) void k
   int32_t* bflag = a.bflag + (size_t)t * a.m_blocks;            // kept block + 1 (0: not yet)
 
   SC sc;
-  sc.init(a.q + (size_t)t * a.n_heads * D, a.w + (size_t)t * a.n_heads, nullptr, a.n_heads,
-          nullptr);
+  sc.init(a.q + (size_t)t * a.n_heads * D, a.w + (size_t)t * a.n_heads,
+          a.heads ? a.heads + (size_t)t * a.heads_stride : nullptr, a.h_use, nullptr);
   // ---- 1. block pass
   if (pass1) {
     for (int i = tid; i < kHistWords; i += kHT) hist[i] = 0;
@@ -720,14 +720,16 @@ hipError_t launch_hisa(const HisaArgs& a, hipStream_t stream) {
       a.sblk_n < a.ch2 / a.block + 2 || a.nq < 1 || a.nq > 65535 || a.m_blocks < 1 ||
       a.m_blocks > kHisaMaxBlocks || (int64_t)a.m_blocks * a.block > kHisaRegKeys)
     return hipErrorInvalidValue;
+  if (a.h_use < 1 || a.h_use > a.n_heads || (a.heads && a.heads_stride < a.h_use))
+    return hipErrorInvalidValue;
   if (a.head_dim == 128) {
-    if (a.n_heads <= 16) return launch_hisa_t<ScorerMfma16<128>, 4, 128>(a, stream);
-    if (a.n_heads <= 32) return launch_hisa_t<ScorerMfma32<1, 128>, 4, 128>(a, stream);
+    if (a.h_use <= 16) return launch_hisa_t<ScorerMfma16<128>, 4, 128>(a, stream);
+    if (a.h_use <= 32) return launch_hisa_t<ScorerMfma32<1, 128>, 4, 128>(a, stream);
     return launch_hisa_t<ScorerMfma32<2, 128>, 3, 128>(a, stream);
   }
   if (a.head_dim == 64) {
-    if (a.n_heads <= 16) return launch_hisa_t<ScorerMfma16<64>, 4, 64>(a, stream);
-    if (a.n_heads <= 32) return launch_hisa_t<ScorerMfma32<1, 64>, 4, 64>(a, stream);
+    if (a.h_use <= 16) return launch_hisa_t<ScorerMfma16<64>, 4, 64>(a, stream);
+    if (a.h_use <= 32) return launch_hisa_t<ScorerMfma32<1, 64>, 4, 64>(a, stream);
     return launch_hisa_t<ScorerMfma32<2, 64>, 4, 64>(a, stream);
   }
   return hipErrorInvalidValue;

@@ -103,6 +103,14 @@ def test_misa_partial_blocks_and_internal_pooling(dsa):
         _misa_case(dsa, wl, h=3, k=50, kprime=0, pos=pos, pooled=pooled)
 
 
+def test_misa_many_queries_one_router_slice(dsa):
+    """More queries than the router's workgroup target: every query's blocks fit
+    one router slice (the plan stops widening slices there)."""
+    wl = datagen.small(4, nq=600, n_seq=600, l_max=2048)
+    rows = list(range(0, 600, 37)) + [599]
+    _misa_case(dsa, wl, h=12, k=128, kprime=256, rows=rows)
+
+
 def _misa_prefill_wl(nq, L, **kw):
     # MISA's values on the prefill layout: row t at position t of one sequence
     return datagen.small(4, nq=nq, n_seq=1, l_max=L, layout="prefill", plant="points",
@@ -231,6 +239,59 @@ def test_hisa_prefill_rows(dsa):
     rows = list(range(0, 1024, 37)) + [63, 64, 65, 1023]
     _hisa_case(dsa, wl, m=6, k=200, rows=rows)
     _hisa_case(dsa, wl, m=3, k=64, seed=1, rows=rows, pooled=False)
+
+
+def _misa_hisa_case(dsa, wl, h, m, k, seed=0, pos=None, pooled=True, rows=None):
+    inp = datagen.make(wl, seed)
+    if pos is not None:
+        inp["q_pos"] = np.asarray(pos, dtype=np.int32)
+    say(f"[misa-hisa] nq={wl.nq} L={wl.l_max} H={wl.n_heads} B={wl.block} h={h} m={m} k={k} "
+        f"pooled={pooled}")
+    dev = upload(inp, wl)
+    kp = dsa.indexer_mean_pool_keys(dev["k"], wl.block) if pooled else None
+    res = dsa.misa_hisa_topk(dev["q"], dev["w"], dev["k"], dev["q_pos"], dev["q_seq"],
+                             block=wl.block, n_active_heads=h, m_blocks=m, top_k=k, k_pooled=kp,
+                             with_importance=True)
+    torch.cuda.synchronize()
+    out = {key: v.cpu().numpy() for key, v in res.items()}
+    errs = []
+    for t in (range(wl.nq) if rows is None else rows):
+        q_t, w_t, K, p = _rows(inp, wl, t)
+        pooled_ref = O.misa_pooled_for_query(K, wl.block, p)
+        I = O.misa_importance(q_t, w_t, pooled_ref)
+        Fi = np.abs(w_t) * (np.abs(q_t) @ np.abs(pooled_ref).T).sum(axis=1)
+        gi = out["importance"][t].astype(np.float64)
+        bad = np.abs(gi - I) > RTOL * I + FLOOR * Fi
+        if bad.any():
+            errs.append(f"importance q{t}: heads {np.nonzero(bad)[0][:4]}")
+        errs += check_selection(out["heads"][t], None, np.arange(wl.n_heads), I, I, h, Fi,
+                                what=f"heads q{t}")
+        heads = out["heads"][t].astype(np.int64)
+        # blocks, given the GPU's heads
+        bs, bA = O.hisa_block_scores(q_t[heads], w_t[heads], pooled_ref)
+        Fb = O.dot_magnitude(q_t[heads], w_t[heads], pooled_ref)
+        errs += check_selection(out["blocks"][t], out["block_score"][t],
+                                np.arange(pooled_ref.shape[0]), bs, bA, m, Fb,
+                                what=f"blocks q{t}")
+        # tokens, given the GPU's heads and blocks
+        r = O.misa_hisa_row(q_t, w_t, K, p, wl.block, h, m, k, heads=heads,
+                            blocks=out["blocks"][t])
+        errs += _check(out["idx"][t], out["score"][t], r["cand"], r["s"], r["A"], k,
+                       q_t, w_t, K, f"misa-hisa q{t}", heads)
+    assert not errs, "\n".join(errs[:12])
+
+
+def test_misa_hisa_reduced(dsa):
+    wl = datagen.small(5, nq=8, n_seq=8, l_max=65536, n_plant=48)
+    _misa_hisa_case(dsa, wl, h=8, m=16, k=512)
+
+
+def test_misa_hisa_partial_blocks_internal_pooling_and_prefill_rows(dsa):
+    wl = datagen.small(5, nq=6, n_seq=1, l_max=9000, layout="tail", plant="points", n_plant=60)
+    _misa_hisa_case(dsa, wl, h=4, m=8, k=200, pos=[0, 127, 128, 300, 4097, 8999], pooled=False)
+    wl = datagen.small(5, nq=1024, n_seq=1, l_max=1024, layout="prefill", plant="points",
+                       n_plant=128, block=64)
+    _misa_hisa_case(dsa, wl, h=3, m=6, k=200, rows=list(range(0, 1024, 41)) + [63, 64, 1023])
 
 
 def test_hisa_exact_ties_take_lowest_ids(dsa):
