@@ -420,15 +420,22 @@ int hisa_setup(const HisaFusedPlan& f, const void* k, const void* k_pooled, cons
   return DSA_OK;
 }
 
-// k_hisa and k_hisa_topk over the plan; heads (stride heads_stride, first
-// h_use) restricts both passes to routed heads, null uses all n_heads.
+// MISA routing of the HISA kernels: the router's per-slice head sums, from
+// which k_hisa keeps the h_use most important heads, and where it reports them.
+struct HisaRoute {
+  const float* part = nullptr;   // [nq, splits, n_heads], or null: all n_heads
+  int splits = 0, h_use = 0;
+  int32_t* out_heads = nullptr;
+  float* out_importance = nullptr;
+};
+
+// k_hisa and k_hisa_topk over the plan, over all n_heads or the routed ones.
 int run_hisa_kernels(const HisaFusedPlan& f, const void* q, const float* w, const void* k,
                      const uint16_t* pooled, const uint16_t* partial, const int32_t* q_seq,
-                     const int32_t* q_pos, const int32_t* heads, int heads_stride, int h_use,
-                     int nq, int n_heads, int head_dim, int n_seq, int64_t l_max, int block,
-                     int m_blocks, int top_k, int32_t* out_idx, float* out_score,
-                     int32_t* out_blocks, float* out_block_score, void* workspace,
-                     hipStream_t stream) {
+                     const int32_t* q_pos, const HisaRoute& route, int nq, int n_heads,
+                     int head_dim, int n_seq, int64_t l_max, int block, int m_blocks, int top_k,
+                     int32_t* out_idx, float* out_score, int32_t* out_blocks,
+                     float* out_block_score, void* workspace, hipStream_t stream) {
   dsa::HisaArgs h{};
   h.q = reinterpret_cast<const uint16_t*>(q);
   h.w = w;
@@ -437,9 +444,13 @@ int run_hisa_kernels(const HisaFusedPlan& f, const void* q, const float* w, cons
   h.partial = partial;
   h.q_seq = q_seq;
   h.q_pos = q_pos;
-  h.heads = heads;
-  h.heads_stride = heads_stride;
-  h.h_use = h_use;
+  h.heads = nullptr;
+  h.heads_stride = 0;
+  h.h_use = route.part ? route.h_use : n_heads;
+  h.route_part = route.part;
+  h.route_splits = route.splits;
+  h.out_heads = route.out_heads;
+  h.out_importance = route.out_importance;
   h.nq = nq;
   h.n_heads = n_heads;
   h.head_dim = head_dim;
@@ -469,11 +480,10 @@ int run_hisa_kernels(const HisaFusedPlan& f, const void* q, const float* w, cons
                     "HISA kernel", stream);
 }
 
-// MISA∘HISA: the HISA plan, then the router's per-slice sums and the routed
-// heads.
+// MISA∘HISA: the HISA plan, then the router's per-slice sums.
 struct MisaHisaPlan {
   HisaFusedPlan h;
-  size_t part = 0, heads = 0, total = 0;
+  size_t part = 0, total = 0;
   int splits = 1, bps = 1;
 };
 
@@ -488,7 +498,6 @@ MisaHisaPlan plan_misa_hisa(int64_t nq, int n_heads, int head_dim, int n_seq, in
   Arena A;
   A.off = p.h.total;
   p.part = A.take((size_t)nq * p.splits * n_heads * 4);
-  p.heads = A.take((size_t)nq * h_act * 4);
   p.total = A.off;
   return p;
 }
@@ -894,7 +903,7 @@ int hisa_block_filter_topk(const void* q, const float* w, const void* k, const v
     if ((st = hisa_setup(f, k, k_pooled, q_seq, q_pos, nq, n_seq, head_dim, l_max, block, workspace,
                          stream, &pooled, &partial)))
       return st;
-    return run_hisa_kernels(f, q, w, k, pooled, partial, q_seq, q_pos, nullptr, 0, n_heads, nq,
+    return run_hisa_kernels(f, q, w, k, pooled, partial, q_seq, q_pos, HisaRoute{}, nq,
                             n_heads, head_dim, n_seq, l_max, block, m_blocks, top_k, out_idx,
                             out_score, out_blocks, out_block_score, workspace, stream);
   }
@@ -997,30 +1006,16 @@ int misa_hisa_topk(const void* q, const float* w, const void* k, const void* k_p
   ra.part = at<float>(workspace, p.part);
   if ((st = hip_status(timed(DSA_KERNEL_ROUTE, stream, [&] { return dsa::launch_route(ra, stream); }),
                        "router kernel", stream))) return st;
-  // the h most important heads of every query
-  dsa::RouteHeadsArgs rh{};
-  rh.part = ra.part;
-  rh.w = w;
-  rh.q_seq = q_seq;
-  rh.q_pos = q_pos;
-  rh.nq = nq;
-  rh.n_heads = n_heads;
-  rh.splits = p.splits;
-  rh.h_use = n_active_heads;
-  rh.heads_stride = n_active_heads;
-  rh.n_seq = n_seq;
-  rh.l_max = l_max;
-  rh.heads = at<int32_t>(workspace, p.heads);
-  rh.out_heads = out_heads;
-  rh.out_importance = out_importance;
-  if ((st = hip_status(timed(DSA_KERNEL_ROUTE_HEADS, stream,
-                             [&] { return dsa::launch_route_heads(rh, stream); }),
-                       "head selection kernel", stream))) return st;
-  // HISA with the routed heads
-  return run_hisa_kernels(p.h, q, w, k, pooled, partial, q_seq, q_pos, rh.heads, n_active_heads,
-                          n_active_heads, nq, n_heads, head_dim, n_seq, l_max, block, m_blocks,
-                          top_k, out_idx, out_score, out_blocks, out_block_score, workspace,
-                          stream);
+  // HISA over the h most important heads, which k_hisa ranks from the sums
+  HisaRoute route;
+  route.part = ra.part;
+  route.splits = p.splits;
+  route.h_use = n_active_heads;
+  route.out_heads = out_heads;
+  route.out_importance = out_importance;
+  return run_hisa_kernels(p.h, q, w, k, pooled, partial, q_seq, q_pos, route, nq, n_heads,
+                          head_dim, n_seq, l_max, block, m_blocks, top_k, out_idx, out_score,
+                          out_blocks, out_block_score, workspace, stream);
 }
 
 int indexer_selection_iou(const int32_t* a, const int32_t* b, int32_t nq, int32_t k,

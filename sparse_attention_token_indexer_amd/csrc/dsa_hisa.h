@@ -21,6 +21,15 @@ struct HisaArgs {
   const int32_t* q_pos;        // [nq]
   const int32_t* heads;        // [nq, heads_stride] routed heads (first h_use), or null: all
   int heads_stride, h_use;     // h_use = n_heads without routing
+  // MISA routing inside the kernel (route_part non-null, heads null): every
+  // workgroup adds the router's per-slice head sums [nq, route_splits,
+  // n_heads] in slice order, I_j = |w_j| * sum, and keeps the h_use heads of
+  // largest I (ties to the lower index); the first block-pass workgroup of a
+  // query reports them (out_heads [nq, h_use], out_importance [nq, n_heads]).
+  const float* route_part;
+  int route_splits;
+  int32_t* out_heads;
+  float* out_importance;
   int nq, n_heads, head_dim, n_seq, block, m_blocks, top_k;
   int64_t l_max, m_max;
   int groups;                  // workgroups per query (both passes), or

@@ -429,6 +429,49 @@ DSA_DEVICE void select_lds(const uint2* ent, int n, int top_k, int32_t* out_idx,
   }
 }
 
+// MISA head routing finished inside a workgroup: the router's per-slice sums
+// added in slice order, I_j = |w_j| * sum, the h_use heads of largest I (ties
+// to the lower index) into s_heads.  The arithmetic and order are fixed, so
+// every workgroup of a query keeps the same heads.  The query's sums are
+// contiguous ([slice][head]): they come into buf (buf_words words, free until
+// the block pass) with one coalesced load per round, thread j then adds head
+// j's slices.
+static_assert(kHT >= 64, "one thread per head in the routing step");
+DSA_DEVICE void hisa_route_heads(const HisaArgs& a, int t, float* buf, int buf_words,
+                                 int32_t* s_heads, float* s_I, bool report) {
+  const int H = a.n_heads, tid = (int)threadIdx.x;
+  const int per = buf_words / H;                               // slices per round
+  const float* part = a.route_part + (size_t)t * a.route_splits * H;
+  float tot = 0.f;
+  for (int s0 = 0; s0 < a.route_splits; s0 += per) {
+    const int ns = a.route_splits - s0 < per ? a.route_splits - s0 : per;
+    for (int i = tid; i < ns * H; i += (int)blockDim.x) buf[i] = part[(size_t)s0 * H + i];
+    __syncthreads();
+    if (tid < H)
+      for (int sp = 0; sp < ns; ++sp) tot += buf[sp * H + tid];
+    __syncthreads();
+  }
+  if (tid < H) {
+    const float I = fabsf(a.w[(size_t)t * H + tid]) * tot;
+    s_I[tid] = I;
+    if (report && a.out_importance) a.out_importance[(size_t)t * H + tid] = I;
+  }
+  __syncthreads();
+  if (tid < H) {
+    const float Ij = s_I[tid];
+    int rank = 0;
+    for (int i = 0; i < H; ++i) {
+      const float Ii = s_I[i];
+      rank += (Ii > Ij) || (Ii == Ij && i < tid);
+    }
+    if (rank < a.h_use) {
+      s_heads[rank] = tid;
+      if (report && a.out_heads) a.out_heads[(size_t)t * a.h_use + rank] = tid;
+    }
+  }
+  __syncthreads();
+}
+
 template <class SC, int NF, int D>
 __global__ __launch_bounds__(kHT) __attribute__((amdgpu_waves_per_eu(2))) void k_hisa(HisaArgs a) {
   extern __shared__ uint32_t smem[];
@@ -447,6 +490,8 @@ __global__ __launch_bounds__(kHT) __attribute__((amdgpu_waves_per_eu(2))) void k
   uint2* cl = tie + 64;                                         // [kHisaCandCap] block candidates
   __shared__ uint32_t s_cnt, s_ln, s_out, s_sel, s_go, s_above, s_nb;
   __shared__ int s_b;
+  __shared__ int32_t s_heads[64];
+  __shared__ float s_I[64];
 
   // grid: (groups, nq), each workgroup taking part in both passes; or, with
   // split, a 1-D grid of the block-pass items of every query followed by the
@@ -479,6 +524,12 @@ __global__ __launch_bounds__(kHT) __attribute__((amdgpu_waves_per_eu(2))) void k
         blocks[i] = -1;
         if (bscore) bscore[i] = -__builtin_inff();
       }
+      if (a.route_part) {
+        for (int j = tid; j < a.h_use; j += kHT)
+          if (a.out_heads) a.out_heads[(size_t)t * a.h_use + j] = -1;
+        for (int j = tid; j < a.n_heads; j += kHT)
+          if (a.out_importance) a.out_importance[(size_t)t * a.n_heads + j] = 0.f;
+      }
     }
     return;
   }
@@ -493,9 +544,15 @@ __global__ __launch_bounds__(kHT) __attribute__((amdgpu_waves_per_eu(2))) void k
   uint32_t* sy = a.sync + (size_t)t * kHisaSyncWords;
   int32_t* bflag = a.bflag + (size_t)t * a.m_blocks;            // kept block + 1 (0: not yet)
 
+  const int32_t* heads_t = a.heads ? a.heads + (size_t)t * a.heads_stride : nullptr;
+  if (a.route_part) {
+    hisa_route_heads(a, t, reinterpret_cast<float*>(hist), kHistWords, s_heads, s_I,
+                     pass1 && g == 0);
+    heads_t = s_heads;
+  }
   SC sc;
-  sc.init(a.q + (size_t)t * a.n_heads * D, a.w + (size_t)t * a.n_heads,
-          a.heads ? a.heads + (size_t)t * a.heads_stride : nullptr, a.h_use, nullptr);
+  sc.init(a.q + (size_t)t * a.n_heads * D, a.w + (size_t)t * a.n_heads, heads_t, a.h_use,
+          nullptr);
   // ---- 1. block pass
   if (pass1) {
     for (int i = tid; i < kHistWords; i += kHT) hist[i] = 0;
@@ -721,6 +778,8 @@ hipError_t launch_hisa(const HisaArgs& a, hipStream_t stream) {
       a.m_blocks > kHisaMaxBlocks || (int64_t)a.m_blocks * a.block > kHisaRegKeys)
     return hipErrorInvalidValue;
   if (a.h_use < 1 || a.h_use > a.n_heads || (a.heads && a.heads_stride < a.h_use))
+    return hipErrorInvalidValue;
+  if (a.route_part && (a.heads || a.route_splits < 1 || a.n_heads > 64))
     return hipErrorInvalidValue;
   if (a.head_dim == 128) {
     if (a.h_use <= 16) return launch_hisa_t<ScorerMfma16<128>, 4, 128>(a, stream);
