@@ -35,7 +35,7 @@ Readings where the pages are silent (each also listed with the design notes):
   score = the indexer formula with all heads applied to the pooled keys;
   R9 no forced sink/local blocks; R10 MISA dagger ranks candidates by the
   routed score and returns full H_I-head scores; R11 ties go to the lower
-  index, output is a set padded with (-1, -inf), -0.0 equals +0.0; R13 the
+  index, output is a set padded with (-1, -inf), -0.0 equals +0.0; R18 the
   composition of the two (MISA summary, "method": the head axis; HISA review,
   section 3: the token axis) routes h heads with MISA's router and runs both
   HISA stages with only those heads, original weights kept.
@@ -59,7 +59,7 @@ tests live in tests/test_oracle_*.py):
                    hand-worked example.  The block-score formula (R8) is
                    "parity unpinned".
   misa_hisa        h = H_I equals HISA; m = M equals MISA; pure-Python brute
-                   force.  The composition itself (R13) is a reading of the
+                   force.  The composition itself (R18) is a reading of the
                    pages, which name the combination but give no steps.
   iou              hand-computed cases, IoU(A, A) = 1, disjoint = 0
 """
@@ -282,7 +282,7 @@ def hisa_row(q_t, w_t, K_seq, pos: int, B: int, m: int, k: int,
 def misa_hisa_row(q_t, w_t, K_seq, pos: int, B: int, h: int, m: int, k: int,
                   heads: Optional[np.ndarray] = None,
                   blocks: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
-    """MISA∘HISA (R13): route to h heads from the pooled keys as MISA does,
+    """MISA∘HISA (R18): route to h heads from the pooled keys as MISA does,
     then run HISA with only those heads (original weights kept) in both of its
     stages: block scores over the pooled keys and token scores inside the kept
     blocks.  ``heads`` / ``blocks`` skip the routing / block stage (for
