@@ -54,16 +54,22 @@ __global__ __launch_bounds__(kRT) void k_route(RouteArgs a) {
                                     : zero_bf16x8();
     }
     const int n_tiles = (int)((b1 - b0 + 31) / 32);
-    for (int tile = wv; tile < n_tiles; tile += kRT / 64) {
+    // each wave walks every (kRT / 64)-th tile, the next one's pooled rows
+    // loaded while the current one is multiplied
+    auto load = [&](bf16x8 (&kb)[S], int tile) {
       const int64_t b = b0 + (int64_t)tile * 32 + n;
-      const bool valid = b < b1;
-      const int64_t bb = valid ? b : b0;
+      const int64_t bb = b < b1 ? b : b0;
       const uint16_t* rowp = (partial_last && bb == M - 1)
                                  ? a.partial + (size_t)t * D
                                  : a.pooled + ((size_t)seq * (size_t)a.m_max + (size_t)bb) * D;
-      bf16x8 kb[S];
 #pragma unroll
       for (int s = 0; s < S; ++s) kb[s] = load_bf16x8(rowp + 8 * h + 16 * s);
+    };
+    bf16x8 ka[S], kn[S];
+    if (wv < n_tiles) load(ka, wv);
+    for (int tile = wv; tile < n_tiles; tile += kRT / 64) {
+      if (tile + kRT / 64 < n_tiles) load(kn, tile + kRT / 64);
+      const bool valid = b0 + (int64_t)tile * 32 + n < b1;
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
         f32x16 acc;
@@ -71,12 +77,14 @@ __global__ __launch_bounds__(kRT) void k_route(RouteArgs a) {
         for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
         for (int s = 0; s < S; ++s)
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ht][s], kb[s], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ht][s], ka[s], acc, 0, 0, 0);
         if (valid) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) hsum[ht][r] += relu(acc[r]);
         }
       }
+#pragma unroll
+      for (int s = 0; s < S; ++s) ka[s] = kn[s];
     }
   }
   // sum over the 32 block columns held by lanes with the same half h
