@@ -61,6 +61,10 @@ tests live in tests/test_oracle_*.py):
   misa_hisa        h = H_I equals HISA; m = M equals MISA; pure-Python brute
                    force.  The composition itself (R18) is a reading of the
                    pages, which name the combination but give no steps.
+  dosa_*           the bounds bracket every score; the selection equals
+                   dense_row's; h = H_I collapses both bounds onto the score
+                   (survivors are exactly the keys at or above the k-th
+                   score); brute force on tiny inputs.
   iou              hand-computed cases, IoU(A, A) = 1, disjoint = 0
 """
 from __future__ import annotations
@@ -275,6 +279,45 @@ def hisa_row(q_t, w_t, K_seq, pos: int, B: int, m: int, k: int,
     fine = rescore_row(q_t, w_t, K_seq, cand, k)
     fine.update({"bs": bs, "bA": bA, "blocks": np.asarray(blocks), "pooled": pooled})
     return fine
+
+
+# ------------------------------------------------- DoSA-style certificate ---
+
+def dosa_certificate(q_t, w_t, K_rows, k: int, h: int) -> Dict[str, np.ndarray]:
+    """A sound score certificate for exact top-k pruning (DoSA blog, sections
+    1 and 3: screen with part of the heads, bound the rest, prune, rescore the
+    survivors; the page gives no formulas, so these bounds are our own).
+    Screening heads S: the h heads of largest |w_j| * ||q_j|| (ties to the
+    lower index).  For every other head, Cauchy-Schwarz gives
+    0 <= max(0, q_j . k) <= ||q_j|| * ||k||, so with s_S the exact screened sum
+      LB(u) = s_S(u) + ||k_u|| * sum_{j not in S, w_j < 0} w_j ||q_j||
+      UB(u) = s_S(u) + ||k_u|| * sum_{j not in S, w_j > 0} w_j ||q_j||
+    bracket the full score.  The k keys of largest LB have true scores >= tau
+    (the k-th largest LB), so the k-th largest score is >= tau and a key with
+    UB < tau scores strictly below it: the exact top-k (ties included) lies
+    among the survivors UB >= tau."""
+    D = head_dots(q_t, K_rows)                         # [H, n]
+    qn = np.sqrt((q_t * q_t).sum(axis=1))
+    kn = np.sqrt((K_rows * K_rows).sum(axis=1))
+    S, _ = top_k(np.abs(w_t) * qn, np.arange(w_t.size), h)
+    rest = np.setdiff1d(np.arange(w_t.size), S)
+    sS = w_t[S] @ np.maximum(D[S], 0.0)
+    LB = sS + kn * (np.minimum(w_t[rest], 0.0) * qn[rest]).sum()
+    UB = sS + kn * (np.maximum(w_t[rest], 0.0) * qn[rest]).sum()
+    n = LB.size
+    tau = np.sort(LB)[n - min(k, n)] if n else -np.inf
+    return {"heads": S, "LB": LB, "UB": UB, "tau": tau, "survive": UB >= tau}
+
+
+def dosa_row(q_t, w_t, K_seq, pos: int, k: int, h: int) -> Dict[str, np.ndarray]:
+    """Exact top-k through the certificate: full scores for the survivors
+    only, then their top-k; equals dense_row's selection."""
+    ids = prefix(pos)
+    c = dosa_certificate(q_t, w_t, K_seq[:pos + 1], k, h)
+    keep = ids[c["survive"]]
+    s, A = indexer_scores(q_t, w_t, K_seq[keep])
+    idx, val = top_k(s, keep, k)
+    return {"idx": idx, "val": val, "cand": keep, "s": s, "A": A, "cert": c}
 
 
 # -------------------------------------------------------------- MISA∘HISA ---

@@ -378,3 +378,78 @@ def test_planted_selection_mistakes_fail_a_pin(gold):
     assert O.top_k(np.zeros(10), np.arange(10), 3)[0].tolist() == [0, 1, 2]
     assert np.lexsort((-np.arange(10), -np.zeros(10)))[:3].tolist() != [0, 1, 2]    # tie flip
     assert sorted(np.argsort(s)[:3].tolist()) != sorted(want)                         # ascending
+
+
+# ------------------------------------------------- DoSA-style certificate ---
+
+def _brute_certificate(q, w, K, k, h):
+    """The certificate written out with loops: screening heads by |w_j| ||q_j||
+    (ties to the lower index), exact screened sum, Cauchy-Schwarz for the rest."""
+    import math
+    H, n = len(w), len(K)
+    qn = [math.sqrt(sum(x * x for x in q[j])) for j in range(H)]
+    order = sorted(range(H), key=lambda j: (-abs(w[j]) * qn[j], j))
+    S, rest = order[:h], order[h:]
+    LB, UB = [], []
+    for u in range(n):
+        kn = math.sqrt(sum(x * x for x in K[u]))
+        sS = sum(w[j] * max(0.0, sum(a * b for a, b in zip(q[j], K[u]))) for j in S)
+        LB.append(sS + kn * sum(min(w[j], 0.0) * qn[j] for j in rest))
+        UB.append(sS + kn * sum(max(w[j], 0.0) * qn[j] for j in rest))
+    tau = sorted(LB)[n - min(k, n)]
+    return sorted(S), LB, UB, tau
+
+
+def test_dosa_certificate_brute_bounds_and_exact_selection():
+    """The bounds against the loop form, bracketing every score; the pruned
+    selection equals the dense one; with every head screened both bounds are
+    the score and the survivors are exactly the keys at or above the k-th."""
+    rng = np.random.default_rng(31)
+    for it in range(60):
+        H = int(rng.integers(1, 7)); d = int(rng.integers(1, 9)); L = int(rng.integers(1, 80))
+        q = rng.standard_normal((H, d)); w = rng.standard_normal(H)
+        K = rng.standard_normal((L, d))
+        if it % 3 == 0:                              # a few keys along one head's query
+            j = int(rng.integers(0, H))
+            K[rng.integers(0, L, size=max(1, L // 8))] = q[j] + 0.3 * rng.standard_normal(d)
+        pos = int(rng.integers(0, L)); k = int(rng.integers(1, 12)); h = int(rng.integers(1, H + 1))
+        c = O.dosa_certificate(q, w, K[:pos + 1], k, h)
+        S, LB, UB, tau = _brute_certificate(q.tolist(), w.tolist(), K[:pos + 1].tolist(), k, h)
+        assert sorted(c["heads"].tolist()) == S
+        assert np.allclose(c["LB"], LB, rtol=1e-12, atol=1e-12)
+        assert np.allclose(c["UB"], UB, rtol=1e-12, atol=1e-12)
+        s, _ = O.indexer_scores(q, w, K[:pos + 1])
+        assert (c["LB"] <= s + 1e-9).all() and (s <= c["UB"] + 1e-9).all()
+        r, dref = O.dosa_row(q, w, K, pos, k, h), O.dense_row(q, w, K, pos, k)
+        assert sorted(r["idx"].tolist()) == sorted(dref["idx"].tolist())
+    # integer inputs, every head screened: exact arithmetic, bounds = score
+    for _ in range(20):
+        H = int(rng.integers(1, 5)); d = int(rng.integers(1, 6)); L = int(rng.integers(2, 50))
+        q, w, K = _int_inputs(rng, H, d, L)
+        k = int(rng.integers(1, L + 1))
+        c = O.dosa_certificate(q, w, K, k, H)
+        s, _ = O.indexer_scores(q, w, K)
+        assert np.array_equal(c["LB"], s) and np.array_equal(c["UB"], s)
+        kth = np.sort(s)[L - k]
+        assert np.array_equal(c["survive"], s >= kth)
+
+
+@pytest.mark.parametrize("wid,row", [(2, 0), (3, 32767)])
+def test_dosa_certificate_does_not_prune_the_synthetic_workloads(wid, row):
+    """Measured, not a property of the method: on the dense decode and dense
+    prefill inputs (Gaussian q, k in 128 dimensions) the Cauchy-Schwarz slack
+    of the unscreened heads (about ||q|| ||k|| per head) dwarfs the spread of
+    the scores, so even 48 of 64 screened heads leave over 90 % of the keys
+    alive.  Exactness still holds."""
+    import datagen
+    wl = datagen.WORKLOADS[wid]
+    q, w = datagen.queries(wl, 0)
+    q_seq, q_pos = datagen.positions(wl)
+    K = O.to_f64(datagen.keys(wl, int(q_seq[row]), q, w, 0), wl.dtype)
+    q_t, w_t, pos = O.to_f64(q[row], wl.dtype), w[row].astype(np.float64), int(q_pos[row])
+    for h in (16, 48):
+        c = O.dosa_certificate(q_t, w_t, K[:pos + 1], wl.top_k, h)
+        assert c["survive"].mean() > 0.9, (h, c["survive"].mean())
+    r = O.dosa_row(q_t, w_t, K, pos, wl.top_k, 48)
+    dref = O.dense_row(q_t, w_t, K, pos, wl.top_k)
+    assert np.array_equal(np.sort(r["idx"]), np.sort(dref["idx"]))
