@@ -129,3 +129,25 @@ def iou(a: Sequence[int], b: Sequence[int]) -> float:
     if not (sa or sb):
         return 1.0
     return len(sa & sb) / len(sa | sb)
+
+
+# ------------------------------------------- sparse attention over the list --
+
+def sparse_mla(q_t: Sequence[Sequence[float]], rows: Sequence[Sequence[float]],
+               idx_t: Sequence[int], d_v: int, scale: float) -> List[List[float]]:
+    """Softmax attention of every head over the listed rows (entries outside
+    the rows are skipped), value = the first d_v entries of each row; loops
+    and math.exp only."""
+    sel = [i for i in idx_t if 0 <= i < len(rows)]
+    out = []
+    for qh in q_t:
+        if not sel:
+            out.append([0.0] * d_v)
+            continue
+        s = [scale * dot(qh, rows[i]) for i in sel]
+        top = max(s)
+        e = [math.exp(x - top) for x in s]
+        tot = sum(e)
+        out.append([sum(e[n] * rows[sel[n]][c] for n in range(len(sel))) / tot
+                    for c in range(d_v)])
+    return out
