@@ -191,6 +191,38 @@ int misa_hisa_topk(const void* q, const float* w, const void* k, const void* k_p
                    size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Sparse attention over the selected index list, the operator the indexer
+ * feeds (HISA review, key terms and section 3: the selected indices go to
+ * Sparse MLA unchanged; IndexCache review, section 1: O(L k) attention with
+ * k selected tokens).  The pages give no formula; the reading taken is
+ * scaled-softmax attention in absorbed multi-head latent attention form: one
+ * latent row c[s, u] of d_qk = 576 values per token is the key of every head,
+ * its first d_v = 512 values are the value, and for query t and head h
+ *   o[t, h] = sum_i softmax_i(softmax_scale * q[t, h] . c[s_t, idx[t, i]])
+ *             * c[s_t, idx[t, i], 0:512]
+ * over the entries of idx[t] inside the prefix 0..q_pos[t] (others, such as
+ * the -1 padding of the top-k outputs, are skipped; a repeated entry counts
+ * each time).  A query with no valid entry, or with an invalid (seq, pos),
+ * gets zeros.
+ *   q [nq, n_heads, 576] bf16;  kv [n_seq, l_max, 576] bf16 latent cache;
+ *   q_seq [nq] int32 or NULL (all on cache 0);  q_pos [nq] int32;
+ *   idx [nq, top_k] int32 (e.g. the out_idx of an indexer call);
+ *   out [nq, n_heads, 512] bf16.
+ * fp32 accumulation; probabilities rounded to bf16 for the value product.
+ * Only DSA_DTYPE_BF16, d_qk = 576, d_v = 512, n_heads in {32, 64, 96, 128},
+ * 1 <= top_k <= 32768 (DSA_EUNSUPPORTED otherwise).  q, kv and out 16-byte
+ * aligned.  The workspace holds the per-slice partial outputs when a query's
+ * list is split over several workgroups (zero bytes otherwise).
+ */
+size_t sparse_mla_workspace_size(int32_t nq, int32_t n_heads, int32_t d_qk, int32_t d_v,
+                                 int32_t top_k);
+int sparse_mla_attention(const void* q, const void* kv, int32_t dtype, const int32_t* q_seq,
+                         const int32_t* q_pos, const int32_t* idx, int32_t nq, int32_t n_heads,
+                         int32_t d_qk, int32_t d_v, int32_t n_seq, int64_t l_max, int32_t top_k,
+                         float softmax_scale, void* out, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Selection agreement (MISA summary, "results"; HISA review, section 3): per
  * query IoU = |A & B| / |A | B| over the non-negative entries of a[t, :] and
  * b[t, :] (two empty rows give 1).  Rows must hold no duplicate indices.
@@ -223,7 +255,8 @@ int indexer_selection_iou(const int32_t* a, const int32_t* b, int32_t nq, int32_
 #define DSA_KERNEL_ROUTE_HEADS 11 /* MISA head selection (prefill shape) */
 #define DSA_KERNEL_PREFILL_ROUTED 12 /* MISA routed scoring on the prefill shape */
 #define DSA_KERNEL_HISA 13        /* HISA in one kernel: blocks, top-m, tokens, top-k */
-#define DSA_KERNEL_KINDS 14
+#define DSA_KERNEL_MLA 14         /* sparse attention over the index list (+ slice merge) */
+#define DSA_KERNEL_KINDS 15
 int dsa_kernel_timing(int enable);
 int dsa_kernel_timing_read(int32_t kind, int64_t* launches, double* total_ms, double* min_ms,
                            double* max_ms);

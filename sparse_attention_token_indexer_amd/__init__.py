@@ -49,6 +49,9 @@ _SIGS = {
     "misa_hisa_topk": ([_c_p, _c_p, _c_p, _c_p, _i32, _c_p, _c_p, _i32, _i32, _i32, _i32, _i64,
                         _i32, _i32, _i32, _i32, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _sz,
                         _c_p], ctypes.c_int),
+    "sparse_mla_workspace_size": ([_i32, _i32, _i32, _i32, _i32], _sz),
+    "sparse_mla_attention": ([_c_p, _c_p, _i32, _c_p, _c_p, _c_p, _i32, _i32, _i32, _i32, _i32,
+                              _i64, _i32, ctypes.c_float, _c_p, _c_p, _sz, _c_p], ctypes.c_int),
     "indexer_selection_iou": ([_c_p, _c_p, _i32, _i32, _c_p, _c_p], ctypes.c_int),
     "dsa_kernel_timing": ([ctypes.c_int], ctypes.c_int),
     "dsa_kernel_timing_read": ([_i32, ctypes.POINTER(_i64), ctypes.POINTER(ctypes.c_double),
@@ -60,7 +63,7 @@ _SIGS = {
 KERNEL_KINDS = {
     "prepare": 0, "score_tokens": 1, "score_pooled": 2, "score_list": 3, "score_blocks": 4,
     "route": 5, "pool": 6, "iou": 7, "prefill": 8, "rowselect": 9, "merge": 10,
-    "route_heads": 11, "prefill_routed": 12, "hisa": 13,
+    "route_heads": 11, "prefill_routed": 12, "hisa": 13, "mla": 14,
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -339,6 +342,48 @@ def misa_hisa_topk(q, w, k, q_pos, q_seq=None, *, block: int, n_active_heads: in
     return out
 
 
+def sparse_mla_workspace_size(nq, n_heads, d_qk, d_v, top_k) -> int:
+    return int(lib().sparse_mla_workspace_size(nq, n_heads, d_qk, d_v, top_k))
+
+
+def sparse_mla_attention(q, kv, q_pos, idx, q_seq=None, *, softmax_scale: float, out=None,
+                         workspace=None) -> torch.Tensor:
+    """Attention of every query's heads over the latent rows its index list
+    names (absorbed-MLA form: q [nq, H, 576], kv [n_seq, L, 576], the first
+    512 values of a row are its value).  Returns out [nq, H, 512] bf16."""
+    _need(q, "q", torch.bfloat16, 3)
+    dev = q.device
+    _need(kv, "kv", torch.bfloat16, 3, dev)
+    _need(q_pos, "q_pos", torch.int32, 1, dev)
+    _need(idx, "idx", torch.int32, 2, dev)
+    nq, H, d_qk = q.shape
+    n_seq, l_max, d_kv = kv.shape
+    if d_kv != d_qk:
+        raise ValueError("q and kv rows must have the same width")
+    if q_pos.shape[0] != nq or idx.shape[0] != nq:
+        raise ValueError("q_pos and idx need one row per query")
+    if q_seq is not None:
+        _need(q_seq, "q_seq", torch.int32, 1, dev)
+        if q_seq.shape[0] != nq:
+            raise ValueError("q_seq needs one entry per query")
+    top_k = idx.shape[1]
+    d_v = 512
+    if out is None:
+        out = torch.empty((nq, H, d_v), dtype=torch.bfloat16, device=dev)
+    else:
+        _need(out, "out", torch.bfloat16, 3, dev)
+        if tuple(out.shape) != (nq, H, d_v):
+            raise ValueError("out must be [nq, H, 512]")
+    nbytes = sparse_mla_workspace_size(nq, H, d_qk, d_v, top_k)
+    ws = _workspace(nbytes, dev, workspace)
+    st = lib().sparse_mla_attention(_ptr(q), _ptr(kv), DSA_DTYPE_BF16, _ptr(q_seq), _ptr(q_pos),
+                                    _ptr(idx), nq, H, d_qk, d_v, n_seq, l_max, top_k,
+                                    float(softmax_scale), _ptr(out), _ptr(ws), nbytes,
+                                    _stream(dev))
+    _check(st, "sparse_mla_attention")
+    return out
+
+
 def indexer_selection_iou(a: torch.Tensor, b: torch.Tensor,
                           out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Per-row IoU of two [nq, k] int32 selections (padding -1 ignored)."""
@@ -378,5 +423,7 @@ __all__ = [
     "indexer_mean_pool_keys",
     "misa_route_score_topk", "misa_route_score_topk_workspace_size",
     "hisa_block_filter_topk", "hisa_block_filter_topk_workspace_size",
+    "misa_hisa_topk", "misa_hisa_topk_workspace_size",
+    "sparse_mla_attention", "sparse_mla_workspace_size",
     "indexer_selection_iou",
 ]

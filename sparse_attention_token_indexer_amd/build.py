@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(os.path.dirname(HERE), "_build")
 LIB = os.path.join(HERE, "libdsa_indexer.so")
 SOURCES = ["api.hip", "k_score_select.hip", "k_prefill.hip", "k_prefill_routed.hip", "k_pool.hip",
-           "k_route.hip", "k_hisa.hip",
+           "k_route.hip", "k_hisa.hip", "k_mla.hip",
            "k_iou.hip"]
 ARCH = "gfx950"
 

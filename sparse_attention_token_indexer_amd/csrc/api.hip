@@ -12,6 +12,7 @@
 
 #include "dsa_hisa.h"
 #include "dsa_internal.h"
+#include "dsa_mla.h"
 
 namespace {
 
@@ -1016,6 +1017,94 @@ int misa_hisa_topk(const void* q, const float* w, const void* k, const void* k_p
   return run_hisa_kernels(p.h, q, w, k, pooled, partial, q_seq, q_pos, route, nq, n_heads,
                           head_dim, n_seq, l_max, block, m_blocks, top_k, out_idx, out_score,
                           out_blocks, out_block_score, workspace, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Sparse attention: each query's list in `splits` slices of whole 32-row
+// steps, enough slices for about kTargetWorkgroups / 2 workgroups (one
+// 8-wave workgroup fills a compute unit), at most kMlaMaxTiles steps each.
+struct MlaPlan {
+  int splits = 1, tiles_per_split = 1;
+  size_t part_o = 0, part_ml = 0, total = 0;
+};
+
+MlaPlan plan_mla(int64_t nq, int n_heads, int top_k) {
+  MlaPlan p;
+  const int64_t tiles = cdiv(top_k, dsa::kMlaTile);
+  int64_t splits = std::max<int64_t>(1, cdiv(kTargetWorkgroups / 2, nq));
+  splits = std::min<int64_t>({splits, tiles, dsa::kMlaMaxSplits});
+  splits = std::max<int64_t>(splits, cdiv(tiles, dsa::kMlaMaxTiles));
+  p.tiles_per_split = (int)cdiv(tiles, splits);
+  p.splits = (int)cdiv(tiles, p.tiles_per_split);
+  if (p.splits > 1) {
+    Arena A;
+    p.part_o = A.take((size_t)nq * p.splits * n_heads * dsa::kMlaDv * 4);
+    p.part_ml = A.take((size_t)nq * p.splits * n_heads * 8);
+    p.total = A.off;
+  }
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sparse_mla_workspace_size(int32_t nq, int32_t n_heads, int32_t d_qk, int32_t d_v,
+                                 int32_t top_k) {
+  (void)d_qk;
+  (void)d_v;
+  if (nq <= 0 || n_heads <= 0 || top_k <= 0 || top_k > dsa::kMlaMaxTopK) return 0;
+  return plan_mla(nq, n_heads, top_k).total;
+}
+
+int sparse_mla_attention(const void* q, const void* kv, int32_t dtype, const int32_t* q_seq,
+                         const int32_t* q_pos, const int32_t* idx, int32_t nq, int32_t n_heads,
+                         int32_t d_qk, int32_t d_v, int32_t n_seq, int64_t l_max, int32_t top_k,
+                         float softmax_scale, void* out, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  if (dtype != DSA_DTYPE_BF16) return fail(DSA_EUNSUPPORTED, "sparse attention supports bf16 only");
+  if (d_qk != dsa::kMlaDqk || d_v != dsa::kMlaDv)
+    return fail(DSA_EUNSUPPORTED, "d_qk must be %d and d_v %d (got %d, %d)", dsa::kMlaDqk,
+                dsa::kMlaDv, d_qk, d_v);
+  if (n_heads < 32 || n_heads > 128 || n_heads % 32)
+    return fail(DSA_EUNSUPPORTED, "n_heads must be 32, 64, 96 or 128 (got %d)", n_heads);
+  if (top_k < 1 || top_k > dsa::kMlaMaxTopK)
+    return fail(DSA_EUNSUPPORTED, "top_k must be in [1, %d] (got %d)", dsa::kMlaMaxTopK, top_k);
+  if (nq < 0 || n_seq < 1 || l_max < 1) return fail(DSA_EINVAL, "bad nq / n_seq / l_max");
+  if (!(softmax_scale > 0.f) || !(softmax_scale < 1e30f))
+    return fail(DSA_EINVAL, "softmax_scale must be positive and finite");
+  if (nq == 0) return DSA_OK;
+  if (!q || !kv || !q_pos || !idx || !out)
+    return fail(DSA_EINVAL, "q, kv, q_pos, idx and out must not be NULL");
+  if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(out, 16))
+    return fail(DSA_EINVAL, "q, kv and out must be 16-byte aligned");
+  if (!aligned(q_pos, 4) || !aligned(idx, 4) || (q_seq && !aligned(q_seq, 4)))
+    return fail(DSA_EINVAL, "q_seq, q_pos and idx must be 4-byte aligned");
+  const MlaPlan p = plan_mla(nq, n_heads, top_k);
+  int st;
+  if ((st = check_ws(workspace, workspace_bytes, p.total))) return st;
+  dsa::MlaArgs a{};
+  a.q = reinterpret_cast<const uint16_t*>(q);
+  a.kv = reinterpret_cast<const uint16_t*>(kv);
+  a.q_seq = q_seq;
+  a.q_pos = q_pos;
+  a.idx = idx;
+  a.nq = nq;
+  a.n_heads = n_heads;
+  a.n_seq = n_seq;
+  a.top_k = top_k;
+  a.splits = p.splits;
+  a.tiles_per_split = p.tiles_per_split;
+  a.l_max = l_max;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.out = reinterpret_cast<uint16_t*>(out);
+  a.part_o = p.splits > 1 ? at<float>(workspace, p.part_o) : nullptr;
+  a.part_ml = p.splits > 1 ? at<float2>(workspace, p.part_ml) : nullptr;
+  return hip_status(timed(DSA_KERNEL_MLA, stream, [&] { return dsa::launch_sparse_mla(a, stream); }),
+                    "sparse attention kernel", stream);
 }
 
 int indexer_selection_iou(const int32_t* a, const int32_t* b, int32_t nq, int32_t k,

@@ -1,0 +1,159 @@
+"""GPU parity of the sparse attention over the selected index list.
+
+Every checked output value must satisfy
+    |o_gpu - o| <= 2^-7 * sum_i p_i |v_i| + 2^-8 * |o|
+with o and the weights p from the float64 oracle.  The kernel's own error:
+bf16 rounding of each probability before the value product (relative 2^-9
+per term, so at most 2^-9 * sum_i p_i |v_i| over the row, and the same again
+for the sum in the denominator, which is kept unrounded), float32 scores and
+accumulation (relative ~2^-20), and the bf16 rounding of the output (2^-9
+|o|).  The bound above leaves a factor of two over that.
+"""
+import numpy as np
+import pytest
+import torch
+
+import datagen
+from datagen import mla as M
+from oracle import attention as A
+
+from _helpers import say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_attention_token_indexer_amd as m
+    m.lib()
+    return m
+
+
+def _bf16(x: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def _f64(bits: np.ndarray) -> np.ndarray:
+    return datagen.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def _check_rows(o, q, rows_of, idx, qs, qp, wl, rows, what):
+    errs = []
+    for t in rows:
+        kv_rows = rows_of(int(qs[t]), int(qp[t]))
+        ref, mag = A.sparse_mla_row(_f64(q[t]), kv_rows, idx[t], wl.d_v, wl.scale)
+        bad = np.abs(o[t] - ref) > 2.0 ** -7 * mag + 2.0 ** -8 * np.abs(ref)
+        if bad.any():
+            h, c = np.argwhere(bad)[0]
+            errs.append(f"{what} q{t}: {int(bad.sum())} values off, first head {h} col {c}: "
+                        f"gpu {o[t, h, c]} ref {ref[h, c]} mag {mag[h, c]}")
+    assert not errs, "\n".join(errs[:8])
+
+
+def _case(dsa, wl, seed=0, idx=None, qs=None, qp=None, rows=None, what="mla"):
+    q = M.queries(wl, seed)
+    C = M.cache(wl, seed)
+    qs0, qp0 = M.positions(wl)
+    qs = qs0 if qs is None else np.asarray(qs, dtype=np.int32)
+    qp = qp0 if qp is None else np.asarray(qp, dtype=np.int32)
+    idx = M.index_lists(wl, seed) if idx is None else np.asarray(idx, dtype=np.int32)
+    say(f"[{what}] nq={wl.nq} L={wl.l_max} H={wl.n_heads} k={idx.shape[1]} "
+        f"ws={dsa.sparse_mla_workspace_size(wl.nq, wl.n_heads, wl.d_qk, wl.d_v, idx.shape[1])}")
+    out = dsa.sparse_mla_attention(_bf16(q), _bf16(C), torch.from_numpy(qp).cuda(),
+                                   torch.from_numpy(idx).cuda(), torch.from_numpy(qs).cuda(),
+                                   softmax_scale=wl.scale)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy().astype(np.float64)
+
+    def rows_of(s, p):
+        if not (0 <= s < wl.n_seq and 0 <= p < wl.l_max):
+            return np.zeros((0, wl.d_qk))
+        return _f64(C[s, :p + 1])
+    _check_rows(o, q, rows_of, idx, qs, qp, wl, range(wl.nq) if rows is None else rows, what)
+    return o
+
+
+def test_mla_split_lists_all_head_counts(dsa):
+    """Lists split over several workgroups (few queries): 32..128 heads."""
+    for H in (128, 32, 64, 96):
+        wl = M.WORKLOADS["sparse_mla_decode_L128K_H128"].replace(
+            nq=8, n_seq=1, l_max=3000, n_heads=H, top_k=2048, layout="tail")
+        _case(dsa, wl, seed=H, what=f"mla H{H}")
+
+
+def test_mla_unsplit_lists_and_ragged_k(dsa):
+    """Enough queries that every list stays in one workgroup; k not a multiple
+    of the 32-row step."""
+    wl = M.WORKLOADS["sparse_mla_decode_L128K_H128"].replace(
+        nq=320, n_seq=1, l_max=2000, n_heads=64, top_k=1000, layout="tail")
+    _case(dsa, wl, seed=3, rows=list(range(0, 320, 29)) + [319])
+    wl = wl.replace(nq=16, top_k=77)
+    _case(dsa, wl, seed=4)
+
+
+def test_mla_padding_repeats_out_of_range_and_invalid_rows(dsa):
+    """-1 padding (prefixes shorter than k), entries beyond the prefix or the
+    cache, repeated entries, and queries with no keys at all."""
+    wl = M.WORKLOADS["sparse_mla_decode_L128K_H128"].replace(
+        nq=12, n_seq=2, l_max=100, n_heads=128, top_k=160, layout="tail")
+    qs = np.array([0, 1] * 6, dtype=np.int32)
+    qp = np.array([0, 5, 31, 32, 63, 99, 99, 50, -1, 100, 99, 7], dtype=np.int32)
+    idx = np.full((12, 160), -1, dtype=np.int32)
+    rng = np.random.default_rng(7)
+    for t in range(12):
+        n = max(int(qp[t]) + 1, 1)
+        idx[t, :min(n, 160)] = rng.permutation(n)[:160]
+    idx[6, 100:140] = rng.integers(0, 100, size=40)           # repeats
+    idx[7, 60:70] = [51, 60, 99, 100, 5000, -7, 50, 0, 50, 2]  # beyond the prefix / cache
+    qs_bad = qs.copy()
+    qs_bad[10] = 5                                             # no such cache
+    _case(dsa, wl, seed=5, idx=idx, qs=qs_bad, qp=qp, what="mla edge")
+
+
+def test_mla_after_the_indexer(dsa):
+    """The dense indexer's top-k (with its padding) fed straight to the
+    attention over a latent cache of the same length."""
+    iwl = datagen.small(2, nq=8, n_seq=8, l_max=4096)
+    inp = datagen.make(iwl, 0)
+    from _helpers import upload
+    dev = upload(inp, iwl)
+    sel, _ = dsa.indexer_score_topk(dev["q"], dev["w"], dev["k"], dev["q_pos"], dev["q_seq"],
+                                    top_k=2048)
+    idx = sel.cpu().numpy()
+    wl = M.WORKLOADS["sparse_mla_decode_L128K_H128"].replace(nq=8, n_seq=8, l_max=4096)
+    _case(dsa, wl, seed=6, idx=idx, what="mla after indexer")
+
+
+def test_mla_full_size_sampled_queries(dsa):
+    """64 queries x 128 heads over their own 131072-row caches, k = 2048, as
+    timed: the rows the lists name are generated and placed in a zeroed cache
+    (no other row is read), and 6 queries are checked against the oracle."""
+    wl = M.WORKLOADS["sparse_mla_decode_L128K_H128"]
+    q = M.queries(wl, 0)
+    idx = M.index_lists(wl, 0)
+    qs, qp = M.positions(wl)
+    say(f"[mla full] nq={wl.nq} L={wl.l_max} H={wl.n_heads} k={wl.top_k}")
+    kv = torch.zeros((wl.n_seq, wl.l_max, wl.d_qk), dtype=torch.bfloat16, device="cuda")
+    sample = [0, 1, 17, 40, 62, 63]
+    gathered = {}
+    for t in range(wl.nq):
+        r = M.rows(wl, int(qs[t]), idx[t], 0)
+        if t in sample:
+            gathered[t] = r
+        kv[int(qs[t])][torch.from_numpy(idx[t].astype(np.int64)).cuda()] = _bf16(r)
+    out = dsa.sparse_mla_attention(_bf16(q), kv, torch.from_numpy(qp).cuda(),
+                                   torch.from_numpy(idx).cuda(), torch.from_numpy(qs).cuda(),
+                                   softmax_scale=wl.scale)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy().astype(np.float64)
+    del kv
+    errs = []
+    for t in sample:
+        ref, mag = A.sparse_mla_row(_f64(q[t]), _f64(gathered[t]), np.arange(wl.top_k), wl.d_v,
+                                    wl.scale)
+        bad = np.abs(o[t] - ref) > 2.0 ** -7 * mag + 2.0 ** -8 * np.abs(ref)
+        if bad.any():
+            errs.append(f"q{t}: {int(bad.sum())} values off")
+    assert not errs, "\n".join(errs)
