@@ -11,8 +11,11 @@ dense_prefill (32768 causal rows of one 32768-key cache), misa_prefill (the same
 rows routed to h = 8 of 64 heads over 64-key pooled blocks), misa / misa_dagger
 (h = 8 of 64 heads, B = 64, k' = 8192), hisa (32 heads, L = 1M, B = 128,
 m = 64), misa_hisa (the same with the router's h = 8 heads), pool (mean
-pooling of the 128K caches).  tiny, hisa and misa_hisa touch less than the
-256 MB last-level cache and are timed cold.
+pooling of the 128K caches), sparse_mla (the attention that consumes the
+index lists: 64 queries x 128 heads over 2048 listed rows of their own
+131072-row latent caches, absorbed-MLA rows of 576 bf16 values).  tiny, hisa,
+misa_hisa and sparse_mla touch less than the 256 MB last-level cache and are
+timed cold.
 
 The steps are timed twice: first the calls alone (ms_per_step, value), then
 the same number of calls with the library's per-launch HIP events on the
@@ -36,7 +39,8 @@ CSRC = os.path.join(ROOT, "sparse_attention_token_indexer_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 WORKLOADS = {"dense_decode": 2, "tiny": 1, "dense_prefill": 3, "misa": 4, "misa_dagger": 4,
-             "hisa": 5, "pool": 4, "misa_prefill": 3, "hisa_prefill": 3, "misa_hisa": 5}
+             "hisa": 5, "pool": 4, "misa_prefill": 3, "hisa_prefill": 3, "misa_hisa": 5,
+             "sparse_mla": None}
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
 
 
@@ -46,7 +50,8 @@ KERNEL_SOURCE = {"dense_decode": "k_score_select.hip", "tiny": "k_score_select.h
                  "misa": "k_score_select.hip", "misa_dagger": "k_score_select.hip",
                  "hisa": "k_hisa.hip", "dense_prefill": "k_prefill.hip",
                  "misa_prefill": "k_prefill_routed.hip", "pool": "k_pool.hip",
-                 "hisa_prefill": "k_hisa.hip", "misa_hisa": "k_hisa.hip"}
+                 "hisa_prefill": "k_hisa.hip", "misa_hisa": "k_hisa.hip",
+                 "sparse_mla": "k_mla.hip"}
 
 
 def _local_sources(name: str) -> list:
@@ -171,6 +176,34 @@ def cpu_baseline(wl, seed, seconds: float, mode: str):
                       f"{spent:.1f} s of compute on {os.cpu_count()} visible host cores"}
 
 
+def cpu_baseline_mla(wl, seed, seconds: float):
+    """The attention oracle, as it stands, on whole queries of the same
+    workload until about `seconds` of compute have run (row generation is
+    not timed)."""
+    import numpy as np
+
+    import datagen
+    from datagen import mla as M
+    from oracle import attention as A
+    q = M.queries(wl, seed)
+    idx = M.index_lists(wl, seed)
+    qs, _ = M.positions(wl)
+    spent, done = 0.0, 0
+    for t in range(wl.nq):
+        rows = datagen.bf16_bits_to_f32(M.rows(wl, int(qs[t]), idx[t], seed)).astype(np.float64)
+        q_t = datagen.bf16_bits_to_f32(q[t]).astype(np.float64)
+        t0 = time.perf_counter()
+        A.sparse_mla_row(q_t, rows, np.arange(wl.top_k), wl.d_v, wl.scale)
+        spent += time.perf_counter() - t0
+        done += 1
+        if spent >= seconds:
+            break
+    return {"value": done * wl.top_k / spent, "unit": "attended (query, row) pairs/s",
+            "cores": blas_threads(), "kind": "oracle",
+            "sample": f"{done} of {wl.nq} queries (all {wl.n_heads} heads, {wl.top_k} rows each), "
+                      f"float64 NumPy, {spent:.1f} s of compute on {os.cpu_count()} visible host cores"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -210,19 +243,55 @@ def main() -> int:
 
     dsa.lib()
     name = args.workload
-    wl = datagen.WORKLOADS[WORKLOADS[name]]
-    inp = gen_inputs(wl, args.seed, dev)
-    q, w, k, q_pos, q_seq = inp["q"], inp["w"], inp["k"], inp["q_pos"], inp["q_seq"]
-    nq, H, d, L, topk = wl.nq, wl.n_heads, wl.head_dim, wl.l_max, wl.top_k
-    eb = 2 if wl.dtype == datagen.BF16 else 4
-    pos_np = inp["np"]["q_pos"]
-    pairs = int((pos_np.astype(np.int64) + 1).sum())
-    out_i = torch.empty((nq, topk), dtype=torch.int32, device=dev)
-    out_s = torch.empty((nq, topk), dtype=torch.float32, device=dev)
-    io_bytes = nq * H * d * eb + nq * H * 4 + nq * topk * 8       # q, w, outputs
     extra = {}
+    if name == "sparse_mla":
+        from datagen import mla as M
+        wl = M.WORKLOADS["sparse_mla_decode_L128K_H128"]
+        nq, H, d, L, topk, eb = wl.nq, wl.n_heads, wl.d_qk, wl.l_max, wl.top_k, 2
+        pairs = nq * topk                        # attended (query, listed row) pairs
 
-    if name == "dense_prefill":
+        def bf16(x):
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(torch.bfloat16)
+        mq = bf16(M.queries(wl, args.seed))
+        idx_np = M.index_lists(wl, args.seed)
+        qs_np, qp_np = M.positions(wl)
+        # only the listed rows are ever read: they are generated and placed in
+        # a zeroed cache of the full size
+        kv = torch.zeros((wl.n_seq, L, d), dtype=torch.bfloat16, device=dev)
+        for t in range(nq):
+            kv[int(qs_np[t])][torch.from_numpy(idx_np[t].astype(np.int64)).to(dev)] = bf16(
+                M.rows(wl, int(qs_np[t]), idx_np[t], args.seed))
+        m_idx, m_qs, m_qp = (torch.from_numpy(x).to(dev) for x in (idx_np, qs_np, qp_np))
+        m_out = torch.empty((nq, H, wl.d_v), dtype=torch.bfloat16, device=dev)
+        nbytes = dsa.sparse_mla_workspace_size(nq, H, d, wl.d_v, topk)
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+
+        def step():
+            dsa.sparse_mla_attention(mq, kv, m_qp, m_idx, m_qs, softmax_scale=wl.scale,
+                                     out=m_out, workspace=ws)
+        kind = "mla"
+        gathered = nq * topk * d * 2
+        kernel_bytes = gathered + nq * H * d * 2 + nq * topk * 4 + nq * H * wl.d_v * 2
+        call_bytes = kernel_bytes
+        call_flops = 2 * nq * H * topk * (d + wl.d_v)
+        bound_note = ("HBM: every listed latent row (1152 B) read once, plus the queries, the "
+                      "lists and the outputs (the per-slice partial outputs are extra traffic)")
+        extra["attention"] = {"d_qk": d, "d_v": wl.d_v, "softmax_scale": wl.scale}
+    else:
+        wl = datagen.WORKLOADS[WORKLOADS[name]]
+        inp = gen_inputs(wl, args.seed, dev)
+        q, w, k, q_pos, q_seq = inp["q"], inp["w"], inp["k"], inp["q_pos"], inp["q_seq"]
+        nq, H, d, L, topk = wl.nq, wl.n_heads, wl.head_dim, wl.l_max, wl.top_k
+        eb = 2 if wl.dtype == datagen.BF16 else 4
+        pos_np = inp["np"]["q_pos"]
+        pairs = int((pos_np.astype(np.int64) + 1).sum())
+        out_i = torch.empty((nq, topk), dtype=torch.int32, device=dev)
+        out_s = torch.empty((nq, topk), dtype=torch.float32, device=dev)
+        io_bytes = nq * H * d * eb + nq * H * 4 + nq * topk * 8       # q, w, outputs
+
+    if name == "sparse_mla":
+        pass
+    elif name == "dense_prefill":
         nbytes = dsa.indexer_score_topk_workspace_size(nq, H, d, wl.n_seq, L, topk, 0)
         ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
 
@@ -367,7 +436,7 @@ def main() -> int:
     # (--flush write: they end up holding dirty lines, whose write-back then
     # competes with the step's own reads).
     flush = None
-    if name in ("hisa", "misa_hisa", "tiny"):
+    if name in ("hisa", "misa_hisa", "tiny", "sparse_mla"):
         flush_buf = torch.zeros(128 << 20, dtype=torch.float32, device=dev)
         if args.flush == "write":
             flush = lambda: flush_buf.zero_()
@@ -448,13 +517,19 @@ def main() -> int:
 
     if name == "pool":
         metric, unit, value = "mean-pooled key-cache bytes/s", "GB/s", kernel_bytes / (ms_per_step * 1e-3) / 1e9
+    elif name == "sparse_mla":
+        metric = "sparse attention over the index lists: attended (query, row) pairs/s (1 MI355X)"
+        unit = "pairs/s"
+        value = pairs / (ms_per_step * 1e-3)
     else:
         metric = "indexer q·k pair-scores/sec + top-k latency at L=128K, H_I=64 (1 MI355X)"
         unit = "pair-scores/s"
         value = pairs / (ms_per_step * 1e-3)
 
     cpu = None
-    if not args.no_cpu_baseline and name != "pool":
+    if not args.no_cpu_baseline and name == "sparse_mla":
+        cpu = cpu_baseline_mla(wl, args.seed, args.cpu_seconds)
+    elif not args.no_cpu_baseline and name != "pool":
         cpu = cpu_baseline(wl, args.seed, args.cpu_seconds, name)
 
     line = {
@@ -476,12 +551,14 @@ def main() -> int:
                                 "hisa_prefill": "hisa_prefill_L32K_H64_B128_m64",
                                 "misa_hisa": "misa_hisa_decode_L1M_H32_h8"}.get(name, wl.name),
                    "queries": nq, "l_max": L, "n_heads": H, "head_dim": d,
-                   "top_k": topk, "causal_pairs": pairs, "parallelism": "single GPU",
-                   **({"block": wl.block} if wl.block else {}),
+                   "top_k": topk, ("attended_pairs" if name == "sparse_mla" else "causal_pairs"): pairs,
+                   "parallelism": "single GPU",
+                   **({"block": wl.block} if getattr(wl, "block", 0) else {}),
                    **({"h": 8 if name == "misa_hisa" else wl.n_active_heads}
                       if name.startswith("misa") else {}),
                    **({"k_prime": wl.k_prime} if name == "misa_dagger" else {}),
-                   **({"m_blocks": wl.m_blocks} if name in ("hisa", "misa_hisa") else {})},
+                   **({"m_blocks": wl.m_blocks} if name in ("hisa", "misa_hisa") else {}),
+                   **({"d_v": wl.d_v} if name == "sparse_mla" else {})},
         "topk_latency_us": ms_per_step * 1e3,
         "ms_per_step_with_kernel_events": ms_per_step_events,
         "call": {"latency_median_us": call_med_ms * 1e3, "latency_min_us": per_call[0] * 1e3,

@@ -1041,7 +1041,7 @@ MlaPlan plan_mla(int64_t nq, int n_heads, int top_k) {
   p.splits = (int)cdiv(tiles, p.tiles_per_split);
   if (p.splits > 1) {
     Arena A;
-    p.part_o = A.take((size_t)nq * p.splits * n_heads * dsa::kMlaDv * 4);
+    p.part_o = A.take((size_t)nq * p.splits * n_heads * dsa::kMlaDv * 2);
     p.part_ml = A.take((size_t)nq * p.splits * n_heads * 8);
     p.total = A.off;
   }
@@ -1101,7 +1101,7 @@ int sparse_mla_attention(const void* q, const void* kv, int32_t dtype, const int
   a.l_max = l_max;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.out = reinterpret_cast<uint16_t*>(out);
-  a.part_o = p.splits > 1 ? at<float>(workspace, p.part_o) : nullptr;
+  a.part_o = p.splits > 1 ? at<uint16_t>(workspace, p.part_o) : nullptr;
   a.part_ml = p.splits > 1 ? at<float2>(workspace, p.part_ml) : nullptr;
   return hip_status(timed(DSA_KERNEL_MLA, stream, [&] { return dsa::launch_sparse_mla(a, stream); }),
                     "sparse attention kernel", stream);

@@ -25,7 +25,8 @@ struct MlaArgs {
   int64_t l_max;
   float scale_log2;        // softmax scale * log2(e)
   uint16_t* out;           // [nq, n_heads, kMlaDv] bf16
-  float* part_o;           // [nq, splits, n_heads, kMlaDv] unnormalised slices (splits > 1)
+  uint16_t* part_o;        // [nq, splits, n_heads, kMlaDv] bf16 slices, each divided by its
+                           // own sum (splits > 1)
   float2* part_ml;         // [nq, splits, n_heads] (running max in log2 units, sum)
 };
 
@@ -33,7 +34,8 @@ struct MlaArgs {
 // transposed (padded), the last kMlaQLds k-steps of every wave's query rows
 // (padded), and the slice's row ids.
 constexpr int kMlaCRow = kMlaDqk * 2 + 16;        // bytes per staged row
-constexpr int kMlaVRow = kMlaTile * 2 + 16;       // bytes per transposed value row
+constexpr int kMlaVRow = kMlaTile * 2 + 8;        // bytes per transposed value row (18 banks:
+                                                  // 16 consecutive rows hit distinct bank pairs)
 constexpr int kMlaQRow = kMlaQLds * 64 + 16;      // bytes per query row kept in LDS
 inline size_t mla_lds_bytes(int n_heads, int tiles_per_split) {
   return (size_t)kMlaTile * kMlaCRow + (size_t)kMlaDv * kMlaVRow + (size_t)n_heads * kMlaQRow +

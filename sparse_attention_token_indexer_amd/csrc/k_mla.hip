@@ -23,7 +23,8 @@
 // sit in the lane (the k order of the product is the lane's own row order),
 // and O^T (512 x 16 per wave) stays in accumulation registers.  A query whose
 // list is split writes its unnormalised slices with their (max, sum); a
-// second kernel merges them.
+// second kernel merges them.  Slices are stored in bf16 (relative 2^-9, like
+// the output itself).
 #include "dsa_common.h"
 #include "dsa_mla.h"
 
@@ -180,27 +181,24 @@ __global__ __launch_bounds__(64 * NW) void k_sparse_mla(MlaArgs a) {
   // the head's sum over the four lane groups
   float l = l_run + shfl_xor_f(l_run, 16);
   l += shfl_xor_f(l, 32);
-  if (a.splits == 1) {
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    uint16_t* o = a.out + ((size_t)t * a.n_heads + head) * kMlaDv + 4 * g;
+  // the output, or this slice's output (divided by its own sum) for the merge
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const size_t slot = ((size_t)t * a.splits + sp) * a.n_heads + head;
+  uint16_t* o = (a.splits == 1 ? a.out + ((size_t)t * a.n_heads + head) * kMlaDv
+                               : a.part_o + slot * kMlaDv) + 4 * g;
 #pragma unroll
-    for (int d = 0; d < kDt; ++d) {
-      bf16x4 v;
+  for (int d = 0; d < kDt; ++d) {
+    bf16x4 v;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = (__bf16)(acc[d][r] * inv);
-      *reinterpret_cast<bf16x4*>(o + 16 * d) = v;
-    }
-  } else {
-    const size_t slot = ((size_t)t * a.splits + sp) * a.n_heads + head;
-    float* po = a.part_o + slot * kMlaDv + 4 * g;
-#pragma unroll
-    for (int d = 0; d < kDt; ++d) *reinterpret_cast<f32x4*>(po + 16 * d) = acc[d];
-    if (g == 0) a.part_ml[slot] = make_float2(m_run, l);
+    for (int r = 0; r < 4; ++r) v[r] = (__bf16)(acc[d][r] * inv);
+    *reinterpret_cast<bf16x4*>(o + 16 * d) = v;
   }
+  if (a.splits > 1 && g == 0) a.part_ml[slot] = make_float2(m_run, l);
 }
 
-// Merge of a query's slices: weights 2^(m_s - M) with M the largest max,
-// o = sum_s w_s o_s / sum_s w_s l_s (zeros when no slice saw a valid row).
+// Merge of a query's slices: with M the largest running max and
+// w_s = 2^(m_s - M) l_s, o = sum_s w_s o_s / sum_s w_s, o_s the slice's
+// normalised output (zeros when no slice saw a valid row).
 // One thread = one head x 4 value columns.
 __global__ __launch_bounds__(256) void k_mla_combine(MlaArgs a) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -219,9 +217,11 @@ __global__ __launch_bounds__(256) void k_mla_combine(MlaArgs a) {
       const size_t slot = ((size_t)t * a.splits + s) * a.n_heads + head;
       const float2 ml = a.part_ml[slot];
       if (ml.x == -__builtin_inff()) continue;
-      const float w = exp2f(ml.x - M);
-      L += w * ml.y;
-      o += w * *reinterpret_cast<const f32x4*>(a.part_o + slot * kMlaDv + 4 * c4);
+      const float w = exp2f(ml.x - M) * ml.y;
+      const bf16x4 os = *reinterpret_cast<const bf16x4*>(a.part_o + slot * kMlaDv + 4 * c4);
+      L += w;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[r] += w * (float)os[r];
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;

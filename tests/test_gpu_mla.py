@@ -6,8 +6,10 @@ with o and the weights p from the float64 oracle.  The kernel's own error:
 bf16 rounding of each probability before the value product (relative 2^-9
 per term, so at most 2^-9 * sum_i p_i |v_i| over the row, and the same again
 for the sum in the denominator, which is kept unrounded), float32 scores and
-accumulation (relative ~2^-20), and the bf16 rounding of the output (2^-9
-|o|).  The bound above leaves a factor of two over that.
+accumulation (relative ~2^-20), the bf16 rounding of each slice's output when
+a list is split over workgroups (at most 2^-9 * sum_i p_i |v_i| after the
+merge) and of the output (2^-9 |o|): 2^-8 * sum_i p_i |v_i| + 2^-9 |o| in
+all.  The bound above leaves a factor of two over that.
 """
 import numpy as np
 import pytest
