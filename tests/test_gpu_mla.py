@@ -159,3 +159,33 @@ def test_mla_full_size_sampled_queries(dsa):
         if bad.any():
             errs.append(f"q{t}: {int(bad.sum())} values off")
     assert not errs, "\n".join(errs)
+
+
+def test_mla_argument_errors(dsa):
+    """Calls the library rejects before any launch."""
+    wl = M.WORKLOADS["sparse_mla_decode_L128K_H128"].replace(nq=2, n_seq=2, l_max=64, n_heads=32,
+                                                             top_k=16)
+    q = _bf16(M.queries(wl, 0))
+    kv = _bf16(M.cache(wl, 0))
+    qs, qp = (torch.from_numpy(x).cuda() for x in M.positions(wl))
+    idx = torch.from_numpy(M.index_lists(wl, 0)).cuda()
+    for bad in (0.0, float("nan"), -1.0, float("inf")):
+        with pytest.raises(dsa.DsaError):
+            dsa.sparse_mla_attention(q, kv, qp, idx, qs, softmax_scale=bad)
+    q48 = torch.zeros((2, 48, 576), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(dsa.DsaError):                       # 48 heads: not a multiple of 32
+        dsa.sparse_mla_attention(q48, kv, qp, idx, qs, softmax_scale=0.1)
+    q512 = torch.zeros((2, 32, 512), dtype=torch.bfloat16, device="cuda")
+    kv512 = torch.zeros((2, 64, 512), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(dsa.DsaError):                       # rows of 512: not the 576 layout
+        dsa.sparse_mla_attention(q512, kv512, qp, idx, qs, softmax_scale=0.1)
+    big = torch.zeros((2, 32769), dtype=torch.int32, device="cuda")
+    with pytest.raises(dsa.DsaError):                       # list longer than supported
+        dsa.sparse_mla_attention(q, kv, qp, big, qs, softmax_scale=0.1)
+    idx256 = torch.full((2, 256), -1, dtype=torch.int32, device="cuda")
+    idx256[:, :16] = idx
+    need = dsa.sparse_mla_workspace_size(2, 32, 576, 512, 256)
+    assert need > 0                                         # two queries: lists are split
+    ws = torch.empty(need - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises((dsa.DsaError, ValueError)):
+        dsa.sparse_mla_attention(q, kv, qp, idx256, qs, softmax_scale=0.1, workspace=ws)

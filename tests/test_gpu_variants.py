@@ -294,6 +294,17 @@ def test_misa_hisa_partial_blocks_internal_pooling_and_prefill_rows(dsa):
     _misa_hisa_case(dsa, wl, h=3, m=6, k=200, rows=list(range(0, 1024, 41)) + [63, 64, 1023])
 
 
+def test_misa_hisa_argument_errors(dsa):
+    """Calls the library rejects before any launch."""
+    wl = datagen.small(5, nq=2, n_seq=2, l_max=4096)
+    dev = upload(datagen.make(wl, 0), wl)
+    args = (dev["q"], dev["w"], dev["k"], dev["q_pos"], dev["q_seq"])
+    for h, m in ((0, 8), (wl.n_heads + 1, 8), (4, 0), (4, 1025), (4, 100)):
+        # h out of range, no blocks, more blocks than supported, m * B > 8192
+        with pytest.raises(dsa.DsaError):
+            dsa.misa_hisa_topk(*args, block=128, n_active_heads=h, m_blocks=m, top_k=64)
+
+
 def test_hisa_exact_ties_take_lowest_ids(dsa):
     """Zero queries make every block and token score exactly 0.0, so both
     selections are decided by the tie-break alone (lower index first): the
