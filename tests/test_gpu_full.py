@@ -9,7 +9,7 @@ import torch
 
 import datagen
 from oracle import indexer as O
-from oracle.check import check_selection
+from oracle.check import FLOOR, RTOL, check_selection
 
 from _helpers import say, to_device
 
@@ -129,6 +129,55 @@ def test_hisa_full_with_iou(dsa):
         errs += _check(hi[t], hv[t], rr, wl.top_k, q_t, w_t, K, f"hisa q{t}")
         d = O.dense_row(q_t, w_t, K, p, wl.top_k)
         errs += _check(dni[t], None, d, wl.top_k, q_t, w_t, K, f"dense q{t}")
+    assert not errs, "\n".join(errs[:10])
+
+
+def test_hisa_and_misa_hisa_full_sampled_rows(dsa):
+    """32 queries x 1048576 keys, 32 heads, B 128, m 64, k 2048, as timed: the
+    pooling, HISA over all heads and MISA∘HISA with h = 8 (the three calls of
+    the hisa and misa_hisa workloads).  Rows 0, 13 and 31 against the oracle,
+    each stage conditional on the GPU's own upstream choice."""
+    wl = datagen.WORKLOADS[5]
+    h_act = 8
+    say("[full] HISA and MISA∘HISA 32 x 1048576")
+    dev, h = _device_inputs(wl)
+    args = (dev["q"], dev["w"], dev["k"], dev["q_pos"], dev["q_seq"])
+    kp = dsa.indexer_mean_pool_keys(dev["k"], wl.block)
+    r = dsa.hisa_block_filter_topk(*args, block=wl.block, m_blocks=wl.m_blocks, top_k=wl.top_k,
+                                   k_pooled=kp)
+    mh = dsa.misa_hisa_topk(*args, block=wl.block, n_active_heads=h_act, m_blocks=wl.m_blocks,
+                            top_k=wl.top_k, k_pooled=kp, with_importance=True)
+    torch.cuda.synchronize()
+    hi, hv, blocks, bsc = (r[x].cpu().numpy() for x in ("idx", "score", "blocks", "block_score"))
+    out = {x: v.cpu().numpy() for x, v in mh.items()}
+    errs = []
+    for t in (0, 13, 31):
+        say(f"[full] oracle row {t}")
+        q_t, w_t, K, p = _host_row(wl, h, t)
+        pooled = O.misa_pooled_for_query(K, wl.block, p)
+        # HISA: blocks, then tokens inside the GPU's blocks
+        bs, bA = O.hisa_block_scores(q_t, w_t, pooled)
+        errs += check_selection(blocks[t], bsc[t], np.arange(pooled.shape[0]), bs, bA, wl.m_blocks,
+                                O.dot_magnitude(q_t, w_t, pooled), what=f"hisa blocks q{t}")
+        rr = O.hisa_row(q_t, w_t, K, p, wl.block, wl.m_blocks, wl.top_k, blocks=blocks[t])
+        errs += _check(hi[t], hv[t], rr, wl.top_k, q_t, w_t, K, f"hisa q{t}")
+        # MISA∘HISA: importance and heads, blocks with the GPU's heads, tokens
+        I = O.misa_importance(q_t, w_t, pooled)
+        Fi = np.abs(w_t) * (np.abs(q_t) @ np.abs(pooled).T).sum(axis=1)
+        gi = out["importance"][t].astype(np.float64)
+        if (np.abs(gi - I) > RTOL * I + FLOOR * Fi).any():
+            errs.append(f"misa-hisa importance q{t}")
+        errs += check_selection(out["heads"][t], None, np.arange(wl.n_heads), I, I, h_act, Fi,
+                                what=f"misa-hisa heads q{t}")
+        hs = out["heads"][t].astype(np.int64)
+        bs2, bA2 = O.hisa_block_scores(q_t[hs], w_t[hs], pooled)
+        errs += check_selection(out["blocks"][t], out["block_score"][t], np.arange(pooled.shape[0]),
+                                bs2, bA2, wl.m_blocks, O.dot_magnitude(q_t[hs], w_t[hs], pooled),
+                                what=f"misa-hisa blocks q{t}")
+        r2 = O.misa_hisa_row(q_t, w_t, K, p, wl.block, h_act, wl.m_blocks, wl.top_k, heads=hs,
+                             blocks=out["blocks"][t])
+        errs += _check(out["idx"][t], out["score"][t], r2, wl.top_k, q_t, w_t, K,
+                       f"misa-hisa q{t}", hs)
     assert not errs, "\n".join(errs[:10])
 
 
