@@ -81,3 +81,68 @@ def test_argument_errors_return_before_any_launch(lib):
     assert lib.hisa_block_filter_topk(aligned, aligned, aligned, None, 1, None, aligned, 1, 8, 128,
                                       1, 100, 16, 4, 4, aligned, None, None, None, None, 0,
                                       None) == 2                     # f32 HISA unsupported
+
+
+def _call_mla(lib, **kw):
+    args = dict(q=16, kv=16, dtype=0, q_seq=None, q_pos=4, idx=4, nq=2, H=32, d_qk=576, d_v=512,
+                n_seq=1, l_max=100, top_k=256, scale=0.1, out=16, ws=None, ws_bytes=0,
+                stream=None)
+    args.update(kw)
+    # fake pointers are never dereferenced: every case below fails validation first
+    return lib.sparse_mla_attention(*[args[x] for x in (
+        "q", "kv", "dtype", "q_seq", "q_pos", "idx", "nq", "H", "d_qk", "d_v", "n_seq", "l_max",
+        "top_k", "scale", "out", "ws", "ws_bytes", "stream")])
+
+
+def test_sparse_attention_rejects_bad_arguments(lib):
+    EINVAL, EUNSUP, EWS = 1, 2, 3
+    assert _call_mla(lib, dtype=1) == EUNSUP
+    assert _call_mla(lib, d_qk=512) == EUNSUP
+    assert _call_mla(lib, d_v=576) == EUNSUP
+    for H in (16, 48, 160):
+        assert _call_mla(lib, H=H) == EUNSUP
+    assert _call_mla(lib, top_k=0) == EUNSUP
+    assert _call_mla(lib, top_k=32769) == EUNSUP
+    for s in (0.0, -1.0, float("inf"), float("nan")):
+        assert _call_mla(lib, scale=s) == EINVAL
+    assert _call_mla(lib, nq=-1) == EINVAL
+    assert _call_mla(lib, q=None) == EINVAL
+    assert _call_mla(lib, q=8) == EINVAL               # not 16-byte aligned
+    assert _call_mla(lib, idx=2) == EINVAL             # not 4-byte aligned
+    assert _call_mla(lib) == EWS                       # two queries: the lists are split
+    assert _call_mla(lib, nq=0, q=None, kv=None, out=None) == 0
+
+
+def test_sparse_attention_workspace_sizes(lib):
+    # 64 queries x 128 heads x 2048 rows: 2 head groups do not change the
+    # slices; 4 slices of 16 steps, bf16 slice outputs and (max, sum) pairs
+    n = dsa.sparse_mla_workspace_size(64, 128, 576, 512, 2048)
+    assert n == 64 * 4 * 128 * 512 * 2 + 64 * 4 * 128 * 8
+    assert dsa.sparse_mla_workspace_size(256, 128, 576, 512, 2048) == 0   # one slice each
+    assert dsa.sparse_mla_workspace_size(2, 32, 576, 512, 16) == 0        # one step
+    assert dsa.sparse_mla_workspace_size(2, 32, 576, 512, 32769) == 0     # unsupported
+
+
+def _call_misa_hisa(lib, **kw):
+    args = dict(q=16, w=4, k=16, kp=None, dtype=0, q_seq=None, q_pos=4, nq=1, H=32, d=128,
+                n_seq=1, l_max=4096, B=128, h=8, m=16, top_k=64, out_idx=4, out_score=None,
+                heads=None, imp=None, blocks=None, bscore=None, ws=None, ws_bytes=0, stream=None)
+    args.update(kw)
+    return lib.misa_hisa_topk(*[args[x] for x in (
+        "q", "w", "k", "kp", "dtype", "q_seq", "q_pos", "nq", "H", "d", "n_seq", "l_max", "B",
+        "h", "m", "top_k", "out_idx", "out_score", "heads", "imp", "blocks", "bscore", "ws",
+        "ws_bytes", "stream")])
+
+
+def test_misa_hisa_rejects_bad_arguments(lib):
+    EINVAL, EUNSUP, EWS = 1, 2, 3
+    assert _call_misa_hisa(lib, h=0) == EINVAL
+    assert _call_misa_hisa(lib, h=33) == EINVAL
+    assert _call_misa_hisa(lib, m=0) == EINVAL
+    assert _call_misa_hisa(lib, B=0) == EINVAL
+    assert _call_misa_hisa(lib, dtype=1) == EUNSUP
+    assert _call_misa_hisa(lib, m=65, B=128) == EUNSUP       # m * B above 8192
+    assert _call_misa_hisa(lib, m=1025, B=4) == EUNSUP       # more blocks than supported
+    assert _call_misa_hisa(lib) == EWS
+    assert dsa.misa_hisa_topk_workspace_size(32, 32, 128, 32, 1 << 20, 128, 8, 64, 2048, 1) > \
+        dsa.hisa_block_filter_topk_workspace_size(32, 32, 128, 32, 1 << 20, 128, 64, 2048, 1)
