@@ -199,18 +199,18 @@ __global__ __launch_bounds__(64 * NW) void k_sparse_mla(MlaArgs a) {
 // Merge of a query's slices: with M the largest running max and
 // w_s = 2^(m_s - M) l_s, o = sum_s w_s o_s / sum_s w_s, o_s the slice's
 // normalised output (zeros when no slice saw a valid row).
-// One thread = one head x 4 value columns.
+// One thread = one head x 8 value columns (16-byte loads and stores).
 __global__ __launch_bounds__(256) void k_mla_combine(MlaArgs a) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t per_q = (int64_t)a.n_heads * (kMlaDv / 4);
+  const int64_t per_q = (int64_t)a.n_heads * (kMlaDv / 8);
   if (i >= (int64_t)a.nq * per_q) return;
   const int t = (int)(i / per_q);
   const int rem = (int)(i - (int64_t)t * per_q);
-  const int head = rem / (kMlaDv / 4), c4 = rem - head * (kMlaDv / 4);
+  const int head = rem / (kMlaDv / 8), c8 = rem - head * (kMlaDv / 8);
   float M = -__builtin_inff();
   for (int s = 0; s < a.splits; ++s)
     M = fmaxf(M, a.part_ml[((size_t)t * a.splits + s) * a.n_heads + head].x);
-  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
   if (M != -__builtin_inff()) {
     for (int s = 0; s < a.splits; ++s) {
@@ -218,17 +218,17 @@ __global__ __launch_bounds__(256) void k_mla_combine(MlaArgs a) {
       const float2 ml = a.part_ml[slot];
       if (ml.x == -__builtin_inff()) continue;
       const float w = exp2f(ml.x - M) * ml.y;
-      const bf16x4 os = *reinterpret_cast<const bf16x4*>(a.part_o + slot * kMlaDv + 4 * c4);
+      const bf16x8 os = *reinterpret_cast<const bf16x8*>(a.part_o + slot * kMlaDv + 8 * c8);
       L += w;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o[r] += w * (float)os[r];
+      for (int r = 0; r < 8; ++r) o[r] += w * (float)os[r];
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  bf16x4 v;
+  bf16x8 v;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) v[r] = (__bf16)(o[r] * inv);
-  *reinterpret_cast<bf16x4*>(a.out + ((size_t)t * a.n_heads + head) * kMlaDv + 4 * c4) = v;
+  for (int r = 0; r < 8; ++r) v[r] = (__bf16)(o[r] * inv);
+  *reinterpret_cast<bf16x8*>(a.out + ((size_t)t * a.n_heads + head) * kMlaDv + 8 * c8) = v;
 }
 
 template <int NW>
@@ -241,7 +241,7 @@ hipError_t launch_t(const MlaArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(k, dim3(a.nq * a.splits), dim3(64 * NW), lds, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.splits > 1) {
-    const int64_t n = (int64_t)a.nq * a.n_heads * (kMlaDv / 4);
+    const int64_t n = (int64_t)a.nq * a.n_heads * (kMlaDv / 8);
     hipLaunchKernelGGL(k_mla_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a);
     e = hipGetLastError();
   }
