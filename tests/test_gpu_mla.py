@@ -189,3 +189,19 @@ def test_mla_argument_errors(dsa):
     ws = torch.empty(need - 256, dtype=torch.uint8, device="cuda")
     with pytest.raises((dsa.DsaError, ValueError)):
         dsa.sparse_mla_attention(q, kv, qp, idx256, qs, softmax_scale=0.1, workspace=ws)
+
+
+def test_mla_without_sequence_ids(dsa):
+    """q_seq omitted: every query reads cache 0."""
+    wl = M.WORKLOADS["sparse_mla_decode_L128K_H128"].replace(
+        nq=5, n_seq=1, l_max=700, n_heads=64, top_k=300, layout="tail")
+    q = M.queries(wl, 9)
+    C = M.cache(wl, 9)
+    _, qp = M.positions(wl)
+    idx = M.index_lists(wl, 9)
+    out = dsa.sparse_mla_attention(_bf16(q), _bf16(C), torch.from_numpy(qp).cuda(),
+                                   torch.from_numpy(idx).cuda(), None, softmax_scale=wl.scale)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy().astype(np.float64)
+    _check_rows(o, q, lambda s, p: _f64(C[0, :p + 1]), idx, np.zeros(5, np.int32), qp, wl,
+                range(5), "mla no q_seq")
