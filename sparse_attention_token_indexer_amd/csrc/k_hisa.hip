@@ -714,20 +714,28 @@ __global__ __launch_bounds__(kTT) void k_hisa_topk(HisaArgs a) {
   const int m1 = a.m_blocks < M ? a.m_blocks : M;
   const int items2 = m1 * a.block;
   const int32_t* blocks = a.blocks + (size_t)t * a.m_blocks;
-  for (int i = tid; i < m1; i += kTT) sbid[i] = blocks[i];
-  __syncthreads();
   // (key, token id) of every item into LDS: item i = tid + j * kTT is token
   // list[i / block] * block + i % block; list index and offset advance by kTT
-  // per step without a division
+  // per step without a division.  The first batch of keys is read before the
+  // kept-block list, so the two reads overlap.
   const uint32_t* keys_t = a.keys2 + (size_t)t * (a.split ? a.groups2 : a.groups) * a.ch2;
   const int blk = a.block, step = kTT / blk, rem = kTT % blk;
   int li = tid / blk, r = tid % blk;
-  for (int base = 0; base < items2; base += kSU * kTT) {
-    uint32_t k[kSU];
+  uint32_t k[kSU];
 #pragma unroll
-    for (int u = 0; u < kSU; ++u) {
-      const int i = base + tid + u * kTT;
-      k[u] = i < items2 ? keys_t[i] : 0u;
+  for (int u = 0; u < kSU; ++u) {
+    const int i = tid + u * kTT;
+    k[u] = i < items2 ? keys_t[i] : 0u;
+  }
+  for (int i = tid; i < m1; i += kTT) sbid[i] = blocks[i];
+  __syncthreads();
+  for (int base = 0; base < items2; base += kSU * kTT) {
+    if (base > 0) {
+#pragma unroll
+      for (int u = 0; u < kSU; ++u) {
+        const int i = base + tid + u * kTT;
+        k[u] = i < items2 ? keys_t[i] : 0u;
+      }
     }
 #pragma unroll
     for (int u = 0; u < kSU; ++u) {
