@@ -294,6 +294,17 @@ def test_misa_hisa_partial_blocks_internal_pooling_and_prefill_rows(dsa):
     _misa_hisa_case(dsa, wl, h=3, m=6, k=200, rows=list(range(0, 1024, 41)) + [63, 64, 1023])
 
 
+def test_misa_hisa_wider_routes_and_head_dims(dsa):
+    """Routed head counts that select the wider scorers (h = 24 of 32: one
+    32-row tile; h = 40 of 64: two tiles) and d = 64."""
+    wl = datagen.small(5, nq=4, n_seq=4, l_max=32768, n_plant=48)
+    _misa_hisa_case(dsa, wl, h=24, m=16, k=300, seed=1)
+    wl = datagen.small(5, nq=4, n_seq=4, l_max=32768, n_plant=48, n_heads=64)
+    _misa_hisa_case(dsa, wl, h=40, m=16, k=300, seed=2)
+    wl = datagen.small(5, nq=4, n_seq=4, l_max=20000, n_plant=48, head_dim=64)
+    _misa_hisa_case(dsa, wl, h=5, m=32, k=500, seed=3)
+
+
 def test_misa_hisa_argument_errors(dsa):
     """Calls the library rejects before any launch."""
     wl = datagen.small(5, nq=2, n_seq=2, l_max=4096)
