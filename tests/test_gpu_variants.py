@@ -241,6 +241,16 @@ def test_hisa_prefill_rows(dsa):
     _hisa_case(dsa, wl, m=3, k=64, seed=1, rows=rows, pooled=False)
 
 
+def test_hisa_heads_dims_and_the_multi_launch_path(dsa):
+    """The fused kernel's other scorers (16 heads: one 16-row tile; 64 heads:
+    two 32-row tiles; d = 64), and m * B above 8192 (the multi-launch path)."""
+    for H, d in ((16, 128), (64, 128), (48, 64)):
+        wl = datagen.small(5, nq=4, n_seq=4, l_max=30000, n_plant=48, n_heads=H, head_dim=d)
+        _hisa_case(dsa, wl, m=24, k=400, seed=H + d)
+    wl = datagen.small(5, nq=3, n_seq=3, l_max=40000, n_plant=60, block=64)
+    _hisa_case(dsa, wl, m=200, k=1000, seed=7)
+
+
 def _misa_hisa_case(dsa, wl, h, m, k, seed=0, pos=None, pooled=True, rows=None):
     inp = datagen.make(wl, seed)
     if pos is not None:
