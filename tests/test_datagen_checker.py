@@ -98,3 +98,24 @@ def test_checker_tie_band_allows_swaps_only_inside_band():
     # all-equal scores: every swap is inside the band, but the count must hold
     z = np.zeros(10)
     assert check_selection(np.array([9, 8, 7]), None, np.arange(10), z, z + 1, 3) == []
+
+
+def test_mla_inputs_regenerate_and_lists_are_valid():
+    from datagen import mla as M
+    wl = M.WORKLOADS["sparse_mla_decode_L128K_H128"].replace(nq=6, n_seq=1, l_max=300,
+                                                             n_heads=32, top_k=128, layout="tail")
+    C = M.cache(wl, 3)
+    pos = np.array([5, 299, 0, 17])
+    assert np.array_equal(M.rows(wl, 0, pos, 3), C[0, pos])       # a row alone = in the cache
+    assert not np.array_equal(M.rows(wl, 0, pos, 4), C[0, pos])   # the seed matters
+    assert np.array_equal(M.queries(wl, 3), M.queries(wl, 3))
+    _, qp = M.positions(wl)
+    idx = M.index_lists(wl, 3)
+    for t in range(wl.nq):
+        n = int(qp[t]) + 1
+        valid = idx[t][idx[t] >= 0]
+        assert len(valid) == min(n, wl.top_k) and len(set(valid.tolist())) == len(valid)
+        assert valid.max() < n and (idx[t][len(valid):] == -1).all()
+    short = wl.replace(l_max=50, nq=3)                             # prefixes shorter than k
+    li = M.index_lists(short, 1)
+    assert (np.sort(li[0][li[0] >= 0]) == np.arange(48)).all() and (li[0][48:] == -1).all()
