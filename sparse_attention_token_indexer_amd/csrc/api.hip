@@ -489,7 +489,7 @@ struct MisaHisaPlan {
 };
 
 MisaHisaPlan plan_misa_hisa(int64_t nq, int n_heads, int head_dim, int n_seq, int64_t l_max,
-                            int block, int h_act, int m, bool pooled_given) {
+                            int block, int m, bool pooled_given) {
   MisaHisaPlan p;
   p.h = plan_hisa_fused(nq, head_dim, n_seq, l_max, block, m, pooled_given);
   int64_t bps = 64;
@@ -957,7 +957,7 @@ size_t misa_hisa_topk_workspace_size(int32_t nq, int32_t n_heads, int32_t head_d
   (void)top_k;
   if (nq <= 0 || l_max <= 0 || block <= 0 || m_blocks <= 0 || n_active_heads <= 0 || n_heads <= 0)
     return 0;
-  return plan_misa_hisa(nq, n_heads, head_dim, n_seq, l_max, block, n_active_heads, m_blocks,
+  return plan_misa_hisa(nq, n_heads, head_dim, n_seq, l_max, block, m_blocks,
                         pooled_given != 0).total;
 }
 
@@ -977,8 +977,8 @@ int misa_hisa_topk(const void* q, const float* w, const void* k, const void* k_p
   if (m_blocks < 1) return fail(DSA_EINVAL, "m_blocks must be >= 1 (got %d)", m_blocks);
   if (nq == 0) return DSA_OK;
   if (k_pooled && !aligned(k_pooled, 16)) return fail(DSA_EINVAL, "k_pooled must be 16-byte aligned");
-  MisaHisaPlan p = plan_misa_hisa(nq, n_heads, head_dim, n_seq, l_max, block, n_active_heads,
-                                  m_blocks, k_pooled != nullptr);
+  MisaHisaPlan p = plan_misa_hisa(nq, n_heads, head_dim, n_seq, l_max, block, m_blocks,
+                                  k_pooled != nullptr);
   if (!p.h.ok)
     return fail(DSA_EUNSUPPORTED, "MISA-HISA needs m_blocks <= %d, m_blocks * block <= %d and "
                 "nq <= 65535", dsa::kHisaMaxBlocks, dsa::kHisaRegKeys);

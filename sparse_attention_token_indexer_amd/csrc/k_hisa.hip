@@ -514,8 +514,6 @@ __global__ __launch_bounds__(kHT) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int tid = (int)threadIdx.x, lane = lane_id();
   const int seq = a.q_seq ? a.q_seq[t] : 0;
   const int64_t pos = a.q_pos[t];
-  int32_t* out_i = a.out_idx + (size_t)t * a.top_k;
-  float* out_s = a.out_score ? a.out_score + (size_t)t * a.top_k : nullptr;
   int32_t* blocks = a.blocks + (size_t)t * a.m_blocks;
   float* bscore = a.out_block_score ? a.out_block_score + (size_t)t * a.m_blocks : nullptr;
   if (!(seq >= 0 && seq < a.n_seq && pos >= 0 && pos < a.l_max)) {   // no keys: padding only
