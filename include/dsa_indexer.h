@@ -14,7 +14,9 @@
  * lower token index.  Two reduced variants are provided: MISA head routing (same
  * MISA summary, sections "method" and "hierarchical variant") and HISA block
  * filtering ("HISA: Efficient Hierarchical Indexing for Fine-Grained Sparse
- * Attention" review, sections 1 and 3).
+ * Attention" review, sections 1 and 3), and both composed (MISA∘HISA).  The
+ * sparse attention that consumes the selected indices is provided too
+ * (sparse_mla_attention).
  *
  * Conventions shared by every entry point
  *  - Every pointer is a DEVICE pointer (hipMalloc'ed or equivalent) on the
@@ -41,10 +43,11 @@
  *  - Workspace contents on entry are ignored (the library clears what it needs
  *    at the start of each call); two calls that run concurrently must not share
  *    a workspace.
- *  - Supported shapes: head_dim 64 or 128; 1 <= n_heads <= 64; bf16 inputs
- *    use MFMA, float32 inputs (dense call only) the vector ALUs; l_max (and
- *    any candidate list a pass scores) at most 67108864 = 8192 * 8192
- *    items per query (DSA_EUNSUPPORTED beyond).
+ *  - Supported shapes (indexer calls): head_dim 64 or 128; 1 <= n_heads <= 64;
+ *    bf16 inputs use MFMA, float32 inputs (dense call only) the vector ALUs;
+ *    l_max (and any candidate list a pass scores) at most 67108864 =
+ *    8192 * 8192 items per query (DSA_EUNSUPPORTED beyond).  The sparse
+ *    attention has its own shapes, alignment and outputs, stated with it.
  */
 #ifndef DSA_INDEXER_H
 #define DSA_INDEXER_H
