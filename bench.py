@@ -10,7 +10,9 @@ Other workloads (--workload): tiny (float32, 16 queries, L = 4096),
 dense_prefill (32768 causal rows of one 32768-key cache), misa_prefill (the same
 rows routed to h = 8 of 64 heads over 64-key pooled blocks), misa / misa_dagger
 (h = 8 of 64 heads, B = 64, k' = 8192), hisa (32 heads, L = 1M, B = 128,
-m = 64), misa_hisa (the same with the router's h = 8 heads), pool (mean
+m = 64; --l-max shortens the caches and, at 128K or less, also times the
+dense indexer on the same inputs), misa_hisa (the same with the router's
+h = 8 heads), pool (mean
 pooling of the 128K caches), sparse_mla (the attention that consumes the
 index lists: 64 queries x 128 heads over 2048 listed rows of their own
 131072-row latent caches, absorbed-MLA rows of 576 bf16 values).  tiny, hisa,
@@ -215,6 +217,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flush", default="read", choices=("read", "write"),
                     help="how cold-timed workloads evict the caches before each step")
+    ap.add_argument("--l-max", type=int, default=None,
+                    help="cache length of the hisa workload (default 1048576); at 131072 or "
+                         "less the run also times the dense indexer on the same inputs")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device copy (for HBM counter calibration)")
     args = ap.parse_args()
@@ -279,6 +284,12 @@ def main() -> int:
         extra["attention"] = {"d_qk": d, "d_v": wl.d_v, "softmax_scale": wl.scale}
     else:
         wl = datagen.WORKLOADS[WORKLOADS[name]]
+        if args.l_max is not None:
+            if name != "hisa" or args.l_max < wl.m_blocks * wl.block:
+                print("--l-max applies to the hisa workload, at least m * B = "
+                      f"{wl.m_blocks * wl.block}", file=sys.stderr)
+                return 2
+            wl = wl.replace(l_max=args.l_max, name=f"hisa_decode_L{args.l_max // 1024}K_H32")
         inp = gen_inputs(wl, args.seed, dev)
         q, w, k, q_pos, q_seq = inp["q"], inp["w"], inp["k"], inp["q_pos"], inp["q_seq"]
         nq, H, d, L, topk = wl.nq, wl.n_heads, wl.head_dim, wl.l_max, wl.top_k
@@ -500,6 +511,36 @@ def main() -> int:
         per_call.append(e0.elapsed_time(e1))
     per_call.sort()
     call_med_ms = per_call[len(per_call) // 2]
+    if name == "hisa" and L <= 131072:
+        # the dense indexer (all heads, every prefix key) on the same inputs,
+        # timed the same way, for the HISA/dense latency ratio
+        dws = torch.empty(dsa.indexer_score_topk_workspace_size(nq, H, d, wl.n_seq, L, topk, 0),
+                          dtype=torch.uint8, device=dev)
+        d_i = torch.empty_like(out_i)
+        d_s = torch.empty_like(out_s)
+
+        def dense_step():
+            dsa.indexer_score_topk(q, w, k, q_pos, q_seq, top_k=topk, out_idx=d_i, out_score=d_s,
+                                   workspace=dws)
+        for _ in range(args.warmup):
+            dense_step()
+        dense_calls = []
+        for _ in range(args.steps):
+            if flush is not None:
+                flush()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            dense_step()
+            e1.record()
+            torch.cuda.synchronize()
+            dense_calls.append(e0.elapsed_time(e1))
+        dense_calls.sort()
+        dense_med = dense_calls[len(dense_calls) // 2]
+        extra["dense_same_inputs"] = {"call_median_us": dense_med * 1e3,
+                                      "hisa_call_median_us": call_med_ms * 1e3,
+                                      "dense_over_hisa": dense_med / call_med_ms}
     k_avg_ms = kt["total_ms"] / max(kt["launches"], 1)
     per_kernel[kind] = round(k_avg_ms * 1e3, 2)
     traffic = stored_traffic(name)
