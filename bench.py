@@ -44,6 +44,9 @@ WORKLOADS = {"dense_decode": 2, "tiny": 1, "dense_prefill": 3, "misa": 4, "misa_
              "hisa": 5, "pool": 4, "misa_prefill": 3, "hisa_prefill": 3, "misa_hisa": 5,
              "sparse_mla": None}
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
+# the IoU against the dense indexer is measured up to this cache length (the
+# dense call over the HISA workload's 1M-key caches is covered by the tests)
+DENSE_IOU_MAX_L = 131072
 
 
 # source file of each workload's dominant kernel (its hash, with every shared
@@ -298,6 +301,7 @@ def main() -> int:
         pairs = int((pos_np.astype(np.int64) + 1).sum())
         out_i = torch.empty((nq, topk), dtype=torch.int32, device=dev)
         out_s = torch.empty((nq, topk), dtype=torch.float32, device=dev)
+        status = torch.zeros(nq, dtype=torch.int32, device=dev)       # HISA per-query status
         io_bytes = nq * H * d * eb + nq * H * 4 + nq * topk * 8       # q, w, outputs
 
     if name == "sparse_mla":
@@ -376,7 +380,7 @@ def main() -> int:
         def step():
             dsa.hisa_block_filter_topk(q, w, k, q_pos, q_seq, block=wl.block, m_blocks=wl.m_blocks,
                                        top_k=topk, k_pooled=kp, with_blocks=False, out_idx=out_i,
-                                       out_score=out_s, workspace=ws)
+                                       out_score=out_s, out_status=status, workspace=ws)
         kind = "hisa"
         M = -(-L // wl.block)
         call_bytes = wl.n_seq * M * d * 2 + nq * wl.m_blocks * wl.block * d * eb + io_bytes
@@ -394,7 +398,8 @@ def main() -> int:
         def step():
             dsa.misa_hisa_topk(q, w, k, q_pos, q_seq, block=wl.block, n_active_heads=h,
                                m_blocks=wl.m_blocks, top_k=topk, k_pooled=kp, with_heads=False,
-                               with_blocks=False, out_idx=out_i, out_score=out_s, workspace=ws)
+                               with_blocks=False, out_idx=out_i, out_score=out_s,
+                               out_status=status, workspace=ws)
         kind = "hisa"
         M = -(-L // wl.block)
         pooled_bytes = wl.n_seq * M * d * 2
@@ -416,7 +421,7 @@ def main() -> int:
         def step():
             dsa.hisa_block_filter_topk(q, w, k, q_pos, None, block=B, m_blocks=m, top_k=topk,
                                        k_pooled=kp, with_blocks=False, out_idx=out_i,
-                                       out_score=out_s, workspace=ws)
+                                       out_score=out_s, out_status=status, workspace=ws)
         kind = "hisa"
         kernel_bytes = None
         p1 = pos_np.astype(np.int64) + 1
@@ -541,6 +546,20 @@ def main() -> int:
         extra["dense_same_inputs"] = {"call_median_us": dense_med * 1e3,
                                       "hisa_call_median_us": call_med_ms * 1e3,
                                       "dense_over_hisa": dense_med / call_med_ms}
+    if name in ("hisa", "misa_hisa", "hisa_prefill"):
+        extra["timed_out_queries"] = int(status.sum())       # of the last call (0: complete)
+    if name in ("misa", "misa_dagger", "hisa", "misa_hisa") and L <= DENSE_IOU_MAX_L:
+        # selection agreement of the last call's output with the dense indexer
+        # on the same inputs (the IoU the MISA and HISA pages report)
+        sel = out_i.clone()
+        dws = torch.empty(dsa.indexer_score_topk_workspace_size(nq, H, d, wl.n_seq, L, topk, 0),
+                          dtype=torch.uint8, device=dev)
+        d_i, _ = dsa.indexer_score_topk(q, w, k, q_pos, q_seq, top_k=topk, with_scores=False,
+                                        workspace=dws)
+        iou = dsa.indexer_selection_iou(sel, d_i).cpu().numpy()
+        extra["iou_vs_dense"] = {"mean": float(iou.mean()), "min": float(iou.min()),
+                                 "queries": int(iou.size)}
+        del dws
     k_avg_ms = kt["total_ms"] / max(kt["launches"], 1)
     per_kernel[kind] = round(k_avg_ms * 1e3, 2)
     traffic = stored_traffic(name)

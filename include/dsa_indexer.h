@@ -66,6 +66,7 @@ extern "C" {
 #define DSA_EUNSUPPORTED 2 /* valid but not implemented (e.g. head_dim not 64/128) */
 #define DSA_EWORKSPACE 3   /* workspace_bytes smaller than the *_workspace_size value */
 #define DSA_EHIP 4         /* a HIP call or kernel launch failed */
+#define DSA_ETIMEOUT 5     /* (DSA_DEBUG only) a HISA query's bounded wait gave up; see out_status */
 
 /* input element types of q, k (and k_pooled) */
 #define DSA_DTYPE_BF16 0   /* bf16 carried as 16-bit patterns */
@@ -153,6 +154,13 @@ int misa_route_score_topk(const void* q, const float* w, const void* k, const vo
  *
  *   out_blocks [nq, m_blocks] int32 surviving blocks (padded with -1) or NULL
  *   out_block_score [nq, m_blocks] float32 their block scores, or NULL
+ *   out_status [nq] int32 or NULL (4-byte aligned): 0 when the query's row is
+ *             complete, 1 when the token pass of that query gave up its
+ *             bounded wait for the query's block selection (about 0.67 s; see
+ *             dsa_hisa_wait_limit) - that row of out_idx / out_score then
+ *             holds padding only (-1, -inf), never a partial selection; the
+ *             kept blocks are still reported.  With DSA_DEBUG=1 the call also
+ *             returns DSA_ETIMEOUT when any query timed out.
  * Only DSA_DTYPE_BF16; 1 <= m_blocks; 1 <= block.
  */
 size_t hisa_block_filter_topk_workspace_size(int32_t nq, int32_t n_heads, int32_t head_dim,
@@ -164,7 +172,8 @@ int hisa_block_filter_topk(const void* q, const float* w, const void* k, const v
                            int32_t n_heads, int32_t head_dim, int32_t n_seq, int64_t l_max,
                            int32_t block, int32_t m_blocks, int32_t top_k, int32_t* out_idx,
                            float* out_score, int32_t* out_blocks, float* out_block_score,
-                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+                           int32_t* out_status, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
 
 /*
  * MISA then HISA (MISA summary, "method": the head axis; HISA review,
@@ -175,9 +184,9 @@ int hisa_block_filter_topk(const void* q, const float* w, const void* k, const v
  * weights kept: block scores
  *   bs[t, b] = sum_{j in heads_t} w[t, j] * max(0, q[t, j] . kbar[b]),
  * the m_blocks best blocks, then token scores with the same heads inside the
- * surviving blocks and the top_k.  Outputs as for hisa_block_filter_topk,
- * plus out_heads [nq, h] (most important first) and out_importance
- * [nq, n_heads], each optional.
+ * surviving blocks and the top_k.  Outputs as for hisa_block_filter_topk
+ * (out_status included), plus out_heads [nq, h] (most important first) and
+ * out_importance [nq, n_heads], each optional.
  * Only DSA_DTYPE_BF16; 1 <= h <= n_heads; 1 <= block; 1 <= m_blocks <= 1024
  * and m_blocks * block <= 8192 (DSA_EUNSUPPORTED otherwise); nq <= 65535.
  */
@@ -190,8 +199,19 @@ int misa_hisa_topk(const void* q, const float* w, const void* k, const void* k_p
                    int32_t n_heads, int32_t head_dim, int32_t n_seq, int64_t l_max, int32_t block,
                    int32_t n_active_heads, int32_t m_blocks, int32_t top_k, int32_t* out_idx,
                    float* out_score, int32_t* out_heads, float* out_importance,
-                   int32_t* out_blocks, float* out_block_score, void* workspace,
-                   size_t workspace_bytes, hipStream_t stream);
+                   int32_t* out_blocks, float* out_block_score, int32_t* out_status,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Bound of the HISA token pass's wait for its query's block selection, in
+ * ticks of the GPU's 100 MHz wall clock, for the calls that start after this
+ * one (process-wide).  ticks < 0 restores the default (2^26, about 0.67 s);
+ * 0 makes a wait give up at its first unsuccessful check, which lets a test
+ * drive the timeout path with every kernel still ending normally.  The wait
+ * only ends early when other work holds the compute units that the query's
+ * block selection needs.  Returns DSA_OK.
+ */
+int dsa_hisa_wait_limit(int64_t ticks);
 
 /*
  * Sparse attention over the selected index list, the operator the indexer

@@ -42,13 +42,14 @@ _SIGS = {
     "hisa_block_filter_topk_workspace_size": ([_i32, _i32, _i32, _i32, _i64, _i32, _i32, _i32,
                                                _i32], _sz),
     "hisa_block_filter_topk": ([_c_p, _c_p, _c_p, _c_p, _i32, _c_p, _c_p, _i32, _i32, _i32, _i32,
-                                _i64, _i32, _i32, _i32, _c_p, _c_p, _c_p, _c_p, _c_p, _sz, _c_p],
-                               ctypes.c_int),
+                                _i64, _i32, _i32, _i32, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _sz,
+                                _c_p], ctypes.c_int),
     "misa_hisa_topk_workspace_size": ([_i32, _i32, _i32, _i32, _i64, _i32, _i32, _i32, _i32,
                                        _i32], _sz),
     "misa_hisa_topk": ([_c_p, _c_p, _c_p, _c_p, _i32, _c_p, _c_p, _i32, _i32, _i32, _i32, _i64,
-                        _i32, _i32, _i32, _i32, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _sz,
-                        _c_p], ctypes.c_int),
+                        _i32, _i32, _i32, _i32, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
+                        _sz, _c_p], ctypes.c_int),
+    "dsa_hisa_wait_limit": ([_i64], ctypes.c_int),
     "sparse_mla_workspace_size": ([_i32, _i32, _i32, _i32, _i32], _sz),
     "sparse_mla_attention": ([_c_p, _c_p, _i32, _c_p, _c_p, _c_p, _i32, _i32, _i32, _i32, _i32,
                               _i64, _i32, ctypes.c_float, _c_p, _c_p, _sz, _c_p], ctypes.c_int),
@@ -152,6 +153,15 @@ def _common(q, w, k, q_pos, q_seq):
         raise ValueError("inconsistent shapes: q [nq,H,d], w [nq,H], k [n_seq,l_max,d], "
                          "q_pos/q_seq [nq]")
     return dev, nq, H, d, n_seq, l_max
+
+
+def _status(dev, nq, out_status, with_status):
+    if out_status is None:
+        return torch.empty(nq, dtype=torch.int32, device=dev) if with_status else None
+    _need(out_status, "out_status", torch.int32, 1, dev)
+    if out_status.shape[0] != nq:
+        raise ValueError("out_status must be [nq]")
+    return out_status
 
 
 def _outputs(dev, nq, k, out_idx, out_score, with_scores):
@@ -265,10 +275,13 @@ def hisa_block_filter_topk_workspace_size(nq, n_heads, head_dim, n_seq, l_max, b
 
 
 def hisa_block_filter_topk(q, w, k, q_pos, q_seq=None, *, block: int, m_blocks: int, top_k: int,
-                           k_pooled=None, with_scores=True, with_blocks=True, out_idx=None,
-                           out_score=None, workspace=None) -> Dict[str, torch.Tensor]:
+                           k_pooled=None, with_scores=True, with_blocks=True, with_status=True,
+                           out_idx=None, out_score=None, out_status=None,
+                           workspace=None) -> Dict[str, torch.Tensor]:
     """HISA: top-m pooled blocks, then top_k tokens inside them.  Returns a dict
-    with "idx", "score" and, if asked, "blocks" and "block_score"."""
+    with "idx", "score" and, if asked, "blocks", "block_score" and "status"
+    ([nq] int32: 1 where the query's wait for its block selection timed out and
+    its row holds padding only; see dsa_hisa_wait_limit)."""
     dev, nq, H, d, n_seq, l_max = _common(q, w, k, q_pos, q_seq)
     if q.dtype != torch.bfloat16:
         raise TypeError("HISA takes bf16 inputs")
@@ -279,18 +292,22 @@ def hisa_block_filter_topk(q, w, k, q_pos, q_seq=None, *, block: int, m_blocks: 
     out_idx, out_score = _outputs(dev, nq, top_k, out_idx, out_score, with_scores)
     blocks = torch.empty((nq, m_blocks), dtype=torch.int32, device=dev) if with_blocks else None
     bscore = torch.empty((nq, m_blocks), dtype=torch.float32, device=dev) if with_blocks else None
+    status = _status(dev, nq, out_status, with_status)
     nbytes = hisa_block_filter_topk_workspace_size(nq, H, d, n_seq, l_max, block, m_blocks, top_k,
                                                    k_pooled is not None)
     ws = _workspace(nbytes, dev, workspace)
     st = lib().hisa_block_filter_topk(_ptr(q), _ptr(w), _ptr(k), _ptr(k_pooled), DSA_DTYPE_BF16,
                                       _ptr(q_seq), _ptr(q_pos), nq, H, d, n_seq, l_max, block,
                                       m_blocks, top_k, _ptr(out_idx), _ptr(out_score),
-                                      _ptr(blocks), _ptr(bscore), _ptr(ws), nbytes, _stream(dev))
+                                      _ptr(blocks), _ptr(bscore), _ptr(status), _ptr(ws), nbytes,
+                                      _stream(dev))
     _check(st, "hisa_block_filter_topk")
     out = {"idx": out_idx, "score": out_score}
     if blocks is not None:
         out["blocks"] = blocks
         out["block_score"] = bscore
+    if status is not None:
+        out["status"] = status
     return out
 
 
@@ -303,12 +320,12 @@ def misa_hisa_topk_workspace_size(nq, n_heads, head_dim, n_seq, l_max, block, n_
 
 def misa_hisa_topk(q, w, k, q_pos, q_seq=None, *, block: int, n_active_heads: int,
                    m_blocks: int, top_k: int, k_pooled=None, with_scores=True, with_heads=True,
-                   with_importance=False, with_blocks=True, out_idx=None, out_score=None,
-                   workspace=None) -> Dict[str, torch.Tensor]:
+                   with_importance=False, with_blocks=True, with_status=True, out_idx=None,
+                   out_score=None, out_status=None, workspace=None) -> Dict[str, torch.Tensor]:
     """MISA then HISA: h routed heads, then the top-m pooled blocks and the
     top_k tokens inside them, both scored with those heads.  Returns a dict
-    with "idx", "score" and, if asked, "heads", "importance", "blocks" and
-    "block_score"."""
+    with "idx", "score" and, if asked, "heads", "importance", "blocks",
+    "block_score" and "status" (as for hisa_block_filter_topk)."""
     dev, nq, H, d, n_seq, l_max = _common(q, w, k, q_pos, q_seq)
     if q.dtype != torch.bfloat16:
         raise TypeError("MISA-HISA takes bf16 inputs")
@@ -322,14 +339,15 @@ def misa_hisa_topk(q, w, k, q_pos, q_seq=None, *, block: int, n_active_heads: in
     imp = torch.empty((nq, H), dtype=torch.float32, device=dev) if with_importance else None
     blocks = torch.empty((nq, m_blocks), dtype=torch.int32, device=dev) if with_blocks else None
     bscore = torch.empty((nq, m_blocks), dtype=torch.float32, device=dev) if with_blocks else None
+    status = _status(dev, nq, out_status, with_status)
     nbytes = misa_hisa_topk_workspace_size(nq, H, d, n_seq, l_max, block, h, m_blocks, top_k,
                                            k_pooled is not None)
     ws = _workspace(nbytes, dev, workspace)
     st = lib().misa_hisa_topk(_ptr(q), _ptr(w), _ptr(k), _ptr(k_pooled), DSA_DTYPE_BF16,
                               _ptr(q_seq), _ptr(q_pos), nq, H, d, n_seq, l_max, block, h,
                               m_blocks, top_k, _ptr(out_idx), _ptr(out_score), _ptr(heads),
-                              _ptr(imp), _ptr(blocks), _ptr(bscore), _ptr(ws), nbytes,
-                              _stream(dev))
+                              _ptr(imp), _ptr(blocks), _ptr(bscore), _ptr(status), _ptr(ws),
+                              nbytes, _stream(dev))
     _check(st, "misa_hisa_topk")
     out = {"idx": out_idx, "score": out_score}
     if heads is not None:
@@ -339,7 +357,16 @@ def misa_hisa_topk(q, w, k, q_pos, q_seq=None, *, block: int, n_active_heads: in
     if blocks is not None:
         out["blocks"] = blocks
         out["block_score"] = bscore
+    if status is not None:
+        out["status"] = status
     return out
+
+
+def hisa_wait_limit(ticks: int) -> None:
+    """Bound of the HISA token pass's wait for its query's block selection, in
+    ticks of the GPU's 100 MHz wall clock, for later calls; ticks < 0 restores
+    the default (about 0.67 s).  For tests of the timeout path."""
+    _check(lib().dsa_hisa_wait_limit(int(ticks)), "dsa_hisa_wait_limit")
 
 
 def sparse_mla_workspace_size(nq, n_heads, d_qk, d_v, top_k) -> int:
@@ -423,7 +450,7 @@ __all__ = [
     "indexer_mean_pool_keys",
     "misa_route_score_topk", "misa_route_score_topk_workspace_size",
     "hisa_block_filter_topk", "hisa_block_filter_topk_workspace_size",
-    "misa_hisa_topk", "misa_hisa_topk_workspace_size",
+    "misa_hisa_topk", "misa_hisa_topk_workspace_size", "hisa_wait_limit",
     "sparse_mla_attention", "sparse_mla_workspace_size",
     "indexer_selection_iou",
 ]

@@ -3,6 +3,7 @@
 #include "../../include/dsa_indexer.h"
 
 #include <algorithm>
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -17,6 +18,8 @@
 namespace {
 
 thread_local std::string g_err;
+// bound of the HISA token pass's wait for its query's block selection
+std::atomic<uint64_t> g_hisa_spin{dsa::kHisaSpinTicks};
 
 int fail(int code, const char* fmt, ...) {
   char buf[512];
@@ -378,7 +381,7 @@ HisaFusedPlan plan_hisa_fused(int64_t nq, int head_dim, int n_seq, int64_t l_max
 
 int run_prepare(void* ws, size_t zero_bytes, const void* k, const int32_t* q_seq,
                 const int32_t* q_pos, int nq, int n_seq, int head_dim, int block, int64_t l_max,
-                uint16_t* partial, hipStream_t stream) {
+                uint16_t* partial, hipStream_t stream, int32_t* status = nullptr) {
   dsa::PrepArgs pa{};
   pa.zero = at<uint32_t>(ws, 0);
   pa.zero_words = zero_bytes / 4;
@@ -391,6 +394,7 @@ int run_prepare(void* ws, size_t zero_bytes, const void* k, const int32_t* q_seq
   pa.block = block;
   pa.l_max = l_max;
   pa.partial = partial;
+  pa.status = status;
   return hip_status(timed(DSA_KERNEL_PREPARE, stream, [&] { return dsa::launch_prepare(pa, stream); }),
                     "prepare kernel", stream);
 }
@@ -436,7 +440,8 @@ int run_hisa_kernels(const HisaFusedPlan& f, const void* q, const float* w, cons
                      const int32_t* q_pos, const HisaRoute& route, int nq, int n_heads,
                      int head_dim, int n_seq, int64_t l_max, int block, int m_blocks, int top_k,
                      int32_t* out_idx, float* out_score, int32_t* out_blocks,
-                     float* out_block_score, void* workspace, hipStream_t stream) {
+                     float* out_block_score, int32_t* out_status, void* workspace,
+                     hipStream_t stream) {
   dsa::HisaArgs h{};
   h.q = reinterpret_cast<const uint16_t*>(q);
   h.w = w;
@@ -477,8 +482,27 @@ int run_hisa_kernels(const HisaFusedPlan& f, const void* q, const float* w, cons
   h.out_idx = out_idx;
   h.out_score = out_score;
   h.out_block_score = out_block_score;
-  return hip_status(timed(DSA_KERNEL_HISA, stream, [&] { return dsa::launch_hisa(h, stream); }),
-                    "HISA kernel", stream);
+  h.out_status = out_status;
+  h.spin_ticks = g_hisa_spin.load(std::memory_order_relaxed);
+  int st = hip_status(timed(DSA_KERNEL_HISA, stream, [&] { return dsa::launch_hisa(h, stream); }),
+                      "HISA kernel", stream);
+  if (st || !debug_sync()) return st;
+  // DSA_DEBUG: the call has completed; report queries whose token pass gave up
+  // its wait (their rows hold padding only)
+  std::vector<uint32_t> sy((size_t)nq * dsa::kHisaSyncWords);
+  hipError_t e = hipMemcpyAsync(sy.data(), h.sync, sy.size() * 4, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail(DSA_EHIP, "HISA status read (DSA_DEBUG): %s", hipGetErrorString(e));
+  int n_to = 0, first = -1;
+  for (int t = 0; t < nq; ++t)
+    if (sy[(size_t)t * dsa::kHisaSyncWords + dsa::kHisaSyncTimeout]) {
+      if (first < 0) first = t;
+      ++n_to;
+    }
+  if (n_to)
+    return fail(DSA_ETIMEOUT, "HISA: %d queries (first: %d) timed out waiting for their block "
+                "selection; their rows hold padding only", n_to, first);
+  return DSA_OK;
 }
 
 // MISA∘HISA: the HISA plan, then the router's per-slice sums.
@@ -647,7 +671,12 @@ extern "C" {
 
 const char* dsa_last_error(void) { return g_err.c_str(); }
 
-int dsa_abi_version(void) { return 1; }
+int dsa_abi_version(void) { return 2; }
+
+int dsa_hisa_wait_limit(int64_t ticks) {
+  g_hisa_spin.store(ticks < 0 ? dsa::kHisaSpinTicks : (uint64_t)ticks, std::memory_order_relaxed);
+  return DSA_OK;
+}
 
 int dsa_kernel_timing(int enable) {
   std::lock_guard<std::mutex> lk(g_tmu);
@@ -887,7 +916,8 @@ int hisa_block_filter_topk(const void* q, const float* w, const void* k, const v
                            int32_t n_heads, int32_t head_dim, int32_t n_seq, int64_t l_max,
                            int32_t block, int32_t m_blocks, int32_t top_k, int32_t* out_idx,
                            float* out_score, int32_t* out_blocks, float* out_block_score,
-                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                           int32_t* out_status, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
   int st = check_common(q, w, k, dtype, q_pos, nq, n_heads, head_dim, n_seq, l_max, top_k, out_idx);
   if (st) return st;
   if (dtype != DSA_DTYPE_BF16) return fail(DSA_EUNSUPPORTED, "HISA supports bf16 inputs only");
@@ -896,6 +926,7 @@ int hisa_block_filter_topk(const void* q, const float* w, const void* k, const v
   if ((int64_t)m_blocks * block > 0x7FFFFFFF) return fail(DSA_EINVAL, "m_blocks * block too large");
   if (nq == 0) return DSA_OK;
   if (k_pooled && !aligned(k_pooled, 16)) return fail(DSA_EINVAL, "k_pooled must be 16-byte aligned");
+  if (!aligned(out_status, 4)) return fail(DSA_EINVAL, "out_status must be 4-byte aligned");
   HisaFusedPlan f = plan_hisa_fused(nq, head_dim, n_seq, l_max, block, m_blocks, k_pooled != nullptr);
   if (f.ok) {
     if ((st = check_ws(workspace, workspace_bytes, f.total))) return st;
@@ -906,7 +937,8 @@ int hisa_block_filter_topk(const void* q, const float* w, const void* k, const v
       return st;
     return run_hisa_kernels(f, q, w, k, pooled, partial, q_seq, q_pos, HisaRoute{}, nq,
                             n_heads, head_dim, n_seq, l_max, block, m_blocks, top_k, out_idx,
-                            out_score, out_blocks, out_block_score, workspace, stream);
+                            out_score, out_blocks, out_block_score, out_status, workspace,
+                            stream);
   }
   HisaPlan p = plan_hisa(nq, head_dim, n_seq, l_max, block, m_blocks, k_pooled != nullptr);
   if ((st = check_ws(workspace, workspace_bytes, p.total))) return st;
@@ -920,8 +952,9 @@ int hisa_block_filter_topk(const void* q, const float* w, const void* k, const v
     pooled = dst;
   }
   uint16_t* partial = at<uint16_t>(workspace, p.partial);
+  // (the passes of this path never wait: every query's status is 0)
   if ((st = run_prepare(workspace, p.zero_bytes, k, q_seq, q_pos, nq, n_seq, head_dim, block,
-                        l_max, partial, stream)))
+                        l_max, partial, stream, out_status)))
     return st;
   // stage 1: block scores over the pooled keys, top-m blocks
   int32_t* blocks = out_blocks ? out_blocks : at<int32_t>(workspace, p.blocks);
@@ -966,8 +999,8 @@ int misa_hisa_topk(const void* q, const float* w, const void* k, const void* k_p
                    int32_t n_heads, int32_t head_dim, int32_t n_seq, int64_t l_max, int32_t block,
                    int32_t n_active_heads, int32_t m_blocks, int32_t top_k, int32_t* out_idx,
                    float* out_score, int32_t* out_heads, float* out_importance,
-                   int32_t* out_blocks, float* out_block_score, void* workspace,
-                   size_t workspace_bytes, hipStream_t stream) {
+                   int32_t* out_blocks, float* out_block_score, int32_t* out_status,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
   int st = check_common(q, w, k, dtype, q_pos, nq, n_heads, head_dim, n_seq, l_max, top_k, out_idx);
   if (st) return st;
   if (dtype != DSA_DTYPE_BF16) return fail(DSA_EUNSUPPORTED, "MISA-HISA supports bf16 inputs only");
@@ -977,6 +1010,7 @@ int misa_hisa_topk(const void* q, const float* w, const void* k, const void* k_p
   if (m_blocks < 1) return fail(DSA_EINVAL, "m_blocks must be >= 1 (got %d)", m_blocks);
   if (nq == 0) return DSA_OK;
   if (k_pooled && !aligned(k_pooled, 16)) return fail(DSA_EINVAL, "k_pooled must be 16-byte aligned");
+  if (!aligned(out_status, 4)) return fail(DSA_EINVAL, "out_status must be 4-byte aligned");
   MisaHisaPlan p = plan_misa_hisa(nq, n_heads, head_dim, n_seq, l_max, block, m_blocks,
                                   k_pooled != nullptr);
   if (!p.h.ok)
@@ -1016,7 +1050,7 @@ int misa_hisa_topk(const void* q, const float* w, const void* k, const void* k_p
   route.out_importance = out_importance;
   return run_hisa_kernels(p.h, q, w, k, pooled, partial, q_seq, q_pos, route, nq, n_heads,
                           head_dim, n_seq, l_max, block, m_blocks, top_k, out_idx, out_score,
-                          out_blocks, out_block_score, workspace, stream);
+                          out_blocks, out_block_score, out_status, workspace, stream);
 }
 
 }  // extern "C"

@@ -47,9 +47,18 @@ struct HisaArgs {
   int32_t* out_idx;            // [nq, top_k]
   float* out_score;            // [nq, top_k] or null
   float* out_block_score;      // [nq, m_blocks] or null
+  int32_t* out_status;         // [nq] 0 = complete, 1 = a wait timed out (row padded), or null
+  // longest wait of a token-pass workgroup for its query's block selection,
+  // in ticks of the 100 MHz wall clock
+  uint64_t spin_ticks;
 };
+// default bound of that wait: ~0.67 s
+constexpr uint64_t kHisaSpinTicks = 1ull << 26;
 constexpr int kHisaBins = 4096;
+// per-query sync words: [0] block-pass workgroups arrived, [1] nonzero when a
+// token-pass wait of the query timed out
 constexpr int kHisaSyncWords = 2;
+constexpr int kHisaSyncTimeout = 1;
 constexpr int kHisaMaxGroups = 64;
 constexpr int kHisaMaxChunk = 2048;
 constexpr uint32_t kHisaListCap = 2048;

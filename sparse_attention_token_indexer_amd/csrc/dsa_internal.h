@@ -69,6 +69,7 @@ struct PrepArgs {
   int nq, n_seq, head_dim, block;
   int64_t l_max;
   uint16_t* partial;           // [nq, D] or null
+  int32_t* status;             // [nq] per-query status words cleared with the region, or null
 };
 hipError_t launch_prepare(const PrepArgs& a, hipStream_t stream);
 

@@ -31,8 +31,10 @@
 // workgroups are consecutive in dispatch order (blockIdx.x runs fastest), so
 // the query groups dispatched first can always finish and free room for the
 // rest; in the 1-D grid every block-pass item precedes every token-pass
-// item.  The waits are also bounded in time: a query whose wait times out is
-// marked in its sync words and left incomplete.
+// item.  The waits are also bounded in time (HisaArgs::spin_ticks): a
+// workgroup whose wait times out marks its query in the query's sync words and
+// stops; k_hisa_topk then writes an all-padding row for that query and reports
+// it in out_status, so an incomplete query never returns a partial selection.
 #include "dsa_hisa.h"
 #include "dsa_internal.h"
 #include "dsa_scorers.h"
@@ -61,13 +63,12 @@ struct Hist {
 };
 constexpr int kHistWords = Hist<kHT>::kWords;
 DSA_DEVICE int hpad(int b) { return Hist<kHT>::at(b); }
-constexpr uint64_t kSpinTicks = 1ull << 26;     // ~0.67 s of the 100 MHz wall clock
 constexpr int kSU = 8;                          // entries per thread per pass step
 constexpr int kHisaSegRead = 96;                // candidate slots read per segment up front
 
 enum SyncWord {
-  S_ARRIVE1 = 0,   // block-pass workgroups done
-  S_TIMEOUT = 1,   // a wait of this query timed out
+  S_ARRIVE1 = 0,                  // block-pass workgroups done
+  S_TIMEOUT = kHisaSyncTimeout,   // a wait of this query timed out
 };
 
 // Device-scope stores and loads of data shared between workgroups.
@@ -132,14 +133,14 @@ struct DevSegSource {
 };
 
 // Thread-level wait until *p != 0; returns *p, or 0 (and the query marked)
-// on timeout.
-DSA_DEVICE int32_t wait_nonzero(int32_t* p, uint32_t* timeout_word) {
+// when `ticks` of the wall clock pass first.
+DSA_DEVICE int32_t wait_nonzero(int32_t* p, uint32_t* timeout_word, uint64_t ticks) {
   int32_t v = ld_dev(p);
   if (v != 0) return v;
   const uint64_t t0 = wall_clock64();
   while ((v = ld_dev(p)) == 0) {
     __builtin_amdgcn_s_sleep(1);
-    if (wall_clock64() - t0 > kSpinTicks) {
+    if (wall_clock64() - t0 > ticks) {
       __hip_atomic_store(timeout_word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return 0;
     }
@@ -658,7 +659,7 @@ __global__ __launch_bounds__(kHT) __attribute__((amdgpu_waves_per_eu(2))) void k
   if (tid == 0) s_go = 1;
   __syncthreads();
   for (int i = tid; i <= li1 - li0; i += kHT) {
-    const int32_t v = wait_nonzero(&bflag[li0 + i], &sy[S_TIMEOUT]);
+    const int32_t v = wait_nonzero(&bflag[li0 + i], &sy[S_TIMEOUT], a.spin_ticks);
     if (v == 0) s_go = 0;
     sblk[i] = v - 1;
   }
@@ -701,7 +702,12 @@ __global__ __launch_bounds__(kTT) void k_hisa_topk(HisaArgs a) {
   const int64_t pos = a.q_pos[t];
   int32_t* out_i = a.out_idx + (size_t)t * a.top_k;
   float* out_s = a.out_score ? a.out_score + (size_t)t * a.top_k : nullptr;
-  if (!(seq >= 0 && seq < a.n_seq && pos >= 0 && pos < a.l_max)) {   // no keys: padding only
+  const bool valid = seq >= 0 && seq < a.n_seq && pos >= 0 && pos < a.l_max;
+  // a token-pass workgroup of this query gave up its wait (k_hisa ended before
+  // this kernel started, so the mark is final): its keys were never stored
+  const bool timed_out = valid && ld_dev(a.sync + (size_t)t * kHisaSyncWords + S_TIMEOUT) != 0u;
+  if (a.out_status && tid == 0) a.out_status[t] = timed_out ? 1 : 0;
+  if (!valid || timed_out) {                   // no keys, or incomplete: padding only
     for (int i = tid; i < a.top_k; i += kTT) {
       out_i[i] = -1;
       if (out_s) out_s[i] = -__builtin_inff();

@@ -74,13 +74,17 @@ __global__ __launch_bounds__(256) void k_mean_pool(const uint16_t* __restrict__ 
   }
 }
 
-// Blocks [0, n_zero_blocks) clear the zero region; block n_zero_blocks + t pools
+// Blocks [0, n_zero_blocks) clear the zero region (and the status words, if
+// given); block n_zero_blocks + t pools
 // query t's partial last block when its prefix does not end on a block boundary.
 __global__ __launch_bounds__(256) void k_prepare(PrepArgs a, int n_zero_blocks) {
   if ((int)blockIdx.x < n_zero_blocks) {
     const size_t stride = (size_t)n_zero_blocks * 256;
     for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < a.zero_words; i += stride)
       a.zero[i] = 0u;
+    if (a.status)
+      for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < (size_t)a.nq; i += stride)
+        a.status[i] = 0;
     return;
   }
   const int t = blockIdx.x - n_zero_blocks;
@@ -136,6 +140,7 @@ hipError_t launch_mean_pool(const uint16_t* k, int n_seq, int64_t l_max, int hea
 
 hipError_t launch_prepare(const PrepArgs& a, hipStream_t stream) {
   int nz = (int)((a.zero_words + 255) / 256);
+  if (a.status && nz == 0) nz = 1;
   if (nz > 1024) nz = 1024;
   const int np = a.partial ? a.nq : 0;
   if (nz + np == 0) return hipSuccess;

@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(lib):
     missing = [n for n in _declared() if not hasattr(lib, n)]
     assert not missing, missing
     assert set(_declared()) <= set(dsa._SIGS)
-    assert lib.dsa_abi_version() == 1
+    assert lib.dsa_abi_version() == 2
 
 
 def test_workspace_sizes_are_positive_and_monotone(lib):
@@ -79,8 +79,12 @@ def test_argument_errors_return_before_any_launch(lib):
                                      1, 100, 16, 9, 0, 4, aligned, None, None, None, None, None,
                                      0, None) == 1                   # h > n_heads
     assert lib.hisa_block_filter_topk(aligned, aligned, aligned, None, 1, None, aligned, 1, 8, 128,
-                                      1, 100, 16, 4, 4, aligned, None, None, None, None, 0,
-                                      None) == 2                     # f32 HISA unsupported
+                                      1, 100, 16, 4, 4, aligned, None, None, None, None, None,
+                                      0, None) == 2                  # f32 HISA unsupported
+    assert lib.hisa_block_filter_topk(aligned, aligned, aligned, None, 0, None, aligned, 1, 8, 128,
+                                      1, 100, 16, 4, 4, aligned, None, None, None, aligned + 2,
+                                      None, 0, None) == 1            # misaligned out_status
+    assert b"out_status" in lib.dsa_last_error()
 
 
 def _call_mla(lib, **kw):
@@ -126,12 +130,13 @@ def test_sparse_attention_workspace_sizes(lib):
 def _call_misa_hisa(lib, **kw):
     args = dict(q=16, w=4, k=16, kp=None, dtype=0, q_seq=None, q_pos=4, nq=1, H=32, d=128,
                 n_seq=1, l_max=4096, B=128, h=8, m=16, top_k=64, out_idx=4, out_score=None,
-                heads=None, imp=None, blocks=None, bscore=None, ws=None, ws_bytes=0, stream=None)
+                heads=None, imp=None, blocks=None, bscore=None, status=None, ws=None, ws_bytes=0,
+                stream=None)
     args.update(kw)
     return lib.misa_hisa_topk(*[args[x] for x in (
         "q", "w", "k", "kp", "dtype", "q_seq", "q_pos", "nq", "H", "d", "n_seq", "l_max", "B",
-        "h", "m", "top_k", "out_idx", "out_score", "heads", "imp", "blocks", "bscore", "ws",
-        "ws_bytes", "stream")])
+        "h", "m", "top_k", "out_idx", "out_score", "heads", "imp", "blocks", "bscore", "status",
+        "ws", "ws_bytes", "stream")])
 
 
 def test_misa_hisa_rejects_bad_arguments(lib):
@@ -143,6 +148,15 @@ def test_misa_hisa_rejects_bad_arguments(lib):
     assert _call_misa_hisa(lib, dtype=1) == EUNSUP
     assert _call_misa_hisa(lib, m=65, B=128) == EUNSUP       # m * B above 8192
     assert _call_misa_hisa(lib, m=1025, B=4) == EUNSUP       # more blocks than supported
+    assert _call_misa_hisa(lib, status=6) == EINVAL          # misaligned out_status
     assert _call_misa_hisa(lib) == EWS
     assert dsa.misa_hisa_topk_workspace_size(32, 32, 128, 32, 1 << 20, 128, 8, 64, 2048, 1) > \
         dsa.hisa_block_filter_topk_workspace_size(32, 32, 128, 32, 1 << 20, 128, 64, 2048, 1)
+
+
+def test_hisa_wait_limit_hook(lib):
+    """The test hook that bounds the HISA token pass's wait is callable without a
+    GPU (it only sets the limit later calls pass to the kernel)."""
+    assert lib.dsa_hisa_wait_limit(0) == 0
+    assert lib.dsa_hisa_wait_limit(-1) == 0          # back to the default
+    assert lib.dsa_abi_version() == 2

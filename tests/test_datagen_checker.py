@@ -3,7 +3,7 @@ import numpy as np
 
 import datagen
 from oracle import indexer as O
-from oracle.check import check_selection
+from oracle.check import FLOOR, RTOL, check_selection, rounding_bound, score_tolerance, scores_ok
 
 
 def test_generation_is_deterministic_and_chunk_independent():
@@ -98,6 +98,82 @@ def test_checker_tie_band_allows_swaps_only_inside_band():
     # all-equal scores: every swap is inside the band, but the count must hold
     z = np.zeros(10)
     assert check_selection(np.array([9, 8, 7]), None, np.arange(10), z, z + 1, 3) == []
+
+
+def _edge_row():
+    """20 keys with distinct, well separated scores and no cancellation (A = |s|,
+    F = 0): the rounding bound is 2^-17 |s|, far below the literal 2e-3 |s|."""
+    s = 10.0 - 0.25 * np.arange(20)
+    A = np.abs(s)
+    F = np.zeros(20)
+    return s, A, F
+
+
+def test_checker_score_tolerance_edges():
+    """A returned score 0.99x the tolerance away passes and 1.01x fails, in the
+    literal regime (2e-3 relative) and in the cancellation regime, where the
+    float32 rounding bound E = 2^-17 (F + A) is the tolerance."""
+    s, A, F = _edge_row()
+    ids = np.arange(20)
+    idx, val = O.top_k(s, ids, 5)
+    tol = RTOL * np.abs(val)
+    for f, fails in ((0.99, False), (1.01, True)):
+        for sign in (1.0, -1.0):
+            v = val.copy()
+            v[2] += sign * f * tol[2]
+            assert bool(check_selection(idx, v, ids, s, A, 5, F)) == fails, (f, sign)
+    # cancellation: a score of 1e-6 from terms of size 1 (A = 1, F = 10)
+    s2 = np.array([3.0, 1e-6, -2.0])
+    A2 = np.array([3.0, 1.0, 2.0])
+    F2 = np.array([3.0, 10.0, 2.0])
+    E = FLOOR * (F2[1] + A2[1])
+    assert E > 100 * RTOL * s2[1]
+    for f, fails in ((0.99, False), (1.01, True)):
+        v = np.array([3.0, 1e-6 + f * E])
+        assert bool(check_selection(np.array([0, 1]), v, np.arange(3), s2, A2, 2, F2)) == fails
+    # the relative tolerance is not widened by the magnitude A any more: with
+    # A = 2.2 |s| (typical cancellation at the k-th score), an error of
+    # 1.5 x 2e-3 |s| fails although it is below 2e-3 A
+    s3 = np.array([1.0, 0.5])
+    A3 = np.array([2.2, 0.5])
+    v3 = np.array([1.0 + 1.5 * RTOL])
+    assert check_selection(np.array([0]), v3, np.arange(2), s3, A3, 1, np.zeros(2))
+
+
+def test_checker_band_edge_swaps():
+    """Swapping the k-th key for a key just inside the literal band (0.99 x
+    2e-3 |s*| below s*) passes; just outside it (1.01 x) fails."""
+    s, A, F = _edge_row()
+    k = 5
+    s_star = s[k - 1]
+    ids = np.arange(20)
+    for f, fails in ((0.99, False), (1.01, True)):
+        s2 = s.copy()
+        s2[k] = s_star - f * RTOL * abs(s_star)        # the next key, at the band edge
+        A2 = np.abs(s2)
+        idx, _ = O.top_k(s2, ids, k)
+        swapped = idx.copy()
+        swapped[k - 1] = k                              # k-th key out, edge key in
+        assert bool(check_selection(swapped, None, ids, s2, A2, k, F)) == fails, f
+        assert check_selection(idx, None, ids, s2, A2, k, F) == []
+
+
+def test_checker_counts_what_only_the_rounding_bound_admits():
+    s2 = np.array([3.0, 1e-6, -2.0])
+    A2 = np.array([3.0, 1.0, 2.0])
+    F2 = np.array([3.0, 10.0, 2.0])
+    st = {}
+    assert check_selection(np.array([0, 1]), np.array([3.0, 1e-6 + 1e-5]), np.arange(3), s2, A2,
+                           2, F2, stats=st) == []
+    assert st["score_fallback"] == 1
+    st = {}
+    s, A, F = _edge_row()
+    assert check_selection(*O.top_k(s, np.arange(20), 5), np.arange(20), s, A, 5, F,
+                           stats=st) == []
+    assert st == {"score_fallback": 0, "band_fallback": 0}
+    e = rounding_bound(A2, F2)
+    assert np.allclose(score_tolerance(s2, A2, F2), np.maximum(RTOL * np.abs(s2), e))
+    assert scores_ok(np.array([3.0 + 0.9 * RTOL * 3.0]), np.array([3.0]), np.array([3.0])).all()
 
 
 def test_mla_inputs_regenerate_and_lists_are_valid():

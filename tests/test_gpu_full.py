@@ -1,6 +1,7 @@
 """GPU parity at the full workload sizes, in the launch configuration bench.py
 times; the oracle checks sampled queries one by one (keys of the sampled
 queries' sequences are regenerated on the host from the same seeds)."""
+import threading
 from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
@@ -9,7 +10,7 @@ import torch
 
 import datagen
 from oracle import indexer as O
-from oracle.check import FLOOR, RTOL, check_selection
+from oracle.check import check_selection, scores_ok
 
 from _helpers import say, to_device
 
@@ -25,18 +26,54 @@ def dsa():
     return m
 
 
-def _device_inputs(wl, seed=0):
+def _device_inputs(wl, seed=0, per_seq=None):
     """q, w, positions on the device; K generated per sequence straight into a
-    device tensor (host memory stays at one sequence per worker)."""
+    device tensor (host memory stays at one sequence per worker).  per_seq(s,
+    keys of s), if given, runs in the worker on each sequence's host keys; its
+    results come back as a list (oracle work that needs every sequence's keys)."""
     q, w = datagen.queries(wl, seed)
     q_seq, q_pos = datagen.positions(wl)
     kdev = torch.empty((wl.n_seq, wl.l_max, wl.head_dim), dtype=torch.bfloat16, device="cuda")
+    extra = [None] * wl.n_seq
+
+    def gen(s):
+        ks = datagen.keys(wl, s, q, w, seed)
+        if per_seq is not None:
+            extra[s] = per_seq(s, ks, q, w)
+        return ks
+
     with ThreadPoolExecutor(max_workers=16) as ex:
-        for s, ks in enumerate(ex.map(lambda s: datagen.keys(wl, s, q, w, seed), range(wl.n_seq))):
+        for s, ks in enumerate(ex.map(gen, range(wl.n_seq))):
             kdev[s].copy_(to_device(ks, wl.dtype))
     dev = {"q": to_device(q, wl.dtype), "w": torch.from_numpy(w).cuda(), "k": kdev,
            "q_seq": torch.from_numpy(q_seq).cuda(), "q_pos": torch.from_numpy(q_pos).cuda()}
-    return dev, {"q": q, "w": w, "q_seq": q_seq, "q_pos": q_pos}
+    host = {"q": q, "w": w, "q_seq": q_seq, "q_pos": q_pos}
+    if per_seq is not None:
+        host["per_seq"] = extra
+    return dev, host
+
+
+def _dense_topk_of_own_query(wl):
+    """per_seq hook for the decode layout (query t on sequence t at l_max - 1):
+    the oracle's dense top-k of that query."""
+    def f(s, ks, q, w):
+        t = s
+        r = O.dense_row(O.to_f64(q[t], wl.dtype), w[t].astype(np.float64), O.to_f64(ks, wl.dtype),
+                        wl.l_max - 1, wl.top_k)
+        return r["idx"].astype(np.int32)
+    return f
+
+
+def _iou_report(dsa, name, gpu_idx, ref_idx):
+    """IoU of a variant's selection against a dense selection, per query: the
+    GPU kernel's value must equal the oracle's; prints mean and min."""
+    g = dsa.indexer_selection_iou(torch.from_numpy(np.ascontiguousarray(gpu_idx, np.int32)).cuda(),
+                                  torch.from_numpy(np.ascontiguousarray(ref_idx, np.int32)).cuda())
+    g = g.cpu().numpy().astype(np.float64)
+    o = O.iou_rows(gpu_idx, ref_idx)
+    np.testing.assert_allclose(g, o, rtol=1e-6, atol=1e-7)
+    say(f"[iou] {name}: mean {o.mean():.4f} min {o.min():.4f} max {o.max():.4f} over {o.size} queries")
+    return o
 
 
 def _host_row(wl, hostin, t, seed=0):
@@ -45,10 +82,34 @@ def _host_row(wl, hostin, t, seed=0):
     return O.to_f64(hostin["q"][t], wl.dtype), hostin["w"][t].astype(np.float64), K, int(hostin["q_pos"][t])
 
 
+def _rows_parallel(fn, rows, workers=16):
+    """fn(t) -> list of failure strings, over the rows in a thread pool (the
+    oracle's NumPy work releases the interpreter lock); failures in row order."""
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        return [e for errs in ex.map(fn, rows) for e in errs]
+
+
+# what only the float32 rounding fallback of the matching rule admitted, per test
+_FALLBACK = {}
+_FALLBACK_LOCK = threading.Lock()
+
+
+@pytest.fixture(autouse=True)
+def _fallback_report():
+    _FALLBACK.clear()
+    yield
+    say(f"[checker] admitted only by the rounding bound: {dict(_FALLBACK)}")
+
+
 def _check(gi, gv, r, k, q_t, w_t, K, what, heads=None):
     qq, ww = (q_t, w_t) if heads is None else (q_t[heads], w_t[heads])
     F = O.dot_magnitude(qq, ww, K[r["cand"]])
-    return check_selection(gi, gv, r["cand"], r["s"], r["A"], k, F, what=what)
+    st = {}
+    errs = check_selection(gi, gv, r["cand"], r["s"], r["A"], k, F, what=what, stats=st)
+    with _FALLBACK_LOCK:               # (rows are checked on several threads)
+        for key, v in st.items():
+            _FALLBACK[key] = _FALLBACK.get(key, 0) + v
+    return errs
 
 
 def test_dense_decode_full(dsa):
@@ -68,7 +129,9 @@ def test_dense_decode_full(dsa):
 
 
 def test_misa_full(dsa):
-    """64 x 131072, B 64, h 8 of 64 heads, k 2048 (MISA) and k' 8192 (dagger)."""
+    """64 x 131072, B 64, h 8 of 64 heads, k 2048 (MISA) and k' 8192 (dagger);
+    every query, each stage on the GPU's own upstream choice; the dense call on
+    the same inputs and the IoU of both variants against it."""
     wl = datagen.WORKLOADS[4]
     say("[full] MISA 64 x 131072")
     dev, h = _device_inputs(wl)
@@ -79,11 +142,19 @@ def test_misa_full(dsa):
     md = dsa.misa_route_score_topk(dev["q"], dev["w"], dev["k"], dev["q_pos"], dev["q_seq"],
                                    block=wl.block, n_active_heads=wl.n_active_heads,
                                    top_k=wl.top_k, k_prime=wl.k_prime, k_pooled=kp, with_cand=True)
+    dn, _ = dsa.indexer_score_topk(dev["q"], dev["w"], dev["k"], dev["q_pos"], dev["q_seq"],
+                                   top_k=wl.top_k, with_scores=False)
     mi, mv, heads = (m[x].cpu().numpy() for x in ("idx", "score", "heads"))
     di, dv, cand, dheads = (md[x].cpu().numpy() for x in ("idx", "score", "cand", "heads"))
+    dni = dn.cpu().numpy()
     assert np.array_equal(heads, dheads)
-    errs = []
-    for t in range(0, wl.nq, 8):
+    # selection agreement with the dense indexer on the same inputs (MISA
+    # summary, "results": the pages report MISA dagger above 92 % per layer)
+    _iou_report(dsa, "MISA h=8 vs dense (64 x 131072)", mi, dni)
+    _iou_report(dsa, "MISA dagger k'=8192 vs dense (64 x 131072)", di, dni)
+
+    def row(t):
+        errs = []
         q_t, w_t, K, p = _host_row(wl, h, t)
         pooled = O.misa_pooled_for_query(K, wl.block, p)
         I = O.misa_importance(q_t, w_t, pooled)
@@ -96,6 +167,11 @@ def test_misa_full(dsa):
         errs += _check(mi[t], mv[t], rk, wl.top_k, q_t, w_t, K, f"misa q{t}", hs)
         f = O.rescore_row(q_t, w_t, K, cand[t], wl.top_k)
         errs += _check(di[t], dv[t], f, wl.top_k, q_t, w_t, K, f"dagger q{t}")
+        d = O.dense_row(q_t, w_t, K, p, wl.top_k)
+        errs += _check(dni[t], None, d, wl.top_k, q_t, w_t, K, f"dense q{t}")
+        return errs
+
+    errs = _rows_parallel(row, range(wl.nq))      # every query
     assert not errs, "\n".join(errs[:10])
 
 
@@ -132,15 +208,16 @@ def test_hisa_full_with_iou(dsa):
     assert not errs, "\n".join(errs[:10])
 
 
-def test_hisa_and_misa_hisa_full_sampled_rows(dsa):
+def test_hisa_and_misa_hisa_full_all_rows(dsa):
     """32 queries x 1048576 keys, 32 heads, B 128, m 64, k 2048, as timed: the
     pooling, HISA over all heads and MISA∘HISA with h = 8 (the three calls of
-    the hisa and misa_hisa workloads).  Rows 0, 13 and 31 against the oracle,
-    each stage conditional on the GPU's own upstream choice."""
+    the hisa and misa_hisa workloads).  Every query against the oracle, each
+    stage conditional on the GPU's own upstream choice; the IoU of both
+    variants against the oracle's dense top-k of every query."""
     wl = datagen.WORKLOADS[5]
     h_act = 8
     say("[full] HISA and MISA∘HISA 32 x 1048576")
-    dev, h = _device_inputs(wl)
+    dev, h = _device_inputs(wl, per_seq=_dense_topk_of_own_query(wl))
     args = (dev["q"], dev["w"], dev["k"], dev["q_pos"], dev["q_seq"])
     kp = dsa.indexer_mean_pool_keys(dev["k"], wl.block)
     r = dsa.hisa_block_filter_topk(*args, block=wl.block, m_blocks=wl.m_blocks, top_k=wl.top_k,
@@ -150,9 +227,16 @@ def test_hisa_and_misa_hisa_full_sampled_rows(dsa):
     torch.cuda.synchronize()
     hi, hv, blocks, bsc = (r[x].cpu().numpy() for x in ("idx", "score", "blocks", "block_score"))
     out = {x: v.cpu().numpy() for x, v in mh.items()}
-    errs = []
-    for t in (0, 13, 31):
-        say(f"[full] oracle row {t}")
+    assert not r["status"].cpu().numpy().any() and not out["status"].any()
+    # selection agreement with the dense 32-head indexer on every query, the
+    # dense top-k taken by the oracle (HISA review, section 3: above 99 % on
+    # the pages' models)
+    dense_ref = np.stack(h["per_seq"])
+    _iou_report(dsa, "HISA m=64 vs dense (32 x 1048576)", hi, dense_ref)
+    _iou_report(dsa, "MISA∘HISA h=8 m=64 vs dense (32 x 1048576)", out["idx"], dense_ref)
+
+    def row(t):
+        errs = []
         q_t, w_t, K, p = _host_row(wl, h, t)
         pooled = O.misa_pooled_for_query(K, wl.block, p)
         # HISA: blocks, then tokens inside the GPU's blocks
@@ -165,7 +249,7 @@ def test_hisa_and_misa_hisa_full_sampled_rows(dsa):
         I = O.misa_importance(q_t, w_t, pooled)
         Fi = np.abs(w_t) * (np.abs(q_t) @ np.abs(pooled).T).sum(axis=1)
         gi = out["importance"][t].astype(np.float64)
-        if (np.abs(gi - I) > RTOL * I + FLOOR * Fi).any():
+        if not scores_ok(gi, I, I, Fi).all():
             errs.append(f"misa-hisa importance q{t}")
         errs += check_selection(out["heads"][t], None, np.arange(wl.n_heads), I, I, h_act, Fi,
                                 what=f"misa-hisa heads q{t}")
@@ -178,6 +262,9 @@ def test_hisa_and_misa_hisa_full_sampled_rows(dsa):
                              blocks=out["blocks"][t])
         errs += _check(out["idx"][t], out["score"][t], r2, wl.top_k, q_t, w_t, K,
                        f"misa-hisa q{t}", hs)
+        return errs
+
+    errs = _rows_parallel(row, range(wl.nq))      # every query
     assert not errs, "\n".join(errs[:10])
 
 
@@ -223,7 +310,7 @@ def test_misa_prefill_full_sampled_rows(dsa):
         pooled = O.misa_pooled_for_query(K, B, t)
         I = O.misa_importance(q_t, w_t, pooled)
         Fi = np.abs(w_t) * (np.abs(q_t) @ np.abs(pooled).T).sum(axis=1)
-        bad = np.abs(gI[i] - I) > 2e-3 * I + 2.0 ** -17 * Fi
+        bad = ~scores_ok(gI[i], I, I, Fi)
         if bad.any():
             errs.append(f"importance row {t}: {np.nonzero(bad)[0][:4]}")
         errs += check_selection(gh[i], None, np.arange(wl.n_heads), I, I, h, Fi,

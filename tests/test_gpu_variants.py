@@ -12,7 +12,7 @@ import torch
 
 import datagen
 from oracle import indexer as O
-from oracle.check import FLOOR, RTOL, check_selection
+from oracle.check import check_selection, scores_ok
 
 from _helpers import say, upload
 
@@ -61,7 +61,7 @@ def _misa_case(dsa, wl, h, k, kprime, seed=0, pos=None, pooled=True, rows=None):
         Fi = np.abs(w_t) * (np.abs(q_t) @ np.abs(pooled_ref).T).sum(axis=1)
         # router importance and head choice
         gi = out["importance"][t].astype(np.float64)
-        bad = np.abs(gi - I) > RTOL * I + FLOOR * Fi
+        bad = ~scores_ok(gi, I, I, Fi)
         if bad.any():
             errs.append(f"importance q{t}: heads {np.nonzero(bad)[0][:4]} gpu {gi[bad][:4]} ref {I[bad][:4]}")
         errs += check_selection(out["heads"][t], None, np.arange(wl.n_heads), I, I, h, Fi,
@@ -202,7 +202,7 @@ def _hisa_case(dsa, wl, m, k, seed=0, pos=None, pooled=True, rows=None):
                                      block=wl.block, m_blocks=m, top_k=k, k_pooled=kp)
     torch.cuda.synchronize()
     out = {key: v.cpu().numpy() for key, v in res.items()}
-    errs = []
+    errs = [] if not out["status"].any() else [f"status {out['status'].tolist()[:16]}"]
     for t in (range(wl.nq) if rows is None else rows):
         q_t, w_t, K, p = _rows(inp, wl, t)
         pooled_ref = O.misa_pooled_for_query(K, wl.block, p)
@@ -251,6 +251,67 @@ def test_hisa_heads_dims_and_the_multi_launch_path(dsa):
     _hisa_case(dsa, wl, m=200, k=1000, seed=7)
 
 
+def test_hisa_wait_timeout_is_reported(dsa):
+    """The token pass's bounded wait, forced from the host to give up at its
+    first unsuccessful check (wait limit 0): every kernel still ends normally;
+    a query whose wait gave up reports status 1 and a row of padding only
+    (never a partial selection) while its kept blocks are still exact; every
+    other query's row is the exact selection.  The same workspace then serves
+    a call with the default limit, which completes every query."""
+    wl = datagen.small(5, nq=8, n_seq=8, l_max=65536, n_plant=48)
+    m, k = 16, 512
+    inp = datagen.make(wl, 0)
+    dev = upload(inp, wl)
+    kp = dsa.indexer_mean_pool_keys(dev["k"], wl.block)
+    nb = dsa.hisa_block_filter_topk_workspace_size(wl.nq, wl.n_heads, wl.head_dim, wl.n_seq,
+                                                   wl.l_max, wl.block, m, k, 1)
+    ws = torch.empty(nb + 256, dtype=torch.uint8, device="cuda")
+    ws = ws[(-ws.data_ptr()) % 256:][:nb]
+    args = (dev["q"], dev["w"], dev["k"], dev["q_pos"], dev["q_seq"])
+    say("[hisa] wait limit 0")
+    dsa.hisa_wait_limit(0)
+    try:
+        res0 = dsa.hisa_block_filter_topk(*args, block=wl.block, m_blocks=m, top_k=k, k_pooled=kp,
+                                          workspace=ws)
+        mh0 = dsa.misa_hisa_topk(*args, block=wl.block, n_active_heads=8, m_blocks=m, top_k=k,
+                                 k_pooled=kp)
+        torch.cuda.synchronize()
+    finally:
+        dsa.hisa_wait_limit(-1)
+    res1 = dsa.hisa_block_filter_topk(*args, block=wl.block, m_blocks=m, top_k=k, k_pooled=kp,
+                                      workspace=ws)
+    torch.cuda.synchronize()
+    o0 = {x: v.cpu().numpy() for x, v in res0.items()}
+    o1 = {x: v.cpu().numpy() for x, v in res1.items()}
+    mh = {x: v.cpu().numpy() for x, v in mh0.items()}
+    say(f"[hisa] timed-out queries: hisa {o0['status'].tolist()} misa-hisa {mh['status'].tolist()}")
+    assert set(o0["status"].tolist()) <= {0, 1} and set(mh["status"].tolist()) <= {0, 1}
+    # 64 token-pass workgroups per query, all but the selecting one check for
+    # the kept blocks before the selection can have been published
+    assert o0["status"].sum() > 0 and mh["status"].sum() > 0
+    assert not o1["status"].any()
+    errs = []
+    for t in range(wl.nq):
+        q_t, w_t, K, p = _rows(inp, wl, t)
+        pooled_ref = O.misa_pooled_for_query(K, wl.block, p)
+        bs, bA = O.hisa_block_scores(q_t, w_t, pooled_ref)
+        Fb = O.dot_magnitude(q_t, w_t, pooled_ref)
+        for o, tag in ((o0, "limited"), (o1, "default")):
+            errs += check_selection(o["blocks"][t], o["block_score"][t],
+                                    np.arange(pooled_ref.shape[0]), bs, bA, m, Fb,
+                                    what=f"{tag} blocks q{t}")
+            if o["status"][t]:
+                if (o["idx"][t] != -1).any() or not np.isneginf(o["score"][t]).all():
+                    errs.append(f"{tag} q{t}: timed out but the row is not all padding")
+                continue
+            r = O.hisa_row(q_t, w_t, K, p, wl.block, m, k, blocks=o["blocks"][t])
+            errs += _check(o["idx"][t], o["score"][t], r["cand"], r["s"], r["A"], k,
+                           q_t, w_t, K, f"{tag} hisa q{t}")
+        if mh["status"][t] and ((mh["idx"][t] != -1).any() or not np.isneginf(mh["score"][t]).all()):
+            errs.append(f"misa-hisa q{t}: timed out but the row is not all padding")
+    assert not errs, "\n".join(errs[:12])
+
+
 def _misa_hisa_case(dsa, wl, h, m, k, seed=0, pos=None, pooled=True, rows=None):
     inp = datagen.make(wl, seed)
     if pos is not None:
@@ -271,7 +332,7 @@ def _misa_hisa_case(dsa, wl, h, m, k, seed=0, pos=None, pooled=True, rows=None):
         I = O.misa_importance(q_t, w_t, pooled_ref)
         Fi = np.abs(w_t) * (np.abs(q_t) @ np.abs(pooled_ref).T).sum(axis=1)
         gi = out["importance"][t].astype(np.float64)
-        bad = np.abs(gi - I) > RTOL * I + FLOOR * Fi
+        bad = ~scores_ok(gi, I, I, Fi)
         if bad.any():
             errs.append(f"importance q{t}: heads {np.nonzero(bad)[0][:4]}")
         errs += check_selection(out["heads"][t], None, np.arange(wl.n_heads), I, I, h, Fi,

@@ -320,6 +320,37 @@ def test_hisa_all_blocks_or_unit_blocks_equals_dense():
             assert sorted(h1["idx"].tolist()) == sorted(d["idx"].tolist())
 
 
+def test_dot_magnitude_closed_form_and_loops():
+    """F[u] = sum_j |w_j| sum_i |q_ji| |k_ui| (the term size behind the float32
+    rounding bound of the matching rule): a hand-computed integer case, a loop
+    over random integers, F >= A >= |s|, and planted mistakes that must differ
+    (no |.| on q, on k or on w; a plain dot instead of the term-wise sum)."""
+    q = np.array([[1.0, -2.0], [3.0, 0.0]])
+    w = np.array([2.0, -1.0])
+    K = np.array([[1.0, 1.0], [-2.0, 4.0]])
+    # u=0: 2*(1*1 + 2*1) + 1*(3*1 + 0) = 9;  u=1: 2*(1*2 + 2*4) + 1*(3*2 + 0) = 26
+    assert O.dot_magnitude(q, w, K).tolist() == [9.0, 26.0]
+    rng = np.random.default_rng(21)
+    caught = [False] * 4
+    for _ in range(10):
+        qq, ww, KK = _int_inputs(rng, 3, 4, 12)
+        F = O.dot_magnitude(qq, ww, KK)
+        loop = [sum(abs(ww[j]) * sum(abs(qq[j, i]) * abs(KK[u, i]) for i in range(qq.shape[1]))
+                    for j in range(len(ww))) for u in range(len(KK))]
+        assert F.tolist() == loop
+        s, A = O.indexer_scores(qq, ww, KK)
+        assert np.all(F >= A) and np.all(A >= np.abs(s))
+        wrong = [np.abs(ww) @ np.abs(qq @ KK.T),               # |dot| instead of term-wise
+                 np.abs(ww) @ (qq @ np.abs(KK).T),              # q without |.|
+                 np.abs(ww) @ (np.abs(qq) @ KK.T),              # k without |.|
+                 ww @ (np.abs(qq) @ np.abs(KK).T)]              # w without |.|
+        for i, m in enumerate(wrong):
+            caught[i] |= not np.array_equal(m, F)
+    assert all(caught), caught
+    # a planted mistake differs on the hand case too
+    assert (np.abs(w) @ np.abs(q @ K.T)).tolist() != [9.0, 26.0]
+
+
 def test_iou_cases():
     assert O.iou(np.array([1, 2, 3]), np.array([3, 2, 1])) == 1.0
     assert O.iou(np.array([1, 2]), np.array([3, 4])) == 0.0
