@@ -187,8 +187,9 @@ int hisa_block_filter_topk(const void* q, const float* w, const void* k, const v
  * surviving blocks and the top_k.  Outputs as for hisa_block_filter_topk
  * (out_status included), plus out_heads [nq, h] (most important first) and
  * out_importance [nq, n_heads], each optional.
- * Only DSA_DTYPE_BF16; 1 <= h <= n_heads; 1 <= block; 1 <= m_blocks <= 1024
- * and m_blocks * block <= 8192 (DSA_EUNSUPPORTED otherwise); nq <= 65535.
+ * Only DSA_DTYPE_BF16; 1 <= h <= n_heads; 1 <= block; 1 <= m_blocks <= 1024,
+ * m_blocks * block <= 8192 and ceil(l_max / block) <= 131072
+ * (DSA_EUNSUPPORTED otherwise); nq <= 65535.
  */
 size_t misa_hisa_topk_workspace_size(int32_t nq, int32_t n_heads, int32_t head_dim,
                                      int32_t n_seq, int64_t l_max, int32_t block,

@@ -1014,8 +1014,9 @@ int misa_hisa_topk(const void* q, const float* w, const void* k, const void* k_p
   MisaHisaPlan p = plan_misa_hisa(nq, n_heads, head_dim, n_seq, l_max, block, m_blocks,
                                   k_pooled != nullptr);
   if (!p.h.ok)
-    return fail(DSA_EUNSUPPORTED, "MISA-HISA needs m_blocks <= %d, m_blocks * block <= %d and "
-                "nq <= 65535", dsa::kHisaMaxBlocks, dsa::kHisaRegKeys);
+    return fail(DSA_EUNSUPPORTED, "MISA-HISA needs m_blocks <= %d, m_blocks * block <= %d, "
+                "ceil(l_max / block) <= %d and nq <= 65535", dsa::kHisaMaxBlocks,
+                dsa::kHisaRegKeys, dsa::kHisaMaxGroups * dsa::kHisaMaxChunk);
   if ((st = check_ws(workspace, workspace_bytes, p.total))) return st;
   const uint16_t* pooled = nullptr;
   uint16_t* partial = nullptr;

@@ -459,10 +459,12 @@ DSA_DEVICE void hisa_route_heads(const HisaArgs& a, int t, float* buf, int buf_w
   }
   __syncthreads();
   if (tid < H) {
-    const float Ij = s_I[tid];
+    // (order-preserving keys of I: a total order even for NaN, so the ranks
+    // are a permutation and every routed slot gets a head)
+    const uint32_t Ij = score_to_key(s_I[tid]);
     int rank = 0;
     for (int i = 0; i < H; ++i) {
-      const float Ii = s_I[i];
+      const uint32_t Ii = score_to_key(s_I[i]);
       rank += (Ii > Ij) || (Ii == Ij && i < tid);
     }
     if (rank < a.h_use) {

@@ -453,10 +453,13 @@ __global__ __launch_bounds__(256) void k_route_heads(RouteHeadsArgs a) {
     I = fabsf(a.w[(size_t)t * a.n_heads + j]) * tot;
     if (a.out_importance) a.out_importance[(size_t)t * a.n_heads + j] = row_ok ? I : 0.f;
   }
+  // ranked on the order-preserving keys of I: a total order even for NaN, so
+  // the ranks are a permutation and every routed slot gets a head
+  const uint32_t kI = score_to_key(I);
   int rank = 0;
   for (int i = 0; i < a.n_heads; ++i) {
-    const float Ii = __shfl(I, i, 64);
-    rank += (Ii > I) || (Ii == I && i < j);
+    const uint32_t Ii = (uint32_t)__shfl((int)kI, i, 64);
+    rank += (Ii > kI) || (Ii == kI && i < j);
   }
   if (head_ok && rank < a.h_use) {
     a.heads[(size_t)t * a.heads_stride + rank] = row_ok ? j : 0;

@@ -131,11 +131,13 @@ DSA_DEVICE void route_heads(const SelArgs& a, int t, int32_t* s_heads, float* s_
     if (report && a.out_importance) a.out_importance[(size_t)t * H + j] = I;
   }
   __syncthreads();
+  // ranked on the order-preserving keys of I: a total order even for NaN,
+  // so the ranks are a permutation and every routed slot gets a head
   for (int j = threadIdx.x; j < H; j += blockDim.x) {
-    const float Ij = s_I[j];
+    const uint32_t Ij = score_to_key(s_I[j]);
     int rank = 0;
     for (int i = 0; i < H; ++i) {
-      const float Ii = s_I[i];
+      const uint32_t Ii = score_to_key(s_I[i]);
       rank += (Ii > Ij) || (Ii == Ij && i < j);
     }
     if (rank < a.h_use) {
