@@ -99,6 +99,29 @@ int indexer_score_topk(const void* q, const float* w, const void* k, int32_t dty
                        size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * The dense indexer call for callers that cannot allocate: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, semantics and kernels as indexer_score_topk, without the
+ * workspace: it uses instead a device array of DSA_NOALLOC_SCRATCH_BYTES that
+ * the library holds on each GPU it runs on (allocated when the library's code
+ * is loaded on that GPU, kept until the process ends).  It calls no hipMalloc,
+ * hipFree or other allocating routine; the first call on a device looks the
+ * array's address up (hipGetSymbolAddress) with that device current.
+ *  - A call whose indexer_score_topk_workspace_size exceeds
+ *    DSA_NOALLOC_SCRATCH_BYTES returns DSA_EUNSUPPORTED before any launch
+ *    (the dense decode workload, 64 queries x 131072 keys, needs 68,161,792).
+ *  - Every call on one GPU shares that GPU's array and clears what it needs at
+ *    its start: calls that overlap in time on one GPU (other streams, other
+ *    host threads) race and give undefined results; serialise them.
+ */
+#define DSA_NOALLOC_SCRATCH_BYTES (80u << 20)
+int indexer_score_topk_noalloc(const void* q, const float* w, const void* k, int32_t dtype,
+                               const int32_t* q_seq, const int32_t* q_pos, int32_t nq,
+                               int32_t n_heads, int32_t head_dim, int32_t n_seq, int64_t l_max,
+                               int32_t top_k, int32_t* out_idx, float* out_score,
+                               hipStream_t stream);
+
+/*
  * Mean-pooled block keys (MISA summary, "method" step 1: M = ceil(L/B) blocks
  * and mean-pooled indexing keys; HISA review, section 3: pooled representative
  * vector per block of size B).  Block b of sequence s covers tokens

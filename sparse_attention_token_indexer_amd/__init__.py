@@ -169,6 +169,27 @@ def indexer_score_topk(q: torch.Tensor, w: torch.Tensor, k: torch.Tensor, q_pos:
     return out_idx, out_score
 
 
+def indexer_score_topk_noalloc(q: torch.Tensor, w: torch.Tensor, k: torch.Tensor,
+                               q_pos: torch.Tensor, q_seq: Optional[torch.Tensor] = None,
+                               top_k: int = 2048, out_idx: Optional[torch.Tensor] = None,
+                               out_score: Optional[torch.Tensor] = None, with_scores: bool = True
+                               ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """The dense indexer on the library's own per-GPU scratch (no workspace;
+    the C call allocates nothing).  Pass out_idx / out_score to allocate
+    nothing here either.  Calls that overlap on one GPU race."""
+    dev, nq, H, d, n_seq, l_max = _common(q, w, k, q_pos, q_seq)
+    dt = _dtype_code(q)
+    out_idx, out_score = _outputs(dev, nq, top_k, out_idx, out_score, with_scores)
+    st = lib().indexer_score_topk_noalloc(_ptr(q), _ptr(w), _ptr(k), dt, _ptr(q_seq), _ptr(q_pos),
+                                          nq, H, d, n_seq, l_max, top_k, _ptr(out_idx),
+                                          _ptr(out_score), _stream(dev))
+    _check(st, "indexer_score_topk_noalloc")
+    return out_idx, out_score
+
+
+NOALLOC_SCRATCH_BYTES = 80 << 20
+
+
 def indexer_mean_pool_keys(k: torch.Tensor, block: int,
                            out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Mean-pooled bf16 block keys [n_seq, ceil(l_max/block), d]."""
@@ -410,7 +431,7 @@ def kernel_timing_read(kind: str) -> Dict[str, float]:
 __all__ = [
     "kernel_timing", "kernel_timing_read", "KERNEL_KINDS",
     "DsaError", "LIB_PATH", "lib", "DSA_DTYPE_BF16", "DSA_DTYPE_F32",
-    "indexer_score_topk", "indexer_score_topk_workspace_size",
+    "indexer_score_topk", "indexer_score_topk_workspace_size", "indexer_score_topk_noalloc",
     "indexer_mean_pool_keys",
     "misa_route_score_topk", "misa_route_score_topk_workspace_size",
     "hisa_block_filter_topk", "hisa_block_filter_topk_workspace_size",

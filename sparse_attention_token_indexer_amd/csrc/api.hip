@@ -257,6 +257,12 @@ DensePlan plan_dense(int64_t nq, int head_dim, int64_t l_max, int f32) {
   return p;
 }
 
+// workspace of the dense call (prefill-shaped or decode-shaped)
+size_t dense_workspace(int32_t nq, int32_t head_dim, int32_t n_seq, int64_t l_max, int32_t dtype) {
+  if (use_prefill(dtype, nq, n_seq, l_max)) return plan_prefill(nq, l_max).total;
+  return plan_dense(nq, head_dim, l_max, dtype == DSA_DTYPE_F32).total;
+}
+
 // ----------------------------------------------------------------- MISA ----
 
 struct MisaPlan {
@@ -727,17 +733,20 @@ size_t indexer_score_topk_workspace_size(int32_t nq, int32_t n_heads, int32_t he
                                          int32_t dtype) {
   (void)n_heads; (void)top_k;
   if (nq <= 0 || l_max <= 0) return 0;
-  if (use_prefill(dtype, nq, n_seq, l_max)) return plan_prefill(nq, l_max).total;
-  return plan_dense(nq, head_dim, l_max, dtype == DSA_DTYPE_F32).total;
+  return dense_workspace(nq, head_dim, n_seq, l_max, dtype);
 }
 
-int indexer_score_topk(const void* q, const float* w, const void* k, int32_t dtype,
-                       const int32_t* q_seq, const int32_t* q_pos, int32_t nq, int32_t n_heads,
-                       int32_t head_dim, int32_t n_seq, int64_t l_max, int32_t top_k,
-                       int32_t* out_idx, float* out_score, void* workspace,
-                       size_t workspace_bytes, hipStream_t stream) {
-  int st = check_common(q, w, k, dtype, q_pos, nq, n_heads, head_dim, n_seq, l_max, top_k, out_idx);
-  if (st || nq == 0) return st;
+}  // extern "C"
+
+namespace {
+
+// The dense call after argument validation: the prefill-shaped kernels, or
+// the decode-shaped pass (clear, score-and-emit, merge), over `workspace`.
+int dense_call(const void* q, const float* w, const void* k, int32_t dtype, const int32_t* q_seq,
+               const int32_t* q_pos, int32_t nq, int32_t n_heads, int32_t head_dim,
+               int32_t n_seq, int64_t l_max, int32_t top_k, int32_t* out_idx, float* out_score,
+               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st;
   const int f32 = dtype == DSA_DTYPE_F32;
   if (use_prefill(dtype, nq, n_seq, l_max)) {
     PrefillPlan pp = plan_prefill(nq, l_max);
@@ -781,6 +790,67 @@ int indexer_score_topk(const void* q, const float* w, const void* k, int32_t dty
   a.out_idx = out_idx;
   a.out_score = out_score;
   return hip_status(run_score_select(a, stream), "score/select kernel", stream);
+}
+
+// ---- the entry point that allocates nothing: its workspace is this
+// file-scope device array, one copy per GPU, held until the process ends.
+// Host code never uses the array's name as an address (on the host it is only
+// a stand-in symbol): the device address comes from hipGetSymbolAddress, once
+// per device with that device current, and is kept per device.
+static __device__ __align__(256) unsigned char scratch[DSA_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(DSA_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(DSA_EUNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(DSA_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return DSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int indexer_score_topk(const void* q, const float* w, const void* k, int32_t dtype,
+                       const int32_t* q_seq, const int32_t* q_pos, int32_t nq, int32_t n_heads,
+                       int32_t head_dim, int32_t n_seq, int64_t l_max, int32_t top_k,
+                       int32_t* out_idx, float* out_score, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  int st = check_common(q, w, k, dtype, q_pos, nq, n_heads, head_dim, n_seq, l_max, top_k, out_idx);
+  if (st || nq == 0) return st;
+  return dense_call(q, w, k, dtype, q_seq, q_pos, nq, n_heads, head_dim, n_seq, l_max, top_k,
+                    out_idx, out_score, workspace, workspace_bytes, stream);
+}
+
+int indexer_score_topk_noalloc(const void* q, const float* w, const void* k, int32_t dtype,
+                               const int32_t* q_seq, const int32_t* q_pos, int32_t nq,
+                               int32_t n_heads, int32_t head_dim, int32_t n_seq, int64_t l_max,
+                               int32_t top_k, int32_t* out_idx, float* out_score,
+                               hipStream_t stream) {
+  int st = check_common(q, w, k, dtype, q_pos, nq, n_heads, head_dim, n_seq, l_max, top_k, out_idx);
+  if (st || nq == 0) return st;
+  const size_t need = dense_workspace(nq, head_dim, n_seq, l_max, dtype);
+  if (need > (size_t)DSA_NOALLOC_SCRATCH_BYTES)
+    return fail(DSA_EUNSUPPORTED, "this call needs %zu bytes of scratch; the no-allocation entry "
+                "point holds %zu (use indexer_score_topk with a workspace)", need,
+                (size_t)DSA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if ((st = scratch_of_current_device(&ws))) return st;
+  return dense_call(q, w, k, dtype, q_seq, q_pos, nq, n_heads, head_dim, n_seq, l_max, top_k,
+                    out_idx, out_score, ws, (size_t)DSA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int indexer_mean_pool_keys(const void* k, int32_t dtype, int32_t n_seq, int64_t l_max,

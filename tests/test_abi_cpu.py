@@ -160,3 +160,17 @@ def test_hisa_wait_limit_hook(lib):
     assert lib.dsa_hisa_wait_limit(0) == 0
     assert lib.dsa_hisa_wait_limit(-1) == 0          # back to the default
     assert lib.dsa_abi_version() == 2
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch_before_any_device_work(lib):
+    """The no-allocation dense entry point checks the call's workspace need
+    against its fixed per-GPU scratch before it touches the device."""
+    aligned = 1 << 20
+    args = [aligned, aligned, aligned, 0, None, aligned, 64, 64, 128, 64, 1 << 21, 2048, aligned,
+            None, None]
+    assert lib.indexer_score_topk_noalloc(*args) == 2           # 64 x 2M keys: too large
+    assert b"scratch" in lib.dsa_last_error()
+    args[11] = 0
+    assert lib.indexer_score_topk_noalloc(*args) == 1           # top_k 0
+    assert dsa.indexer_score_topk_workspace_size(64, 64, 128, 64, 131072, 2048) <= \
+        dsa.NOALLOC_SCRATCH_BYTES                                 # the dense decode workload fits
