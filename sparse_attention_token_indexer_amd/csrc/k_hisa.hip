@@ -43,6 +43,7 @@
 namespace dsa {
 
 static_assert(kBins == kHisaBins, "histogram size shared with the host plan");
+static_assert(kHisaMaxBlocks <= 1024, "k_hisa_topk reads one kept block per thread");
 
 namespace {
 
@@ -52,19 +53,18 @@ constexpr int kPB = kBins / kHT;                // histogram bins per thread
 constexpr int kTT = 1024;                       // threads of the selection kernel
 // LDS histograms read by NT threads in runs of P = kBins / NT consecutive bins
 // are padded with one word after every P bins, so the runs start on distinct
-// banks; the padding word between bins P - 1 and P takes the counts of empty
-// slots.
+// banks.
 template <int NT>
 struct Hist {
   static constexpr int P = kBins / NT;
   static constexpr int kWords = kBins + kBins / P;
-  static constexpr int kSink = P;
   DSA_DEVICE static int at(int b) { return b + b / P; }
 };
 constexpr int kHistWords = Hist<kHT>::kWords;
 DSA_DEVICE int hpad(int b) { return Hist<kHT>::at(b); }
 constexpr int kSU = 8;                          // entries per thread per pass step
-constexpr int kHisaSegRead = 96;                // candidate slots read per segment up front
+static_assert(kSU * kTT >= kHisaRegKeys, "k_hisa_topk loads every token key in one batch");
+constexpr int kHisaSegRead = 128;               // candidate slots read per segment up front
 
 enum SyncWord {
   S_ARRIVE1 = 0,                  // block-pass workgroups done
@@ -282,22 +282,22 @@ DSA_DEVICE void select_exact(const Src& src, uint32_t top_k, const Emitter& em, 
 // `stage` (stage_cap pairs) when given, in one coalesced copy; entries in b*
 // are collected in the LDS list and resolved there (brute force up to 64,
 // else finish_bin), or by the radix finish over all entries when the bin
-// overflows the list.  Every pass is a plain loop over the entries, which
-// keeps the register needs (scalar ones in particular) small.
+// overflows the list.  Every pass is a plain loop
+// over the entries, which keeps the register needs (scalar ones in
+// particular) small.  With `hist_clear` the caller has already zeroed hist
+// (and synchronised).
 template <int NT>
 DSA_DEVICE void select_lds(const uint2* ent, int n, int top_k, int32_t* out_idx, float* out_score,
                            uint2* stage, uint32_t stage_cap, uint32_t* hist, uint32_t* scratch,
                            uint2* list, uint2* tie, uint32_t* s_out, uint32_t* s_ln, int* s_b,
-                           uint32_t* s_above, uint32_t* s_nb) {
+                           uint32_t* s_above, uint32_t* s_nb, bool hist_clear = false) {
   typedef Hist<NT> H;
   constexpr int PB = H::P;
   const int tid = (int)threadIdx.x, lane = lane_id();
-  for (int i = tid; i < H::kWords; i += NT) hist[i] = 0;
-  if (tid == 0) {
-    *s_out = 0;
-    *s_ln = 0;
+  if (!hist_clear) {
+    for (int i = tid; i < H::kWords; i += NT) hist[i] = 0;
+    __syncthreads();
   }
-  __syncthreads();
   // (every pass takes kSU entries per thread at a time, their reads in flight
   // together, in the same order each time)
   for (int base = 0; base < n; base += kSU * NT) {
@@ -308,8 +308,12 @@ DSA_DEVICE void select_lds(const uint2* ent, int n, int top_k, int32_t* out_idx,
       k[u] = i < n ? ent[i].x : 0u;
     }
 #pragma unroll
-    for (int u = 0; u < kSU; ++u)
-      atomicAdd(&hist[k[u] ? H::at((int)(k[u] >> kBinShift)) : H::kSink], 1u);
+    for (int u = 0; u < kSU; ++u)                          // (empty slots: key 0)
+      if (k[u]) atomicAdd(&hist[H::at((int)(k[u] >> kBinShift))], 1u);
+  }
+  if (tid == 0) {
+    *s_out = 0;
+    *s_ln = 0;
   }
   __syncthreads();
   const int b0 = kBins - PB * (tid + 1);                   // this thread's bins, from the top
@@ -617,6 +621,9 @@ __global__ __launch_bounds__(kHT) __attribute__((amdgpu_waves_per_eu(2))) void k
         const int f = tid + u * kHT, sg = f / S;
         if (sg < n1) v[u] = ld_dev(cbase + (size_t)sg * a.ch1 + (f - sg * S));
       }
+      // (the selection's histogram is cleared while the loads are in flight;
+      // the barrier of the scan below orders it before the first count)
+      for (int i = tid; i < kHistWords; i += kHT) hist[i] = 0;
       if (c > (uint32_t)a.ch1) c = (uint32_t)a.ch1;
       if (tid < n1) scnt[tid] = c;
       uint32_t tot;
@@ -638,7 +645,7 @@ __global__ __launch_bounds__(kHT) __attribute__((amdgpu_waves_per_eu(2))) void k
             cl[off[sg] + i] = ld_dev(cbase + (size_t)sg * a.ch1 + i);
         __syncthreads();
         select_lds<kHT>(cl, (int)tot, m1, sbid, sbsc, nullptr, 0u, hist, scratch, list, tie,
-                        &s_out, &s_ln, &s_b, &s_above, &s_nb);
+                        &s_out, &s_ln, &s_b, &s_above, &s_nb, true);
       } else {
         const Emitter em{sbid, sbsc, &s_out, (uint32_t)m1};     // into LDS, then out
         const DevSegSource src{cbase, off, n1, a.ch1};
@@ -700,14 +707,30 @@ __global__ __launch_bounds__(kTT) void k_hisa_topk(HisaArgs a) {
   __shared__ uint32_t s_out, s_ln, s_above, s_nb;
   __shared__ int s_b;
   const int t = blockIdx.x, tid = (int)threadIdx.x;
+  // Every load in one round: the token keys of up to m_blocks * block items
+  // (k_hisa stored the query's items2 <= m_blocks * block of them; slots past
+  // items2 lie inside the query's key array and are masked below), the kept
+  // blocks (m_blocks <= kTT: one per thread), the query's row and its timeout
+  // word.
+  const uint32_t* keys_t = a.keys2 + (size_t)t * (a.split ? a.groups2 : a.groups) * a.ch2;
+  const int32_t* blocks = a.blocks + (size_t)t * a.m_blocks;
+  const int items_max = a.m_blocks * a.block;
+  uint32_t k[kSU];
+#pragma unroll
+  for (int u = 0; u < kSU; ++u) {
+    const int i = tid + u * kTT;
+    k[u] = i < items_max ? keys_t[i] : 0u;
+  }
+  const int32_t my_block = tid < a.m_blocks ? blocks[tid] : 0;
   const int seq = a.q_seq ? a.q_seq[t] : 0;
   const int64_t pos = a.q_pos[t];
+  const uint32_t to_word = ld_dev(a.sync + (size_t)t * kHisaSyncWords + S_TIMEOUT);
   int32_t* out_i = a.out_idx + (size_t)t * a.top_k;
   float* out_s = a.out_score ? a.out_score + (size_t)t * a.top_k : nullptr;
   const bool valid = seq >= 0 && seq < a.n_seq && pos >= 0 && pos < a.l_max;
   // a token-pass workgroup of this query gave up its wait (k_hisa ended before
   // this kernel started, so the mark is final): its keys were never stored
-  const bool timed_out = valid && ld_dev(a.sync + (size_t)t * kHisaSyncWords + S_TIMEOUT) != 0u;
+  const bool timed_out = valid && to_word != 0u;
   if (a.out_status && tid == 0) a.out_status[t] = timed_out ? 1 : 0;
   if (!valid || timed_out) {                   // no keys, or incomplete: padding only
     for (int i = tid; i < a.top_k; i += kTT) {
@@ -719,40 +742,22 @@ __global__ __launch_bounds__(kTT) void k_hisa_topk(HisaArgs a) {
   const int M = (int)((pos + a.block) / a.block);
   const int m1 = a.m_blocks < M ? a.m_blocks : M;
   const int items2 = m1 * a.block;
-  const int32_t* blocks = a.blocks + (size_t)t * a.m_blocks;
-  // (key, token id) of every item into LDS: item i = tid + j * kTT is token
+  if (tid < m1) sbid[tid] = my_block;
+  __syncthreads();
+  // (key, token id) of every item into LDS: item i = tid + u * kTT is token
   // list[i / block] * block + i % block; list index and offset advance by kTT
-  // per step without a division.  The first batch of keys is read before the
-  // kept-block list, so the two reads overlap.
-  const uint32_t* keys_t = a.keys2 + (size_t)t * (a.split ? a.groups2 : a.groups) * a.ch2;
+  // per step without a division (kSU * kTT = kHisaRegKeys >= items2: one batch)
   const int blk = a.block, step = kTT / blk, rem = kTT % blk;
   int li = tid / blk, r = tid % blk;
-  uint32_t k[kSU];
 #pragma unroll
   for (int u = 0; u < kSU; ++u) {
     const int i = tid + u * kTT;
-    k[u] = i < items2 ? keys_t[i] : 0u;
-  }
-  for (int i = tid; i < m1; i += kTT) sbid[i] = blocks[i];
-  __syncthreads();
-  for (int base = 0; base < items2; base += kSU * kTT) {
-    if (base > 0) {
-#pragma unroll
-      for (int u = 0; u < kSU; ++u) {
-        const int i = base + tid + u * kTT;
-        k[u] = i < items2 ? keys_t[i] : 0u;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kSU; ++u) {
-      const int i = base + tid + u * kTT;
-      if (i < items2) ent[i] = make_uint2(k[u], (uint32_t)(sbid[li < m1 ? li : m1 - 1] * blk + r));
-      li += step;
-      r += rem;
-      if (r >= blk) {
-        r -= blk;
-        ++li;
-      }
+    if (i < items2) ent[i] = make_uint2(k[u], (uint32_t)(sbid[li < m1 ? li : m1 - 1] * blk + r));
+    li += step;
+    r += rem;
+    if (r >= blk) {
+      r -= blk;
+      ++li;
     }
   }
   __syncthreads();

@@ -535,24 +535,24 @@ hipError_t launch_hisa(const HisaArgs& a, hipStream_t) {
       touch_elems(a.keys2, (int64_t)t * g2 * a.ch2 + j0, (int64_t)t * g2 * a.ch2 + j0 + nc2, "token keys");
     }
   }
-  // k_hisa_topk
+  // k_hisa_topk: every query's first round of loads (token keys up to
+  // m_blocks * block, the m_blocks kept blocks, its row and timeout word)
+  // comes before the row is checked
   g_kernel = "k_hisa_topk";
+  const int64_t G2 = a.split ? a.groups2 : a.groups;
+  const int64_t items_max = (int64_t)a.m_blocks * a.block;
+  if (items_max > G2 * a.ch2) violation("%lld token keys per query, %lld slots", (long long)items_max, (long long)(G2 * a.ch2));
+  if (items_max > kHisaRegKeys) violation("%lld token keys > LDS entries", (long long)items_max);
   for (int t = 0; t < a.nq; ++t) {
     const QRow r = qrow(a.q_seq, a.q_pos, t, a.n_seq, a.l_max);
-    touch_elems(a.out_idx, (int64_t)t * a.top_k, (int64_t)(t + 1) * a.top_k, "out_idx");
-    if (a.out_score) touch_elems(a.out_score, (int64_t)t * a.top_k, (int64_t)(t + 1) * a.top_k, "out_score");
-    if (!r.ok) continue;
+    touch_elems(a.keys2, (int64_t)t * G2 * a.ch2, (int64_t)t * G2 * a.ch2 + items_max, "token keys");
+    touch_elems(a.blocks, (int64_t)t * a.m_blocks, (int64_t)(t + 1) * a.m_blocks, "kept blocks");
     touch_elems(a.sync, (int64_t)t * kHisaSyncWords + kHisaSyncTimeout,
                 (int64_t)t * kHisaSyncWords + kHisaSyncTimeout + 1, "timeout word");
     if (a.out_status) touch_elems(a.out_status, t, t + 1, "out_status");
-    const int64_t M = (r.pos + a.block) / a.block;
-    const int64_t m1 = std::min<int64_t>(a.m_blocks, M);
-    const int64_t items2 = m1 * a.block;
-    const int64_t G2 = a.split ? a.groups2 : a.groups;
-    if (items2 > G2 * a.ch2) violation("query %d: %lld token keys, %lld slots", t, (long long)items2, (long long)(G2 * a.ch2));
-    if (items2 > kHisaRegKeys) violation("query %d: %lld token keys > LDS entries", t, (long long)items2);
-    touch_elems(a.keys2, (int64_t)t * G2 * a.ch2, (int64_t)t * G2 * a.ch2 + items2, "token keys");
-    touch_elems(a.blocks, (int64_t)t * a.m_blocks, (int64_t)t * a.m_blocks + m1, "kept blocks");
+    touch_elems(a.out_idx, (int64_t)t * a.top_k, (int64_t)(t + 1) * a.top_k, "out_idx");
+    if (a.out_score) touch_elems(a.out_score, (int64_t)t * a.top_k, (int64_t)(t + 1) * a.top_k, "out_score");
+    (void)r;
   }
   return hipSuccess;
 }

@@ -41,14 +41,21 @@ def audit_lib():
     os.makedirs(OUT, exist_ok=True)
     asan = _asan_runtime()
     lib = os.path.join(OUT, "libdsa_audit.so")
-    cmd = [_hipcc(), "-x", "hip", "--cuda-host-only", "-std=c++17", "-O1", "-g", "-fPIC",
-           "-shared", "-fno-omit-frame-pointer"]
-    if asan:
-        cmd += ["-Xarch_host", "-fsanitize=address"]
-    cmd += [os.path.join(CSRC, "api.hip"), os.path.join(ROOT, "tests", "audit", "kernel_model.cpp"),
-            "-o", lib]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    assert r.returncode == 0, r.stdout + r.stderr
+    san = ["-Xarch_host", "-fsanitize=address"] if asan else []
+    common = ["-std=c++17", "-O1", "-g", "-fPIC", "-fno-omit-frame-pointer", *san]
+    api_o = os.path.join(OUT, "api.o")
+    model_o = os.path.join(OUT, "kernel_model.o")
+    # api.hip with its device part (it defines the no-allocation entry point's
+    # device array), the model for the host only (it replaces the kernels)
+    steps = [
+        [_hipcc(), "--offload-arch=gfx950", *common, "-c", os.path.join(CSRC, "api.hip"), "-o", api_o],
+        [_hipcc(), "-x", "hip", "--cuda-host-only", *common, "-c",
+         os.path.join(ROOT, "tests", "audit", "kernel_model.cpp"), "-o", model_o],
+        [_hipcc(), "--offload-arch=gfx950", "-shared", *san, api_o, model_o, "-o", lib],
+    ]
+    for cmd in steps:
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        assert r.returncode == 0, " ".join(cmd) + "\n" + r.stdout + r.stderr
     return lib, asan
 
 
