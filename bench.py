@@ -41,6 +41,7 @@ CSRC = os.path.join(ROOT, "sparse_attention_token_indexer_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 WORKLOADS = {"dense_decode": 2, "tiny": 1, "dense_prefill": 3, "misa": 4, "misa_dagger": 4,
+             "dense_shared_decode": 2,
              "hisa": 5, "pool": 4, "misa_prefill": 3, "hisa_prefill": 3, "misa_hisa": 5,
              "sparse_mla": None}
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
@@ -54,6 +55,7 @@ DENSE_IOU_MAX_L = 131072
 KERNEL_SOURCE = {"dense_decode": "k_score_select.hip", "tiny": "k_score_select.hip",
                  "misa": "k_score_select.hip", "misa_dagger": "k_score_select.hip",
                  "hisa": "k_hisa.hip", "dense_prefill": "k_prefill.hip",
+                 "dense_shared_decode": "k_prefill.hip",
                  "misa_prefill": "k_prefill_routed.hip", "pool": "k_pool.hip",
                  "hisa_prefill": "k_hisa.hip", "misa_hisa": "k_hisa.hip",
                  "sparse_mla": "k_mla.hip"}
@@ -287,6 +289,11 @@ def main() -> int:
         extra["attention"] = {"d_qk": d, "d_v": wl.d_v, "softmax_scale": wl.scale}
     else:
         wl = datagen.WORKLOADS[WORKLOADS[name]]
+        if name == "dense_shared_decode":
+            # the dense decode workload's 64 queries on ONE shared 131072-key
+            # cache (its last 64 positions): the shared-cache reading of a
+            # decode batch, served by the query-grouped kernels
+            wl = wl.replace(n_seq=1, layout="tail", name="dense_shared_decode_L128K_H64")
         if args.l_max is not None:
             if name != "hisa" or args.l_max < wl.m_blocks * wl.block:
                 print("--l-max applies to the hisa workload, at least m * B = "
@@ -306,6 +313,20 @@ def main() -> int:
 
     if name == "sparse_mla":
         pass
+    elif name == "dense_shared_decode":
+        nbytes = dsa.indexer_score_topk_workspace_size(nq, H, d, wl.n_seq, L, topk, 0)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+
+        def step():
+            dsa.indexer_score_topk(q, w, k, q_pos, q_seq, top_k=topk, out_idx=out_i,
+                                   out_score=out_s, workspace=ws)
+        kind = "prefill"
+        kernel_bytes = None
+        kernel_flops = pairs * H * d * 2
+        call_bytes = nq * H * d * eb + L * d * eb + nq * H * 4 + nq * topk * 8
+        call_flops = kernel_flops
+        bound_note = ("MFMA: the head contraction of every causal (query, key) pair; the shared "
+                      "cache is staged once per 8-query group")
     elif name == "dense_prefill":
         nbytes = dsa.indexer_score_topk_workspace_size(nq, H, d, wl.n_seq, L, topk, 0)
         ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
@@ -548,6 +569,25 @@ def main() -> int:
                                       "dense_over_hisa": dense_med / call_med_ms}
     if name in ("hisa", "misa_hisa", "hisa_prefill"):
         extra["timed_out_queries"] = int(status.sum())       # of the last call (0: complete)
+    if name == "dense_shared_decode":
+        # the same queries one short of the query-grouped path's 64: the
+        # per-query decode kernels, which stream the shared cache per query
+        dws = torch.empty(dsa.indexer_score_topk_workspace_size(nq - 1, H, d, 1, L, topk, 0),
+                          dtype=torch.uint8, device=dev)
+        qd, wd, pd = q[:-1].contiguous(), w[:-1].contiguous(), q_pos[:-1].contiguous()
+        sd = q_seq[:-1].contiguous()
+        for _ in range(args.warmup):
+            dsa.indexer_score_topk(qd, wd, k, pd, sd, top_k=topk, with_scores=False, workspace=dws)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            dsa.indexer_score_topk(qd, wd, k, pd, sd, top_k=topk, with_scores=False, workspace=dws)
+        e1.record()
+        torch.cuda.synchronize()
+        extra["decode_kernels_63_queries_us"] = e0.elapsed_time(e1) / args.steps * 1e3
+        del dws
     if name in ("misa", "misa_dagger", "hisa", "misa_hisa") and L <= DENSE_IOU_MAX_L:
         # selection agreement of the last call's output with the dense indexer
         # on the same inputs (the IoU the MISA and HISA pages report)

@@ -219,10 +219,24 @@ int check_ws(void* ws, size_t have, size_t need) {
 
 // ---------------------------------------------------------------- dense ----
 
-// Prefill-shaped calls (many queries on one sequence) run the query-grouped
-// kernels; the per-row LDS histograms hold 16-bit counts, hence the l_max limit.
+// Prefill-shaped calls (many queries on one sequence: a prefill, a chunk of
+// one, or decode queries sharing one cache) run the query-grouped kernels.
+// Rows of up to 65535 keys count their scores in 12-bit bins of 16-bit
+// counters, longer rows in 11-bit bins of 32-bit counters.
 bool use_prefill(int32_t dtype, int64_t nq, int n_seq, int64_t l_max) {
-  return dtype == DSA_DTYPE_BF16 && n_seq == 1 && nq >= 64 && l_max <= 65535;
+  return dtype == DSA_DTYPE_BF16 && n_seq == 1 && nq >= 64 && l_max < ((int64_t)1 << 30);
+}
+int prefill_bin_bits(int64_t l_max) { return l_max <= 65535 ? 12 : 11; }
+
+// Keys per workgroup when the row groups (8 rows each) are too few to fill the
+// chip: enough chunks for about 512 workgroups (two share a compute unit when
+// the scorer keeps no histograms), each at least 1024 keys; 0 = no split.
+int prefill_key_chunk(int64_t nq, int64_t l_max) {
+  const int64_t groups = (nq + 7) / 8;
+  if (groups >= 256) return 0;
+  int64_t chunks = std::min<int64_t>((512 + groups - 1) / groups, (l_max + 1023) / 1024);
+  if (chunks <= 1) return 0;
+  return (int)((((l_max + chunks - 1) / chunks) + 127) / 128 * 128);
 }
 
 struct PrefillPlan {
@@ -553,8 +567,11 @@ void fill_common(dsa::SelArgs& a, const void* q, const float* w, const void* k,
 
 // MISA on the prefill shape (one sequence, many bf16 rows, h <= 8, k' = 0): the
 // router, the head selection, the packed routed scoring and the row select.
+// (the routed scorer's per-row histograms have 16-bit counters: rows of up to
+// 65535 keys)
 bool use_misa_prefill(int32_t dtype, int64_t nq, int n_seq, int64_t l_max, int h, int k_prime) {
-  return use_prefill(dtype, nq, n_seq, l_max) && k_prime == 0 && h <= dsa::kRoutedMaxHeads;
+  return use_prefill(dtype, nq, n_seq, l_max) && l_max <= 65535 && k_prime == 0 &&
+         h <= dsa::kRoutedMaxHeads;
 }
 
 struct MisaPrefillPlan {
@@ -766,7 +783,8 @@ int dense_call(const void* q, const float* w, const void* k, int32_t dtype, cons
     pa.scores = at<float>(workspace, pp.scores);
     pa.spare_row = pa.scores + (size_t)nq * pa.row_stride;
     pa.rowmeta = at<int32_t>(workspace, pp.rowmeta);
-    pa.bin_bits = 12;                      // first-level bins of the dense rows
+    pa.key_chunk = prefill_key_chunk(nq, l_max);
+    pa.bin_bits = pa.key_chunk ? 12 : prefill_bin_bits(l_max);   // first-level bins of the rows
     pa.out_idx = out_idx;
     pa.out_score = out_score;
     st = hip_status(timed(DSA_KERNEL_PREFILL, stream,

@@ -110,7 +110,11 @@ struct PrefillArgs {
   int64_t row_stride;          // floats per score row (l_max rounded up to 128)
   float* scores;               // [nq, row_stride] workspace (only u <= pos written)
   int32_t* rowmeta;            // [nq, 4] workspace: threshold bin, count above, count in bin
-  int bin_bits;                // first-level histogram bits (12 dense, 10 routed)
+  int bin_bits;                // first-level histogram bits (dense: 12 up to 65535 keys per
+                               // row, 11 beyond; routed: 10)
+  int key_chunk;               // dense only: > 0 splits every row's keys into chunks of this
+                               // many (a multiple of 128), one workgroup per (row group, chunk),
+                               // and the select kernel counts the rows itself (12-bit bins)
   const int32_t* heads;        // routed pass: [nq, heads_stride] head ids (first h_use used)
   int heads_stride, h_use;
   float* spare_row;            // [row_stride] scratch row taking the stores of rows that are

@@ -10,9 +10,16 @@
 // v_mfma_f32_32x32x16_bf16 with heads as rows and keys as columns, then the
 // fused ReLU-weighted head reduction in registers.  Two 32-key sub-tiles are
 // finished together (one lane-half exchange gives 64 consecutive keys' scores
-// across the wave).  Scores go to a workspace row and into a per-row 12-bit
+// across the wave).  Scores go to a workspace row and into a per-row
 // histogram in LDS; at the end each wave finds the bin that holds its row's
-// k-th score.  Workgroups run longest rows first.
+// k-th score.  Workgroups run longest rows first.  The histogram has 12-bit
+// bins with 16-bit counters while a row holds at most 65535 keys, and 11-bit
+// bins with 32-bit counters beyond (the same 8 KB of LDS per row).
+// When there are too few row groups to fill the chip (decode queries sharing
+// one cache, a short chunk of a long prefill), the keys are split as well:
+// workgroup (g, c) scores its rows over key chunk c only, keeps no histogram
+// (two workgroups then share a compute unit) and the select kernel finds each
+// row's threshold itself with one more pass over the stored row.
 // k_prefill_select: one workgroup per row emits every score above that bin and
 // resolves the bin itself exactly (radix digits over (score, ~index)).
 #include "dsa_internal.h"
@@ -35,12 +42,12 @@ constexpr uint32_t kSelListCap = 2048;   // tie-bin entries kept in LDS (global 
 // waves per SIMD) and the stages plus 8 KB histograms per row within 160 KB.
 constexpr int kRows = 8;
 
-template <int D, int ROWS>
+template <int D, int ROWS, bool SPLIT = false>
 constexpr size_t prefill_lds_bytes() {
-  return 2 * (size_t)kStageKeys * (D * 2 + 16) + (size_t)ROWS * (kPBins / 2) * 4;
+  return 2 * (size_t)kStageKeys * (D * 2 + 16) + (SPLIT ? 0 : (size_t)ROWS * (kPBins / 2) * 4);
 }
 
-template <int HT, int D, int ROWS>
+template <int HT, int D, int ROWS, bool W32, bool SPLIT>
 __global__ __launch_bounds__(64 * ROWS) void k_prefill_score(PrefillArgs a) {
   constexpr int kPT = 64 * ROWS;
   constexpr int S = D / 16;                    // k-steps
@@ -65,14 +72,20 @@ __global__ __launch_bounds__(64 * ROWS) void k_prefill_score(PrefillArgs a) {
     const int p = a.q_pos[t];
     if (seq == 0 && p >= 0 && (int64_t)p < a.l_max) pos = p;
   }
-  for (int i = threadIdx.x; i < ROWS * (kPBins / 2); i += kPT) hist[i] = 0u;
+  if constexpr (!SPLIT)
+    for (int i = threadIdx.x; i < ROWS * (kPBins / 2); i += kPT) hist[i] = 0u;
   if (threadIdx.x == 0) s_maxpos = -1;
   __syncthreads();
   if (lane == 0) atomicMax(&s_maxpos, pos);
   __syncthreads();
   const int maxpos = s_maxpos;
   if (maxpos < 0) return;                      // the select kernel pads these rows
-  const int n_stages = maxpos / kStageKeys + 1;
+  // keys [kb, ke) of this workgroup: the whole prefix of its rows, or with
+  // SPLIT one chunk of it (whole stages; key_chunk is a multiple of 128)
+  const int kb = SPLIT ? (int)blockIdx.y * a.key_chunk : 0;
+  if (kb > maxpos) return;
+  const int ke_last = SPLIT ? min(kb + a.key_chunk - 1, maxpos) : maxpos;   // last key scored
+  const int n_stages = (ke_last - kb) / kStageKeys + 1;
 
   // this wave's query row in registers (zeros for an invalid row).  Head
   // weights: accumulator register r of head tile ht holds head
@@ -113,7 +126,7 @@ __global__ __launch_bounds__(64 * ROWS) void k_prefill_score(PrefillArgs a) {
   // key and land in a buffer nobody reads.)
   auto fetch_piece = [&](int j, int st) {
     const int p = threadIdx.x + j * kPT;
-    const int key = min(st * kStageKeys + p / NC, maxpos);   // inside the cache
+    const int key = min(kb + st * kStageKeys + p / NC, ke_last);   // inside the cache
     pre[j] = *reinterpret_cast<const u32x4*>(kbase + (size_t)key * RB + (p % NC) * 16);
   };
   auto stash_piece = [&](int j, int buf) {
@@ -147,13 +160,20 @@ __global__ __launch_bounds__(64 * ROWS) void k_prefill_score(PrefillArgs a) {
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(pa), __float_as_uint(pb),
                                                      false, false);
     fin_sc = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    *reinterpret_cast<float*>(srow + (uint32_t)(key0 + lane) * 4u) = fin_sc;
+    *reinterpret_cast<float*>(srow + (uint32_t)(kb + key0 + lane) * 4u) = fin_sc;
   };
   auto fin_count = [&](int key0) {
-    const uint32_t word = (fast_key(fin_sc) >> kPBinShift) & (kPBins / 2 - 1);
-    const uint32_t inc =
-        key0 + lane <= pos_u ? ((int32_t)__float_as_uint(fin_sc) < 0 ? 1u : 0x10000u) : 0u;
-    atomicAdd(hrow + word, inc);
+    if constexpr (SPLIT) {                     // (the select kernel counts the row)
+      (void)key0;
+    } else if constexpr (W32) {                // 11-bit bin b in word b, 32-bit counts
+      const uint32_t word = fast_key(fin_sc) >> (kPBinShift + 1);
+      atomicAdd(hrow + word, key0 + lane <= pos_u ? 1u : 0u);
+    } else {
+      const uint32_t word = (fast_key(fin_sc) >> kPBinShift) & (kPBins / 2 - 1);
+      const uint32_t inc =
+          key0 + lane <= pos_u ? ((int32_t)__float_as_uint(fin_sc) < 0 ? 1u : 0x10000u) : 0u;
+      atomicAdd(hrow + word, inc);
+    }
   };
 
   // Software pipeline over 32-key sub-tiles c = 0..3 of each 128-key stage
@@ -238,20 +258,23 @@ __global__ __launch_bounds__(64 * ROWS) void k_prefill_score(PrefillArgs a) {
     fin_count(k_last);
   }
 
-  // this row's threshold: the 12-bit bin holding its k-th score
-  if (pos < 0) return;
+  // this row's threshold: the bin (12-bit, or 11-bit with W32) holding its
+  // k-th score
+  if (SPLIT || pos < 0) return;
   int32_t* meta = a.rowmeta + (size_t)t * 4;
   if (pos + 1 <= a.top_k) {                    // short row: every key is selected
     if (lane == 0) { meta[0] = -1; meta[1] = 0; meta[2] = 0; }
     return;
   }
-  // lane l owns bins [kPBins - PER (l + 1), kPBins - PER l), counted from the top
-  constexpr int PER = kPBins / 64;
-  const int b_hi = kPBins - PER * lane;         // exclusive
-  const int sh = 16 * ((b_hi - 1) / (kPBins / 2));   // all in one half of the words
+  // lane l owns bins [NB - PER (l + 1), NB - PER l), counted from the top
+  constexpr int NB = W32 ? kPBins / 2 : kPBins;
+  constexpr int PER = NB / 64;
+  const int b_hi = NB - PER * lane;             // exclusive
+  const int sh = W32 ? 0 : 16 * ((b_hi - 1) / (kPBins / 2));   // all in one half of the words
+  const uint32_t cmask = W32 ? 0xFFFFFFFFu : 0xFFFFu;
   const int w0 = (b_hi - PER) & (kPBins / 2 - 1);
   uint32_t mine = 0;
-  for (int i = 0; i < PER; ++i) mine += (hrow[w0 + i] >> sh) & 0xFFFFu;
+  for (int i = 0; i < PER; ++i) mine += (hrow[w0 + i] >> sh) & cmask;
   uint32_t incl = mine;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -262,7 +285,7 @@ __global__ __launch_bounds__(64 * ROWS) void k_prefill_score(PrefillArgs a) {
   if (before < need && incl >= need) {
     uint32_t accum = before;
     for (int b = b_hi - 1; b >= b_hi - PER; --b) {
-      const uint32_t c = (hrow[b & (kPBins / 2 - 1)] >> sh) & 0xFFFFu;
+      const uint32_t c = (hrow[b & (kPBins / 2 - 1)] >> sh) & cmask;
       if (accum + c >= need) {
         meta[0] = b;
         meta[1] = (int32_t)accum;
@@ -284,14 +307,19 @@ struct RowSource {
   }
 };
 
-template <int FB>   // first-level bins of the rows' histograms (rowmeta)
-__global__ __launch_bounds__(kST) void k_prefill_select(PrefillArgs a) {
+// FB: first-level bins of the rows' histograms (rowmeta); SELF: the scoring
+// kernel kept no histogram (keys split across workgroups), this kernel counts
+// each row's scores in 12-bit bins itself first.
+template <int FB, bool SELF, int NT>
+__global__ __launch_bounds__(NT) void k_prefill_select(PrefillArgs a) {
+  static_assert(!SELF || FB == 12, "rows counted here use 12-bit bins");
   constexpr int kFBShift = 32 - FB;
   extern __shared__ __align__(16) uint8_t smem[];
   uint2* list = reinterpret_cast<uint2*>(smem);                          // [kSelListCap]
   uint2* tie = list + kSelListCap;                                        // [64]
   uint32_t* hist = reinterpret_cast<uint32_t*>(tie + 64);                 // [1024]
   uint32_t* scratch = hist + 1024;                                        // [64]
+  uint32_t* hist1 = scratch + 64;                                         // [4096] (SELF)
   __shared__ uint32_t s_out, s_ln;
   const int t = (int)gridDim.x - 1 - (int)blockIdx.x;          // longest rows first
   int pos = -1;
@@ -304,26 +332,62 @@ __global__ __launch_bounds__(kST) void k_prefill_select(PrefillArgs a) {
   float* out_s = a.out_score ? a.out_score + (size_t)t * a.top_k : nullptr;
   const uint32_t n = (uint32_t)(pos + 1);
   const uint32_t Kt = pos < 0 ? 0u : (n < (uint32_t)a.top_k ? n : (uint32_t)a.top_k);
-  for (int i = Kt + threadIdx.x; i < a.top_k; i += kST) {
+  for (int i = Kt + threadIdx.x; i < a.top_k; i += NT) {
     out_i[i] = -1;
     if (out_s) out_s[i] = -__builtin_inff();
   }
   if (Kt == 0) return;
   const float* sc = a.scores + (size_t)t * (size_t)a.row_stride;
   if (n <= (uint32_t)a.top_k) {                // every key of a short row
-    for (uint32_t u = threadIdx.x; u < n; u += kST) {
+    for (uint32_t u = threadIdx.x; u < n; u += NT) {
       out_i[u] = (int32_t)u;
       if (out_s) out_s[u] = key_to_score(score_to_key(sc[u]));
     }
     return;
   }
-  const int32_t* meta = a.rowmeta + (size_t)t * 4;
-  const int bstar = meta[0];
-  const uint32_t above = (uint32_t)meta[1], nb = (uint32_t)meta[2];
+  // (few long rows when SELF: more loads in flight per thread)
+  constexpr int U = SELF ? 8 : 4;
+  const uint32_t n4 = (n + 3) / 4;
+  auto load_iter = [&](uint32_t base, auto& v) {
+    constexpr int UU = sizeof(v) / sizeof(v[0]);
+#pragma unroll
+    for (int j = 0; j < UU; ++j) {
+      const uint32_t i4 = base + threadIdx.x + j * NT;
+      v[j] = *reinterpret_cast<const f32x4*>(sc + 4 * (size_t)(i4 < n4 ? i4 : n4 - 1));
+    }
+    __builtin_amdgcn_sched_barrier(0);             // issue every load first
+  };
+  int bstar;
+  uint32_t above, nb;
+  if constexpr (SELF) {
+    // the row's 12-bit histogram from its stored scores, then the k-th bin
+    constexpr int UH = 16;
+    for (int i = threadIdx.x; i < (1 << FB); i += NT) hist1[i] = 0u;
+    __syncthreads();
+    for (uint32_t base = 0; base < n4; base += NT * UH) {
+      f32x4 v[UH];
+      load_iter(base, v);
+#pragma unroll
+      for (int j = 0; j < UH; ++j) {
+        const uint32_t i4 = base + threadIdx.x + j * NT;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (i4 < n4 && 4 * i4 + e < n) atomicAdd(&hist1[fast_key(v[j][e]) >> kFBShift], 1u);
+      }
+    }
+    __syncthreads();
+    bstar = block_find_threshold<NT>(hist1, 1 << FB, Kt, scratch, &above);
+    nb = hist1[bstar];
+  } else {
+    const int32_t* meta = a.rowmeta + (size_t)t * 4;
+    bstar = meta[0];
+    above = (uint32_t)meta[1];
+    nb = (uint32_t)meta[2];
+  }
   const bool fits = nb <= kSelListCap;
   if (threadIdx.x == 0) { s_out = 0; s_ln = 0; }
   if (!fits)                                    // second-digit histogram of the bin
-    for (int i = threadIdx.x; i < 1024; i += kST) hist[i] = 0;
+    for (int i = threadIdx.x; i < 1024; i += NT) hist[i] = 0;
   __syncthreads();
   const Emitter em{out_i, out_s, &s_out, Kt};
   constexpr int kSub = kFBShift - 10;          // the 10 key bits below the first level
@@ -335,16 +399,6 @@ __global__ __launch_bounds__(kST) void k_prefill_select(PrefillArgs a) {
   // its 4U scores of an iteration in two masks (emitted now / kept in the LDS
   // list); one wave scan of the packed counts and one LDS atomic per wave
   // reserve consecutive slots, and each lane writes its flagged scores there.
-  constexpr int U = 4;
-  const uint32_t n4 = (n + 3) / 4;
-  auto load_iter = [&](uint32_t base, f32x4 (&v)[U]) {
-#pragma unroll
-    for (int j = 0; j < U; ++j) {
-      const uint32_t i4 = base + threadIdx.x + j * kST;
-      v[j] = *reinterpret_cast<const f32x4*>(sc + 4 * (size_t)(i4 < n4 ? i4 : n4 - 1));
-    }
-    __builtin_amdgcn_sched_barrier(0);             // issue every load first
-  };
   auto append = [&](uint32_t base, const f32x4 (&v)[U], uint32_t take_m, uint32_t keep_m,
                     uint32_t kcap) {
     const uint32_t packed = (uint32_t)__builtin_popcount(take_m) |
@@ -362,7 +416,7 @@ __global__ __launch_bounds__(kST) void k_prefill_select(PrefillArgs a) {
     uint32_t l = __builtin_amdgcn_readlane(bk, 63) + (excl >> 16);
 #pragma unroll
     for (int j = 0; j < U; ++j) {
-      const uint32_t u0 = 4 * (base + threadIdx.x + j * kST);
+      const uint32_t u0 = 4 * (base + threadIdx.x + j * NT);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int bit = 4 * j + e;
@@ -383,7 +437,7 @@ __global__ __launch_bounds__(kST) void k_prefill_select(PrefillArgs a) {
   // first pass: emit every score above the bin, collect the bin (or, when it
   // overflows the list, count its next 10-bit digit).  Iterations wholly
   // inside the row skip the end-of-row masks; the path is fixed per row.
-  const uint32_t n_whole = n / (4 * kST * U) * (kST * U);   // in 16-byte pieces
+  const uint32_t n_whole = n / (4 * NT * U) * (NT * U);   // in 16-byte pieces
   auto pass1_iter = [&](uint32_t base, auto MASKED, auto FITS) {
     constexpr bool kMasked = decltype(MASKED)::value, kFits = decltype(FITS)::value;
     f32x4 v[U];
@@ -393,7 +447,7 @@ __global__ __launch_bounds__(kST) void k_prefill_select(PrefillArgs a) {
     for (int j = 0; j < U; ++j) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint32_t u = 4 * (base + threadIdx.x + j * kST) + e;
+        const uint32_t u = 4 * (base + threadIdx.x + j * NT) + e;
         const bool ok = !kMasked || u < n;
         const uint32_t key = fast_key(v[j][e]);
         const int b = (int)(key >> kFBShift);
@@ -406,8 +460,8 @@ __global__ __launch_bounds__(kST) void k_prefill_select(PrefillArgs a) {
   };
   auto pass1 = [&](auto FITS) {
     uint32_t base = 0;
-    for (; base < n_whole; base += kST * U) pass1_iter(base, std::false_type{}, FITS);
-    for (; base < n4; base += kST * U) pass1_iter(base, std::true_type{}, FITS);
+    for (; base < n_whole; base += NT * U) pass1_iter(base, std::false_type{}, FITS);
+    for (; base < n4; base += NT * U) pass1_iter(base, std::true_type{}, FITS);
   };
   if (fits) pass1(std::true_type{});
   else pass1(std::false_type{});
@@ -415,26 +469,26 @@ __global__ __launch_bounds__(kST) void k_prefill_select(PrefillArgs a) {
   const uint32_t need = Kt - above;
   if (fits) {
     const uint32_t nl = s_ln < nb ? s_ln : nb;
-    finish_bin<kST, FB>(list, nl, need, bstar, em, hist, scratch, tie);
+    finish_bin<NT, FB>(list, nl, need, bstar, em, hist, scratch, tie);
     return;
   }
   // The bin overflowed the list: its second-digit histogram (counted in the
   // first pass) gives the sub-bin d2 of the k-th entry; one more pass over the
   // row emits the bin's entries above d2 and collects d2 itself.
   uint32_t above2;
-  const int d2 = block_find_threshold<kST>(hist, 1024, need, scratch, &above2);
+  const int d2 = block_find_threshold<NT>(hist, 1024, need, scratch, &above2);
   const uint32_t nd2 = hist[d2];
   const uint32_t need2 = need - above2;
   if (threadIdx.x == 0) s_ln = 0;
   __syncthreads();
   const bool fits2 = nd2 <= kSelListCap;
-  for (uint32_t base = 0; base < n4; base += kST * U) {
+  for (uint32_t base = 0; base < n4; base += NT * U) {
     f32x4 v[U];
     load_iter(base, v);
     uint32_t take_m = 0, keep_m = 0;
 #pragma unroll
     for (int j = 0; j < U; ++j) {
-      const uint32_t i4 = base + threadIdx.x + j * kST;
+      const uint32_t i4 = base + threadIdx.x + j * NT;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t u = 4 * i4 + e;
@@ -454,25 +508,33 @@ __global__ __launch_bounds__(kST) void k_prefill_select(PrefillArgs a) {
   if (fits2) {
     const uint32_t nl = s_ln < nd2 ? s_ln : nd2;
     PairSource src{list, nl};
-    radix_finish<kST>(src, prefix, mask, 64 - FB - 10, need2, nl, em, hist, scratch);
+    radix_finish<NT>(src, prefix, mask, 64 - FB - 10, need2, nl, em, hist, scratch);
   } else {
     RowSource src{sc, n};
-    radix_finish<kST>(src, prefix, mask, 64 - FB - 10, need2, nd2, em, hist, scratch);
+    radix_finish<NT>(src, prefix, mask, 64 - FB - 10, need2, nd2, em, hist, scratch);
   }
 }
 
-template <int HT, int D>
+template <int HT, int D, bool W32, bool SPLIT>
 hipError_t launch_score_t(const PrefillArgs& a, hipStream_t stream) {
   constexpr int ROWS = kRows;
-  const size_t lds = prefill_lds_bytes<D, ROWS>();
+  const size_t lds = prefill_lds_bytes<D, ROWS, SPLIT>();
   static_assert(prefill_lds_bytes<D, ROWS>() <= 160 * 1024, "LDS");
-  auto k = k_prefill_score<HT, D, ROWS>;
+  auto k = k_prefill_score<HT, D, ROWS, W32, SPLIT>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const int groups = (a.nq + ROWS - 1) / ROWS;
-  hipLaunchKernelGGL(k, dim3(groups), dim3(64 * ROWS), lds, stream, a);
+  const int chunks = SPLIT ? (int)((a.l_max + a.key_chunk - 1) / a.key_chunk) : 1;
+  hipLaunchKernelGGL(k, dim3(groups, chunks), dim3(64 * ROWS), lds, stream, a);
   return hipGetLastError();
+}
+
+template <int HT, int D>
+hipError_t launch_score_hd(const PrefillArgs& a, hipStream_t stream) {
+  if (a.key_chunk > 0) return launch_score_t<HT, D, false, true>(a, stream);
+  if (a.bin_bits == 11) return launch_score_t<HT, D, true, false>(a, stream);
+  return launch_score_t<HT, D, false, false>(a, stream);
 }
 
 }  // namespace
@@ -481,27 +543,39 @@ hipError_t launch_prefill_score(const PrefillArgs& a, hipStream_t stream) {
   if (a.nq <= 0) return hipSuccess;
   // every key of a row's last stage is stored: rows span whole stages
   if (a.row_stride % kStageKeys != 0 || a.row_stride < a.l_max || !a.spare_row) return hipErrorInvalidValue;
-  if (a.head_dim == 128) return a.n_heads <= 32 ? launch_score_t<1, 128>(a, stream)
-                                                : launch_score_t<2, 128>(a, stream);
-  if (a.head_dim == 64) return a.n_heads <= 32 ? launch_score_t<1, 64>(a, stream)
-                                               : launch_score_t<2, 64>(a, stream);
+  // 16-bit counters hold rows of up to 65535 keys; 32-bit counters (11-bit
+  // bins) any row; the row offsets are 32-bit byte offsets; split key chunks
+  // are whole stages (and are counted by the select kernel in 12-bit bins)
+  if (a.l_max >= (int64_t)1 << 30 || (a.bin_bits == 12 && a.l_max > 65535 && a.key_chunk == 0) ||
+      (a.bin_bits != 12 && a.bin_bits != 11) || a.key_chunk < 0 || a.key_chunk % kStageKeys ||
+      (a.key_chunk > 0 && a.bin_bits != 12))
+    return hipErrorInvalidValue;
+  if (a.head_dim == 128)
+    return a.n_heads <= 32 ? launch_score_hd<1, 128>(a, stream) : launch_score_hd<2, 128>(a, stream);
+  if (a.head_dim == 64)
+    return a.n_heads <= 32 ? launch_score_hd<1, 64>(a, stream) : launch_score_hd<2, 64>(a, stream);
   return hipErrorInvalidValue;
 }
 
-template <int FB>
+template <int FB, bool SELF = false>
 hipError_t launch_select_t(const PrefillArgs& a, hipStream_t stream) {
-  const size_t lds = (size_t)kSelListCap * 8 + 64 * 8 + (1024 + 64) * 4;
-  auto k = k_prefill_select<FB>;
+  const size_t lds = (size_t)kSelListCap * 8 + 64 * 8 + (1024 + 64) * 4 + (SELF ? (4 << FB) : 0);
+  // (rows of a split call are few and long: 1024 threads each)
+  constexpr int NT = SELF ? 1024 : kST;
+  auto k = k_prefill_select<FB, SELF, NT>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k, dim3(a.nq), dim3(kST), lds, stream, a);
+  hipLaunchKernelGGL(k, dim3(a.nq), dim3(NT), lds, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_prefill_select(const PrefillArgs& a, hipStream_t stream) {
   if (a.nq <= 0) return hipSuccess;
+  if (a.key_chunk > 0) return a.bin_bits == 12 ? launch_select_t<12, true>(a, stream)
+                                                : hipErrorInvalidValue;
   if (a.bin_bits == 12) return launch_select_t<12>(a, stream);
+  if (a.bin_bits == 11) return launch_select_t<11>(a, stream);
   if (a.bin_bits == 10) return launch_select_t<10>(a, stream);
   return hipErrorInvalidValue;
 }

@@ -328,7 +328,8 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
 
 hipError_t launch_prefill_routed_score(const PrefillArgs& a, hipStream_t stream) {
   if (a.nq <= 0) return hipSuccess;
-  if (a.h_use < 1 || a.h_use > kRoutedMaxHeads || a.bin_bits != kRBinBits) return hipErrorInvalidValue;
+  if (a.h_use < 1 || a.h_use > kRoutedMaxHeads || a.bin_bits != kRBinBits || a.key_chunk != 0)
+    return hipErrorInvalidValue;
   // every key of a row's last stage is stored: rows span whole stages
   if (a.row_stride % kStageKeys != 0 || a.row_stride < a.l_max || !a.spare_row) return hipErrorInvalidValue;
   if (a.head_dim == 128) return launch_t<128>(a, stream);

@@ -378,7 +378,9 @@ void prefill_scorer(const PrefillArgs& a, int rows, bool routed) {
       maxpos = std::max(maxpos, pos[i]);
     }
     if (maxpos < 0) continue;
-    if (maxpos > 65535) violation("16-bit LDS row histograms with position %lld", (long long)maxpos);
+    if (maxpos > 65535 && (routed || (a.bin_bits == 12 && a.key_chunk == 0)))
+      violation("16-bit LDS row histograms with position %lld", (long long)maxpos);
+    if (a.key_chunk < 0 || a.key_chunk % 128 || (routed && a.key_chunk)) violation("key chunk %d", a.key_chunk);
     const int64_t n_stages = maxpos / 128 + 1;
     touch(a.keys, 0, (maxpos + 1) * rb, "keys (sequence 0, clamped to the group's last position)");
     for (int i = 0; i < rows; ++i) {
@@ -393,8 +395,9 @@ void prefill_scorer(const PrefillArgs& a, int rows, bool routed) {
       touch_elems(a.w, (int64_t)t * a.n_heads, (int64_t)(t + 1) * a.n_heads, "w");
       // stores span whole stages of the group
       if (n_stages * 128 > a.row_stride) violation("stage stores past the row stride");
+      // (split key chunks store whole stages inside [0, n_stages * 128) too)
       touch_elems(a.scores, (int64_t)t * a.row_stride, (int64_t)t * a.row_stride + n_stages * 128, "score row");
-      touch_elems(a.rowmeta, (int64_t)t * 4, (int64_t)t * 4 + 3, "row metadata");
+      if (a.key_chunk == 0) touch_elems(a.rowmeta, (int64_t)t * 4, (int64_t)t * 4 + 3, "row metadata");
     }
   }
 }
@@ -404,6 +407,10 @@ hipError_t launch_prefill_score(const PrefillArgs& a, hipStream_t) {
   begin("k_prefill_score");
   if (a.nq <= 0) return hipSuccess;
   if (a.row_stride % 128 != 0 || a.row_stride < a.l_max || !a.spare_row) return hipErrorInvalidValue;
+  if (a.l_max >= (int64_t)1 << 30 || (a.bin_bits == 12 && a.l_max > 65535 && a.key_chunk == 0) ||
+      (a.bin_bits != 12 && a.bin_bits != 11) || a.key_chunk < 0 || a.key_chunk % 128 ||
+      (a.key_chunk > 0 && a.bin_bits != 12))
+    return hipErrorInvalidValue;
   prefill_scorer(a, 8, false);
   return hipSuccess;
 }
@@ -420,7 +427,7 @@ hipError_t launch_prefill_routed_score(const PrefillArgs& a, hipStream_t) {
 hipError_t launch_prefill_select(const PrefillArgs& a, hipStream_t) {
   begin("k_prefill_select");
   if (a.nq <= 0) return hipSuccess;
-  if (a.bin_bits != 12 && a.bin_bits != 10) return hipErrorInvalidValue;
+  if (a.bin_bits != 12 && a.bin_bits != 11 && a.bin_bits != 10) return hipErrorInvalidValue;
   for (int t = 0; t < a.nq; ++t) {
     const QRow r = qrow(a.q_seq, a.q_pos, t, 1, a.l_max);
     touch_elems(a.out_idx, (int64_t)t * a.top_k, (int64_t)(t + 1) * a.top_k, "out_idx");
@@ -431,7 +438,7 @@ hipError_t launch_prefill_select(const PrefillArgs& a, hipStream_t) {
     const int64_t hi = n <= a.top_k ? n : 4 * ((n + 3) / 4);
     if (hi > a.row_stride) violation("row %d reads %lld floats of a %lld stride", t, (long long)hi, (long long)a.row_stride);
     touch_elems(a.scores, (int64_t)t * a.row_stride, (int64_t)t * a.row_stride + hi, "score row");
-    if (n > a.top_k) touch_elems(a.rowmeta, (int64_t)t * 4, (int64_t)t * 4 + 3, "row metadata");
+    if (n > a.top_k && a.key_chunk == 0) touch_elems(a.rowmeta, (int64_t)t * 4, (int64_t)t * 4 + 3, "row metadata");
   }
   return hipSuccess;
 }

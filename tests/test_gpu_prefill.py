@@ -88,3 +88,50 @@ def test_prefill_all_equal_keys(dsa):
     gi = idx.cpu().numpy()
     for t in range(64):
         assert check_exact(gi[t], np.arange(2048)) == [], f"row {t}"
+
+
+def test_shared_cache_decode_queries_long_rows(dsa):
+    """64 decode queries sharing one 131072-key cache (its last 64 positions),
+    64 heads, k 2048: the query-grouped kernels with 11-bit bins and 32-bit
+    per-row counters (rows longer than 65535 keys); every row."""
+    wl = datagen.small(2, nq=64, n_seq=1, l_max=131072, layout="tail")
+    _run(dsa, wl, 2048, seed=6)
+
+
+def test_long_prefill_chunk_arbitrary_positions(dsa):
+    """A chunk of 96 prefill rows at arbitrary positions of one 100000-key
+    cache (32 heads, d 64, k 1000), with invalid rows and rows shorter than k;
+    sampled rows plus the invalid ones."""
+    wl = datagen.small(3, nq=96, l_max=100000, n_heads=32, head_dim=64, n_plant=64)
+    rng = np.random.default_rng(8)
+    pos = rng.integers(0, 100000, size=96)
+    pos[0], pos[1], pos[2], pos[3] = 99999, 65534, 65535, 500
+    pos[4] = -1
+    seq = np.zeros(96, dtype=np.int32)
+    seq[5] = 1
+    _run(dsa, wl, 1000, seed=7, pos=pos, seq=seq, rows=list(range(0, 96, 7)) + [1, 2, 3, 4, 5])
+
+
+def test_long_rows_all_equal_keys(dsa):
+    """All scores tie in 70000-key rows (11-bit bins, the tie bin overflows
+    LDS): the lowest indices are selected."""
+    wl = datagen.small(3, nq=64, l_max=70000, layout="tail", n_plant=0)
+    inp = datagen.make(wl, 9)
+    inp["k"][:] = inp["k"][:, :1, :]
+    dev = upload(inp, wl)
+    idx, _ = dsa.indexer_score_topk(dev["q"], dev["w"], dev["k"], dev["q_pos"], dev["q_seq"],
+                                    top_k=2048)
+    gi = idx.cpu().numpy()
+    for t in range(64):
+        assert check_exact(gi[t], np.arange(2048)) == [], f"row {t}"
+
+
+def test_long_rows_many_row_groups(dsa):
+    """2048 rows (256 row groups: no key split) at arbitrary positions of one
+    70000-key cache: rows longer than 65535 keys use 11-bit bins with 32-bit
+    per-row counters in the scoring kernel; sampled rows."""
+    wl = datagen.small(3, nq=2048, l_max=70000, n_heads=16, head_dim=64, n_plant=64)
+    rng = np.random.default_rng(10)
+    pos = rng.integers(0, 70000, size=2048)
+    pos[:8] = [69999, 65535, 65534, 2047, 2048, 0, 69998, 40000]
+    _run(dsa, wl, 2048, seed=11, pos=pos, rows=list(range(0, 2048, 97)) + list(range(8)))
