@@ -228,11 +228,11 @@ bool use_prefill(int32_t dtype, int64_t nq, int n_seq, int64_t l_max) {
 }
 int prefill_bin_bits(int64_t l_max) { return l_max <= 65535 ? 12 : 11; }
 
-// Keys per workgroup when the row groups (8 rows each) are too few to fill the
-// chip: enough chunks for about 512 workgroups (two share a compute unit when
-// the scorer keeps no histograms), each at least 1024 keys; 0 = no split.
-int prefill_key_chunk(int64_t nq, int64_t l_max) {
-  const int64_t groups = (nq + 7) / 8;
+// Keys per workgroup when the row groups (8 rows each, 32 for the routed
+// scorer) are too few to fill the chip: enough chunks for about 512
+// workgroups, each at least 1024 keys; 0 = no split.
+int prefill_key_chunk(int64_t nq, int64_t l_max, int rows_per_group = 8) {
+  const int64_t groups = (nq + rows_per_group - 1) / rows_per_group;
   if (groups >= 256) return 0;
   int64_t chunks = std::min<int64_t>((512 + groups - 1) / groups, (l_max + 1023) / 1024);
   if (chunks <= 1) return 0;
@@ -568,10 +568,10 @@ void fill_common(dsa::SelArgs& a, const void* q, const float* w, const void* k,
 // MISA on the prefill shape (one sequence, many bf16 rows, h <= 8, k' = 0): the
 // router, the head selection, the packed routed scoring and the row select.
 // (the routed scorer's per-row histograms have 16-bit counters: rows of up to
-// 65535 keys)
+// 65535 keys, unless the keys are split and the select counts the rows)
 bool use_misa_prefill(int32_t dtype, int64_t nq, int n_seq, int64_t l_max, int h, int k_prime) {
-  return use_prefill(dtype, nq, n_seq, l_max) && l_max <= 65535 && k_prime == 0 &&
-         h <= dsa::kRoutedMaxHeads;
+  return use_prefill(dtype, nq, n_seq, l_max) && k_prime == 0 && h <= dsa::kRoutedMaxHeads &&
+         (l_max <= 65535 || prefill_key_chunk(nq, l_max, 32) > 0);
 }
 
 struct MisaPrefillPlan {
@@ -676,7 +676,8 @@ int misa_prefill(const void* q, const float* w, const void* k, const void* k_poo
   pa.scores = at<float>(workspace, p.scores);
   pa.spare_row = pa.scores + (size_t)nq * p.row_stride;
   pa.rowmeta = at<int32_t>(workspace, p.rowmeta);
-  pa.bin_bits = 10;
+  pa.key_chunk = prefill_key_chunk(nq, l_max, 32);
+  pa.bin_bits = pa.key_chunk ? 12 : 10;
   pa.heads = rh.heads;
   pa.heads_stride = rh.heads_stride;
   pa.h_use = h;

@@ -14,7 +14,9 @@
 // consecutive keys in one register.
 // Per-row histograms are 10-bit with 16-bit counters, two per word (bin b in
 // word b % 512), 2 KiB per row, so that 32 rows' fit in LDS beside the two
-// stages.
+// stages.  With SPLIT (too few row groups to fill the chip) the keys are split
+// into chunks as well, one workgroup per (row group, chunk), with no
+// histograms: the select kernel counts the stored rows itself.
 #include "dsa_internal.h"
 #include "dsa_common.h"
 
@@ -31,9 +33,9 @@ constexpr int kRBinBits = 10;
 constexpr int kRBins = 1 << kRBinBits;
 constexpr int kRBinShift = 32 - kRBinBits;
 
-template <int D>
+template <int D, bool SPLIT = false>
 constexpr size_t routed_lds_bytes() {
-  return 2 * (size_t)kStageKeys * (D * 2 + 16) + (size_t)kRowsWg * (kRBins / 2) * 4;
+  return 2 * (size_t)kStageKeys * (D * 2 + 16) + (SPLIT ? 0 : (size_t)kRowsWg * (kRBins / 2) * 4);
 }
 
 // per-row partial sums of one sub-tile: p[g] = sum over registers 4g..4g+3 of
@@ -55,7 +57,7 @@ DSA_DEVICE void epi_regs(f32x4& p, const f32x16& acc, float W) {
   epi_seq<R0>(p, acc, W, std::make_integer_sequence<int, N>{});
 }
 
-template <int D>
+template <int D, bool SPLIT>
 __global__ __launch_bounds__(kThreads) void k_prefill_routed_score(PrefillArgs a) {
   constexpr int S = D / 16;
   constexpr int RB = D * 2;
@@ -87,14 +89,19 @@ __global__ __launch_bounds__(kThreads) void k_prefill_routed_score(PrefillArgs a
     }
     wave_max = pos[g] > wave_max ? pos[g] : wave_max;
   }
-  for (int i = threadIdx.x; i < kRowsWg * (kRBins / 2); i += kThreads) hist[i] = 0u;
+  if constexpr (!SPLIT)
+    for (int i = threadIdx.x; i < kRowsWg * (kRBins / 2); i += kThreads) hist[i] = 0u;
   if (threadIdx.x == 0) s_maxpos = -1;
   __syncthreads();
   if (lane == 0) atomicMax(&s_maxpos, wave_max);
   __syncthreads();
   const int maxpos = __builtin_amdgcn_readfirstlane(s_maxpos);
   if (maxpos < 0) return;
-  const int n_stages = maxpos / kStageKeys + 1;
+  // keys [kb, ke_last] of this workgroup (SPLIT: one chunk of whole stages)
+  const int kb = SPLIT ? (int)blockIdx.y * a.key_chunk : 0;
+  if (kb > maxpos) return;
+  const int ke_last = SPLIT ? min(kb + a.key_chunk - 1, maxpos) : maxpos;
+  const int n_stages = (ke_last - kb) / kStageKeys + 1;
   auto pos_of = [&](int g) {                 // pos[g] for a per-lane g
     int p = pos[0];
 #pragma unroll
@@ -130,8 +137,8 @@ __global__ __launch_bounds__(kThreads) void k_prefill_routed_score(PrefillArgs a
   // (a wave-uniform stage base plus a 32-bit lane offset; keys clamp to maxpos)
   auto fetch_piece = [&](int j, int st) {
     const int p = threadIdx.x + j * kThreads;
-    const int sk = min(st * kStageKeys, maxpos);
-    const int key = min(p / NC, maxpos - sk);
+    const int sk = min(kb + st * kStageKeys, ke_last);
+    const int key = min(p / NC, ke_last - sk);
     const uint8_t* sbase = kbase + (size_t)sk * RB;
     pre[j] = *reinterpret_cast<const u32x4*>(sbase + (uint32_t)(key * RB + (p % NC) * 16));
   };
@@ -175,11 +182,12 @@ __global__ __launch_bounds__(kThreads) void k_prefill_routed_score(PrefillArgs a
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(pa[g]), __float_as_uint(pb[g]),
                                                      false, false);
     fin_sc[i] = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) + 0.0f;
-    *reinterpret_cast<float*>(srow[g] + (uint32_t)(key0 + lane) * 4u) = fin_sc[i];
+    *reinterpret_cast<float*>(srow[g] + (uint32_t)(kb + key0 + lane) * 4u) = fin_sc[i];
   };
   // bin b counts in word b % 512: low half for b < 512 (negative scores, key
   // bit 31 clear), high half otherwise
   auto fin_count = [&](int i, int g, int key0) {
+    if constexpr (SPLIT) return;                // (the select kernel counts the rows)
     const float sc = fin_sc[i];
     const uint32_t word = (fast_key(sc) >> kRBinShift) & (kRBins / 2 - 1);
     const uint32_t inc = key0 + lane <= pos[g] ? ((int32_t)__float_as_uint(sc) < 0 ? 1u : 0x10000u) : 0u;
@@ -272,6 +280,7 @@ __global__ __launch_bounds__(kThreads) void k_prefill_routed_score(PrefillArgs a
   __syncthreads();
 
   // each row's threshold: the 10-bit bin holding its k-th score
+  if constexpr (SPLIT) return;
   constexpr int PERB = kRBins / 64;          // bins per lane
 #pragma unroll
   for (int g = 0; g < kPer; ++g) {
@@ -311,16 +320,17 @@ __global__ __launch_bounds__(kThreads) void k_prefill_routed_score(PrefillArgs a
   }
 }
 
-template <int D>
+template <int D, bool SPLIT>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
-  constexpr size_t lds = routed_lds_bytes<D>();
-  static_assert(lds <= 160 * 1024, "LDS");
-  auto k = k_prefill_routed_score<D>;
+  constexpr size_t lds = routed_lds_bytes<D, SPLIT>();
+  static_assert(routed_lds_bytes<D>() <= 160 * 1024, "LDS");
+  auto k = k_prefill_routed_score<D, SPLIT>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const int groups = (a.nq + kRowsWg - 1) / kRowsWg;
-  hipLaunchKernelGGL(k, dim3(groups), dim3(kThreads), lds, stream, a);
+  const int chunks = SPLIT ? (int)((a.l_max + a.key_chunk - 1) / a.key_chunk) : 1;
+  hipLaunchKernelGGL(k, dim3(groups, chunks), dim3(kThreads), lds, stream, a);
   return hipGetLastError();
 }
 
@@ -328,12 +338,17 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
 
 hipError_t launch_prefill_routed_score(const PrefillArgs& a, hipStream_t stream) {
   if (a.nq <= 0) return hipSuccess;
-  if (a.h_use < 1 || a.h_use > kRoutedMaxHeads || a.bin_bits != kRBinBits || a.key_chunk != 0)
+  // (16-bit row histograms without a key split; with one the select counts
+  // the rows in 12-bit bins)
+  const bool split = a.key_chunk > 0;
+  if (a.h_use < 1 || a.h_use > kRoutedMaxHeads || a.key_chunk < 0 || a.key_chunk % kStageKeys ||
+      a.bin_bits != (split ? 12 : kRBinBits) || (!split && a.l_max > 65535) ||
+      a.l_max >= (int64_t)1 << 30)
     return hipErrorInvalidValue;
   // every key of a row's last stage is stored: rows span whole stages
   if (a.row_stride % kStageKeys != 0 || a.row_stride < a.l_max || !a.spare_row) return hipErrorInvalidValue;
-  if (a.head_dim == 128) return launch_t<128>(a, stream);
-  if (a.head_dim == 64) return launch_t<64>(a, stream);
+  if (a.head_dim == 128) return split ? launch_t<128, true>(a, stream) : launch_t<128, false>(a, stream);
+  if (a.head_dim == 64) return split ? launch_t<64, true>(a, stream) : launch_t<64, false>(a, stream);
   return hipErrorInvalidValue;
 }
 

@@ -218,6 +218,15 @@ def workloads(A):
     run_misa(A, "misa prefill C3", 32768, 64, 128, 1, 32768, 64, 8, 0, 2048, pooled=False,
              layout="prefill")
     run_hisa(A, "hisa prefill C3", 32768, 64, 128, 1, 32768, 128, 64, 2048, layout="prefill")
+    # prefill-shaped calls whose rows outgrow 16-bit counts or whose row groups
+    # are too few to fill the chip: keys split over workgroups, 11-bit bins
+    run_dense(A, "dense shared-cache decode 64 x 131072", 64, 64, 128, 1, 131072, 2048,
+              layout="tail")
+    run_misa(A, "misa shared-cache decode 64 x 131072", 64, 64, 128, 1, 131072, 64, 8, 0, 2048,
+             pooled=False, layout="tail")
+    run_dense(A, "dense prefill chunk 96 x 100000", 96, 64, 128, 1, 100000, 2048,
+              layout="prefill", with_seq=False)
+    run_dense(A, "dense long rows 2048 x 70000", 2048, 64, 128, 1, 70000, 2048, layout="tail")
     run_mla(A, "sparse attention 64 x 128 heads x 2048", 64, 128, 64, 131072, 2048)
     run_mla(A, "sparse attention 256 queries (unsplit)", 256, 128, 256, 4096, 2048)
 

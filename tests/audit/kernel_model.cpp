@@ -378,9 +378,9 @@ void prefill_scorer(const PrefillArgs& a, int rows, bool routed) {
       maxpos = std::max(maxpos, pos[i]);
     }
     if (maxpos < 0) continue;
-    if (maxpos > 65535 && (routed || (a.bin_bits == 12 && a.key_chunk == 0)))
+    if (maxpos > 65535 && a.key_chunk == 0 && (routed || a.bin_bits == 12))
       violation("16-bit LDS row histograms with position %lld", (long long)maxpos);
-    if (a.key_chunk < 0 || a.key_chunk % 128 || (routed && a.key_chunk)) violation("key chunk %d", a.key_chunk);
+    if (a.key_chunk < 0 || a.key_chunk % 128) violation("key chunk %d", a.key_chunk);
     const int64_t n_stages = maxpos / 128 + 1;
     touch(a.keys, 0, (maxpos + 1) * rb, "keys (sequence 0, clamped to the group's last position)");
     for (int i = 0; i < rows; ++i) {
@@ -418,7 +418,10 @@ hipError_t launch_prefill_score(const PrefillArgs& a, hipStream_t) {
 hipError_t launch_prefill_routed_score(const PrefillArgs& a, hipStream_t) {
   begin("k_prefill_routed_score");
   if (a.nq <= 0) return hipSuccess;
-  if (a.h_use < 1 || a.h_use > kRoutedMaxHeads || a.bin_bits != 10) return hipErrorInvalidValue;
+  const bool split = a.key_chunk > 0;
+  if (a.h_use < 1 || a.h_use > kRoutedMaxHeads || a.key_chunk < 0 || a.key_chunk % 128 ||
+      a.bin_bits != (split ? 12 : 10) || (!split && a.l_max > 65535) || a.l_max >= (int64_t)1 << 30)
+    return hipErrorInvalidValue;
   if (a.row_stride % 128 != 0 || a.row_stride < a.l_max || !a.spare_row) return hipErrorInvalidValue;
   prefill_scorer(a, 32, true);
   return hipSuccess;

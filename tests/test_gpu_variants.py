@@ -159,6 +159,16 @@ def test_misa_prefill_arbitrary_positions_and_invalid_rows(dsa):
     _misa_case(dsa, wl, h=8, k=256, kprime=0, seed=6, pos=pos, rows=valid)
 
 
+def test_misa_shared_cache_decode_queries(dsa):
+    """MISA for 64 decode queries sharing one 131072-key cache (its last 64
+    positions, most ending inside a 64-key block): the prefill-shaped router
+    and the routed scorer with its keys split over workgroups (rows longer than
+    65535 keys); every query's heads, then its selection given those heads."""
+    wl = datagen.small(4, nq=64, n_seq=1, l_max=131072, layout="tail", plant="points",
+                       n_plant=64)
+    _misa_case(dsa, wl, h=8, k=2048, kprime=0, seed=12)
+
+
 def test_misa_all_heads_equals_dense(dsa):
     """h = H_I routes every head: the selection must be the dense indexer's."""
     wl = datagen.small(4, nq=4, n_seq=4, l_max=8192)
