@@ -83,7 +83,7 @@ inline size_t hisa_lds_bytes(const HisaArgs& a) {
 // LDS of the selection kernel (1024 threads): histogram [bins + bins / 4],
 // scan scratch [64], kept blocks [m_blocks], then (8-byte aligned) the tie
 // list [kHisaListCap], the brute-force tie slots [64], the output staging
-// [kHisaCandCap] and the entries [kHisaRegKeys] (pairs).
+// [kHisaCandCap] and the radix finish's spill [kHisaRegKeys] (pairs).
 inline __host__ __device__ int hisa_topk_list_offset_words(const HisaArgs& a) {
   const int w = kHisaBins + kHisaBins / 4 + 64 + a.m_blocks;
   return (w + 1) & ~1;

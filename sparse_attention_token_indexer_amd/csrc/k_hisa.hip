@@ -273,48 +273,111 @@ DSA_DEVICE void select_exact(const Src& src, uint32_t top_k, const Emitter& em, 
   }
 }
 
-// Exact top-k of the n (key, id) pairs in LDS at ent (key 0 = empty): Kt =
-// min(top_k, valid entries) ids and scores go to out_idx / out_score (LDS or
-// device memory), slots [Kt, top_k) are padded with (-1, -inf).  A padded
-// histogram gives the k-th entry's bin b* from per-thread runs of bins and one
-// scan; every thread's entries above b* take consecutive slots (a wave scan of
-// the per-thread counts, one LDS atomic per wave) and go out through the LDS
-// `stage` (stage_cap pairs) when given, in one coalesced copy; entries in b*
-// are collected in the LDS list and resolved there (brute force up to 64,
-// else finish_bin), or by the radix finish over all entries when the bin
-// overflows the list.  Every pass is a plain loop
-// over the entries, which keeps the register needs (scalar ones in
-// particular) small.  With `hist_clear` the caller has already zeroed hist
-// (and synchronised).
-template <int NT>
-DSA_DEVICE void select_lds(const uint2* ent, int n, int top_k, int32_t* out_idx, float* out_score,
-                           uint2* stage, uint32_t stage_cap, uint32_t* hist, uint32_t* scratch,
-                           uint2* list, uint2* tie, uint32_t* s_out, uint32_t* s_ln, int* s_b,
-                           uint32_t* s_above, uint32_t* s_nb, bool hist_clear = false) {
+// Shared scalars of one selection.
+struct SelVars {
+  uint32_t out, ln, above, nb;
+  int b;
+};
+
+// Exact top-k of entries held in registers: thread tid holds entries tid + u *
+// NT (u < U) as (k[u], id[u]), key 0 = empty.  Kt = min(top_k, valid entries)
+// ids and scores go to out_idx / out_score (LDS or device memory), slots
+// [Kt, top_k) are padded with (-1, -inf).
+//  * First-level bins are linear in the score over the valid entries' own
+//    range, bin = min(4095, (s - smin) * 4096 / (smax - smin)) (every step is
+//    monotone, so the bins are ordered like the keys), which spreads one
+//    query's scores evenly where bins of the key's top bits would put most of
+//    them into the few bins of their shared exponents.  When the range is not
+//    finite (infinite or NaN scores) the bins are the key's offset from the
+//    smallest key, shifted to 12 bits.
+//  * Entries above the k-th entry's bin b* take consecutive slots (a wave scan
+//    of the per-thread counts, one LDS atomic per wave), through the LDS
+//    `stage` (stage_cap pairs) when given, then in one coalesced copy.
+//  * Entries in b* go to the LDS list (or, when they overflow it, to `spill`,
+//    >= NT * U pairs of LDS that are free here) and are resolved there by
+//    brute force (up to 64) or by the radix finish over their whole (key, id)
+//    composites.
+// hist must be zero on entry when `hist_clear` is set; scratch >= 64 words.
+template <int NT, int U>
+DSA_DEVICE void select_regs(const uint32_t (&k)[U], const int32_t (&id)[U], int top_k,
+                            int32_t* out_idx, float* out_score, uint2* stage, uint32_t stage_cap,
+                            uint32_t* hist, uint32_t* scratch, uint2* list, uint2* tie,
+                            uint2* spill, SelVars& sv, bool hist_clear) {
   typedef Hist<NT> H;
   constexpr int PB = H::P;
-  const int tid = (int)threadIdx.x, lane = lane_id();
-  if (!hist_clear) {
-    for (int i = tid; i < H::kWords; i += NT) hist[i] = 0;
-    __syncthreads();
-  }
-  // (every pass takes kSU entries per thread at a time, their reads in flight
-  // together, in the same order each time)
-  for (int base = 0; base < n; base += kSU * NT) {
-    uint32_t k[kSU];
+  constexpr int NW = NT / 64;
+  static_assert(3 * NW <= 64, "range reduction fits the scratch words");
+  const int tid = (int)threadIdx.x, lane = lane_id(), wv = tid >> 6;
+  // the valid entries' count and key range
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u, nv = 0u;
 #pragma unroll
-    for (int u = 0; u < kSU; ++u) {
-      const int i = base + tid + u * NT;
-      k[u] = i < n ? ent[i].x : 0u;
+  for (int u = 0; u < U; ++u)
+    if (k[u]) {
+      mn = k[u] < mn ? k[u] : mn;
+      mx = k[u] > mx ? k[u] : mx;
+      ++nv;
     }
 #pragma unroll
-    for (int u = 0; u < kSU; ++u)                          // (empty slots: key 0)
-      if (k[u]) atomicAdd(&hist[H::at((int)(k[u] >> kBinShift))], 1u);
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint32_t a = (uint32_t)__shfl_xor((int)mn, o, 64);
+    const uint32_t b = (uint32_t)__shfl_xor((int)mx, o, 64);
+    mn = a < mn ? a : mn;
+    mx = b > mx ? b : mx;
+    nv += (uint32_t)__shfl_xor((int)nv, o, 64);
   }
+  if (lane == 0) {
+    scratch[wv] = mn;
+    scratch[NW + wv] = mx;
+    scratch[2 * NW + wv] = nv;
+  }
+  if (!hist_clear)
+    for (int i = tid; i < H::kWords; i += NT) hist[i] = 0;
   if (tid == 0) {
-    *s_out = 0;
-    *s_ln = 0;
+    sv.out = 0;
+    sv.ln = 0;
   }
+  __syncthreads();
+  mn = 0xFFFFFFFFu;
+  mx = 0u;
+  nv = 0u;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t a = scratch[w], b = scratch[NW + w];
+    mn = a < mn ? a : mn;
+    mx = b > mx ? b : mx;
+    nv += scratch[2 * NW + w];
+  }
+  const uint32_t Kt = nv < (uint32_t)top_k ? nv : (uint32_t)top_k;
+  for (int i = (int)Kt + tid; i < top_k; i += NT) {
+    out_idx[i] = -1;
+    if (out_score) out_score[i] = -__builtin_inff();
+  }
+  if (Kt == 0) {                               // (every path ends at a barrier)
+    __syncthreads();
+    return;
+  }
+  const Emitter em{out_idx, out_score, &sv.out, Kt};
+  if (nv <= (uint32_t)top_k) {                 // every valid entry
+#pragma unroll
+    for (int u = 0; u < U; ++u) em.put_wave(k[u] != 0u, k[u], id[u]);
+    __syncthreads();
+    return;
+  }
+  // first-level bins (see above)
+  const float smin = key_to_score(mn), span = key_to_score(mx) - smin;
+  const float scale = (float)kBins / span;
+  const bool lin = span > 0.f && span <= 3.402823466e38f && scale <= 3.402823466e38f;
+  const uint32_t range = mx - mn;
+  const int len = range ? 32 - __clz((int)range) : 0;          // bits of the key range
+  const int shift = len > kBinBits ? len - kBinBits : 0;
+  auto bin_of = [&](uint32_t x) -> int {
+    if (!lin) return (int)((x - mn) >> shift);
+    const int b = (int)((key_to_score(x) - smin) * scale);
+    return b < kBins - 1 ? b : kBins - 1;
+  };
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (k[u]) atomicAdd(&hist[H::at(bin_of(k[u]))], 1u);
   __syncthreads();
   const int b0 = kBins - PB * (tid + 1);                   // this thread's bins, from the top
   uint32_t h[PB], mine = 0;
@@ -323,96 +386,73 @@ DSA_DEVICE void select_lds(const uint2* ent, int n, int top_k, int32_t* out_idx,
     h[j] = hist[H::at(b0) + j];
     mine += h[j];
   }
-  uint32_t n_valid;
-  const uint32_t before = block_exclusive_sum<NT>(mine, scratch, &n_valid);
-  const uint32_t Kt = n_valid < (uint32_t)top_k ? n_valid : (uint32_t)top_k;
-  for (int i = (int)Kt + tid; i < top_k; i += NT) {
-    out_idx[i] = -1;
-    if (out_score) out_score[i] = -__builtin_inff();
-  }
-  if (Kt == 0) return;
+  uint32_t tot;
+  const uint32_t before = block_exclusive_sum<NT>(mine, scratch, &tot);
   if (before < Kt && before + mine >= Kt) {
     uint32_t acc = before;
 #pragma unroll
     for (int j = PB - 1; j >= 0; --j) {
       if (acc + h[j] >= Kt) {
-        *s_b = b0 + j;
-        *s_above = acc;
-        *s_nb = h[j];
+        sv.b = b0 + j;
+        sv.above = acc;
+        sv.nb = h[j];
         break;
       }
       acc += h[j];
     }
   }
   __syncthreads();
-  const int bstar = *s_b;
-  const uint32_t above = *s_above, nb = *s_nb;
+  const int bstar = sv.b;
+  const uint32_t above = sv.above, nb = sv.nb;
   const bool fits = nb <= kHisaListCap;
   uint32_t na = 0, nt = 0;
-  for (int base = 0; base < n; base += kSU * NT) {
-    uint32_t k[kSU];
+  int bu[U];
 #pragma unroll
-    for (int u = 0; u < kSU; ++u) {
-      const int i = base + tid + u * NT;
-      k[u] = i < n ? ent[i].x : 0u;
-    }
-#pragma unroll
-    for (int u = 0; u < kSU; ++u) {
-      const int b = (int)(k[u] >> kBinShift);
-      na += (k[u] && b > bstar) ? 1u : 0u;
-      nt += (fits && k[u] && b == bstar) ? 1u : 0u;
-    }
+  for (int u = 0; u < U; ++u) {
+    bu[u] = k[u] ? bin_of(k[u]) : -1;
+    na += bu[u] > bstar ? 1u : 0u;
+    nt += (fits && bu[u] == bstar) ? 1u : 0u;
   }
   const uint32_t cnt = na | (nt << 16);
   const uint32_t inc = wave_incl_scan(cnt);
   uint32_t base = 0;
   if (lane == 63) {
-    if (inc & 0xffffu) base = atomicAdd(s_out, inc & 0xffffu);
-    if (inc >> 16) base |= atomicAdd(s_ln, inc >> 16) << 16;
+    if (inc & 0xffffu) base = atomicAdd(&sv.out, inc & 0xffffu);
+    if (inc >> 16) base |= atomicAdd(&sv.ln, inc >> 16) << 16;
   }
   base = (uint32_t)__builtin_amdgcn_readlane((int)base, 63);
   const uint32_t ex = inc - cnt;
   uint32_t oa = (base & 0xffffu) + (ex & 0xffffu), ot = (base >> 16) + (ex >> 16);
   const bool staged = stage != nullptr && above <= stage_cap;
-  for (int base = 0; base < n; base += kSU * NT) {
-    uint2 ev[kSU];
 #pragma unroll
-    for (int u = 0; u < kSU; ++u) {
-      const int i = base + tid + u * NT;
-      ev[u] = i < n ? ent[i] : make_uint2(0u, 0u);
-    }
-#pragma unroll
-    for (int u = 0; u < kSU; ++u) {
-      const uint2 e = ev[u];
-      const int b = (int)(e.x >> kBinShift);
-      if (e.x && b > bstar) {
-        if (oa < above) {
-          if (staged) {
-            stage[oa] = e;
-          } else {
-            out_idx[oa] = (int32_t)e.y;
-            if (out_score) out_score[oa] = key_to_score(e.x);
-          }
+  for (int u = 0; u < U; ++u) {
+    if (bu[u] > bstar) {
+      if (oa < above) {
+        if (staged) {
+          stage[oa] = make_uint2(k[u], (uint32_t)id[u]);
+        } else {
+          out_idx[oa] = id[u];
+          if (out_score) out_score[oa] = key_to_score(k[u]);
         }
-        ++oa;
-      } else if (fits && e.x && b == bstar) {
-        if (ot < kHisaListCap) list[ot] = e;
-        ++ot;
       }
+      ++oa;
+    } else if (fits && bu[u] == bstar) {
+      if (ot < kHisaListCap) list[ot] = make_uint2(k[u], (uint32_t)id[u]);
+      ++ot;
     }
   }
   __syncthreads();
   if (staged) {
-    for (uint32_t base = 0; base < above; base += kSU * NT) {
-      uint2 ev[kSU];
+    for (uint32_t base2 = 0; base2 < above; base2 += 8 * NT) {
+      uint2 ev[8];
 #pragma unroll
-      for (int u = 0; u < kSU; ++u) {
-        const uint32_t i = base + tid + u * NT;
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t i = base2 + tid + u * NT;
         ev[u] = i < above ? stage[i] : make_uint2(0u, 0u);
       }
 #pragma unroll
-      for (int u = 0; u < kSU; ++u) {
-        const uint32_t i = base + tid + u * NT;
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t i = base2 + tid + u * NT;
         if (i < above) {
           out_idx[i] = (int32_t)ev[u].y;
           if (out_score) out_score[i] = key_to_score(ev[u].x);
@@ -420,18 +460,27 @@ DSA_DEVICE void select_lds(const uint2* ent, int n, int top_k, int32_t* out_idx,
       }
     }
   }
-  const uint32_t need = Kt - above;                        // *s_out == above here
-  const Emitter em{out_idx, out_score, s_out, Kt};
-  if (fits) {
-    const uint32_t nl = *s_ln < nb ? *s_ln : nb;
-    if (need < nl && nl <= 64) rank_finish64(list, nl, need, em);
-    else finish_bin<NT>(list, nl, need, bstar, em, hist, scratch, tie);
-  } else {
-    const uint64_t prefix = (uint64_t)bstar << (64 - kBinBits);
-    const uint64_t mask = (uint64_t)(kBins - 1) << (64 - kBinBits);
-    radix_finish<NT>(PairSource{ent, (uint32_t)n}, prefix, mask, 64 - kBinBits, need, nb, em,
-                      hist, scratch);
+  const uint32_t need = Kt - above;                        // sv.out == above here
+  const uint2* ties = list;
+  uint32_t nl = sv.ln < nb ? sv.ln : nb;
+  if (!fits) {
+    // the tied bin's entries into spill (sv.ln is still 0: nothing was listed)
+    uint32_t c = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) c += bu[u] == bstar ? 1u : 0u;
+    const uint32_t ci = wave_incl_scan(c);
+    uint32_t sb = 0;
+    if (lane == 63) sb = atomicAdd(&sv.ln, ci);
+    sb = (uint32_t)__builtin_amdgcn_readlane((int)sb, 63) + (ci - c);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (bu[u] == bstar) spill[sb++] = make_uint2(k[u], (uint32_t)id[u]);
+    __syncthreads();
+    ties = spill;
+    nl = nb;
   }
+  if (need < nl && nl <= 64) rank_finish64(ties, nl, need, em);
+  else radix_finish<NT>(PairSource{ties, nl}, 0ull, 0ull, 64, need, nl, em, hist, scratch);
 }
 
 // MISA head routing finished inside a workgroup: the router's per-slice sums
@@ -495,8 +544,9 @@ __global__ __launch_bounds__(kHT) __attribute__((amdgpu_waves_per_eu(2))) void k
   uint2* list = reinterpret_cast<uint2*>(smem + hisa_list_offset_words(a));   // [kHisaListCap]
   uint2* tie = list + kHisaListCap;                             // [64]
   uint2* cl = tie + 64;                                         // [kHisaCandCap] block candidates
-  __shared__ uint32_t s_cnt, s_ln, s_out, s_sel, s_go, s_above, s_nb;
+  __shared__ uint32_t s_cnt, s_ln, s_out, s_sel, s_go;
   __shared__ int s_b;
+  __shared__ SelVars sv;
   __shared__ int32_t s_heads[64];
   __shared__ float s_I[64];
 
@@ -644,8 +694,17 @@ __global__ __launch_bounds__(kHT) __attribute__((amdgpu_waves_per_eu(2))) void k
           for (int i = S + tid; i < (int)scnt[sg]; i += kHT)
             cl[off[sg] + i] = ld_dev(cbase + (size_t)sg * a.ch1 + i);
         __syncthreads();
-        select_lds<kHT>(cl, (int)tot, m1, sbid, sbsc, nullptr, 0u, hist, scratch, list, tie,
-                        &s_out, &s_ln, &s_b, &s_above, &s_nb, true);
+        uint32_t kk[kSU];
+        int32_t ii[kSU];
+#pragma unroll
+        for (int u = 0; u < kSU; ++u) {
+          const int i = tid + u * kHT;
+          const uint2 e = i < (int)tot ? cl[i] : make_uint2(0u, 0u);
+          kk[u] = e.x;
+          ii[u] = (int32_t)e.y;
+        }
+        select_regs<kHT, kSU>(kk, ii, m1, sbid, sbsc, nullptr, 0u, hist, scratch, list, tie, cl,
+                              sv, true);
       } else {
         const Emitter em{sbid, sbsc, &s_out, (uint32_t)m1};     // into LDS, then out
         const DevSegSource src{cbase, off, n1, a.ch1};
@@ -703,9 +762,8 @@ __global__ __launch_bounds__(kTT) void k_hisa_topk(HisaArgs a) {
   uint2* list = reinterpret_cast<uint2*>(smem + hisa_topk_list_offset_words(a));   // [kHisaListCap]
   uint2* tie = list + kHisaListCap;                             // [64]
   uint2* stage = tie + 64;                                      // [kHisaCandCap]
-  uint2* ent = stage + kHisaCandCap;                            // [kHisaRegKeys] (key, id)
-  __shared__ uint32_t s_out, s_ln, s_above, s_nb;
-  __shared__ int s_b;
+  uint2* ent = stage + kHisaCandCap;                            // [kHisaRegKeys] radix spill
+  __shared__ SelVars sv;
   const int t = blockIdx.x, tid = (int)threadIdx.x;
   // Every load in one round: the token keys of up to m_blocks * block items
   // (k_hisa stored the query's items2 <= m_blocks * block of them; slots past
@@ -744,15 +802,17 @@ __global__ __launch_bounds__(kTT) void k_hisa_topk(HisaArgs a) {
   const int items2 = m1 * a.block;
   if (tid < m1) sbid[tid] = my_block;
   __syncthreads();
-  // (key, token id) of every item into LDS: item i = tid + u * kTT is token
-  // list[i / block] * block + i % block; list index and offset advance by kTT
-  // per step without a division (kSU * kTT = kHisaRegKeys >= items2: one batch)
+  // token id of every item: item i = tid + u * kTT is token list[i / block] *
+  // block + i % block; list index and offset advance by kTT per step without a
+  // division (kSU * kTT = kHisaRegKeys >= items2: one batch)
   const int blk = a.block, step = kTT / blk, rem = kTT % blk;
   int li = tid / blk, r = tid % blk;
+  int32_t idv[kSU];
 #pragma unroll
   for (int u = 0; u < kSU; ++u) {
     const int i = tid + u * kTT;
-    if (i < items2) ent[i] = make_uint2(k[u], (uint32_t)(sbid[li < m1 ? li : m1 - 1] * blk + r));
+    if (i >= items2) k[u] = 0u;
+    idv[u] = sbid[li < m1 ? li : m1 - 1] * blk + r;
     li += step;
     r += rem;
     if (r >= blk) {
@@ -760,9 +820,8 @@ __global__ __launch_bounds__(kTT) void k_hisa_topk(HisaArgs a) {
       ++li;
     }
   }
-  __syncthreads();
-  select_lds<kTT>(ent, items2, a.top_k, out_i, out_s, stage, kHisaCandCap, hist, scratch, list,
-                  tie, &s_out, &s_ln, &s_b, &s_above, &s_nb);
+  select_regs<kTT, kSU>(k, idv, a.top_k, out_i, out_s, stage, kHisaCandCap, hist, scratch, list,
+                        tie, ent, sv, false);
 }
 
 template <class SC, int NF, int D>

@@ -456,3 +456,77 @@ def test_hisa_all_blocks_equals_dense_and_iou(dsa):
     iou = dsa.indexer_selection_iou(small["idx"], dn).cpu().numpy()
     ref = O.iou_rows(small["idx"].cpu().numpy(), dn.cpu().numpy())
     np.testing.assert_allclose(iou, ref, rtol=1e-6)
+
+
+def _by_groups(ids, labels, gscore, kk, what):
+    """The kk items of largest group score, ties to the lower id; identical key
+    rows give bit-identical scores on both sides, so this set is exact as long
+    as the groups around the k-th place are farther apart than the tolerance
+    (asserted, so that an input too close to call fails loudly)."""
+    order = sorted(range(len(ids)), key=lambda i: (-gscore[labels[i]], ids[i]))
+    kk = min(kk, len(ids))
+    if kk < len(ids):
+        g = labels[order[kk - 1]]
+        vals = sorted({float(gscore[x]) for x in set(labels.tolist())}, reverse=True)
+        j = vals.index(float(gscore[g]))
+        tol = 2e-3 * abs(vals[j]) + 1e-6
+        near = [abs(vals[j] - vals[i]) for i in (j - 1, j + 1) if 0 <= i < len(vals)]
+        assert min(near, default=np.inf) > 4 * tol, \
+            f"{what}: groups around the k-th place too close to call"
+    return sorted(int(ids[i]) for i in order[:kk])
+
+
+@pytest.mark.parametrize("per_block", [False, True])
+def test_hisa_few_distinct_key_rows_resolve_ties_by_index(dsa, per_block):
+    """Keys drawn from a small palette of distinct rows (per token: 24 rows; per
+    block: 8 rows, every token of a block the same row).  Identical rows score
+    identically, so the k-th token score's bin holds one tied row's items
+    (about 170 of 4096, or 512) and, per block, the m-th block score's bin
+    about 128 tied blocks: both selections resolve large tie bins, which must
+    keep every item of the higher-scoring rows and, of the tied row, the lowest
+    indices.  Scores are checked against the oracle under the usual rule."""
+    n_seq, L, H, D, B, m, k = 4, 65536, 32, 128, 64, 64, 1000
+    P = 8 if per_block else 24
+    rng = np.random.default_rng(21 if per_block else 22)
+    pos = np.array([L - 1, L - 30, 40000, 9000], dtype=np.int32)
+    say(f"[hisa palette] per_block={per_block} P={P} nq={n_seq} L={L} B={B} m={m} k={k}")
+    pal = torch.from_numpy(rng.standard_normal((P, D)).astype(np.float32)).to(torch.bfloat16)
+    lab = (np.repeat(rng.integers(0, P, size=(n_seq, L // B)), B, axis=1) if per_block
+           else rng.integers(0, P, size=(n_seq, L)))
+    q = torch.from_numpy(rng.standard_normal((n_seq, H, D)).astype(np.float32)).to(torch.bfloat16)
+    w = torch.from_numpy(rng.standard_normal((n_seq, H)).astype(np.float32))
+    keys = pal[torch.from_numpy(lab)]                                   # [n_seq, L, D]
+    res = dsa.hisa_block_filter_topk(q.cuda(), w.cuda(), keys.cuda(), torch.from_numpy(pos).cuda(),
+                                     torch.arange(n_seq, dtype=torch.int32, device="cuda"),
+                                     block=B, m_blocks=m, top_k=k)
+    torch.cuda.synchronize()
+    out = {key: v.cpu().numpy() for key, v in res.items()}
+    errs = [] if not out["status"].any() else [f"status {out['status'].tolist()}"]
+    bits = lambda x: x.view(torch.int16).numpy().view(np.uint16)
+    pal64 = O.to_f64(bits(pal), datagen.BF16)
+    K_all = O.to_f64(bits(keys), datagen.BF16)
+    for t in range(n_seq):
+        q_t = O.to_f64(bits(q[t]), datagen.BF16)
+        w_t = w[t].numpy().astype(np.float64)
+        p = int(pos[t])
+        gs, _ = O.hisa_block_scores(q_t, w_t, pal64)                      # score of each row
+        M = (p + B) // B
+        if per_block:                                                  # blocks: exact set
+            want = _by_groups(np.arange(M), lab[t, ::B][:M], gs, m, f"blocks q{t}")
+            got = sorted(out["blocks"][t][:min(m, M)].tolist())
+            if got != want:
+                errs.append(f"q{t}: blocks differ from the tie rule ({len(set(got) ^ set(want))})")
+        K = K_all[t]
+        pooled_ref = O.misa_pooled_for_query(K, B, p)
+        bs, bA = O.hisa_block_scores(q_t, w_t, pooled_ref)
+        errs += check_selection(out["blocks"][t], out["block_score"][t], np.arange(M), bs, bA, m,
+                                O.dot_magnitude(q_t, w_t, pooled_ref), what=f"blocks q{t}")
+        r = O.hisa_row(q_t, w_t, K, p, B, m, k, blocks=out["blocks"][t])
+        errs += _check(out["idx"][t], out["score"][t], r["cand"], r["s"], r["A"], k, q_t, w_t, K,
+                       f"hisa q{t}")
+        cand = r["cand"]
+        want = _by_groups(cand, lab[t][cand], gs, k, f"tokens q{t}")
+        got = sorted(out["idx"][t][:min(k, cand.size)].tolist())
+        if got != want:
+            errs.append(f"q{t}: tokens differ from the tie rule ({len(set(got) ^ set(want))})")
+    assert not errs, "\n".join(errs[:12])
