@@ -51,15 +51,6 @@ constexpr int kHT = 256;                        // threads per workgroup
 constexpr int kHW = kHT / 64;
 constexpr int kPB = kBins / kHT;                // histogram bins per thread
 constexpr int kTT = 1024;                       // threads of the selection kernel
-// LDS histograms read by NT threads in runs of P = kBins / NT consecutive bins
-// are padded with one word after every P bins, so the runs start on distinct
-// banks.
-template <int NT>
-struct Hist {
-  static constexpr int P = kBins / NT;
-  static constexpr int kWords = kBins + kBins / P;
-  DSA_DEVICE static int at(int b) { return b + b / P; }
-};
 constexpr int kHistWords = Hist<kHT>::kWords;
 DSA_DEVICE int hpad(int b) { return Hist<kHT>::at(b); }
 constexpr int kSU = 8;                          // entries per thread per pass step
@@ -271,216 +262,6 @@ DSA_DEVICE void select_exact(const Src& src, uint32_t top_k, const Emitter& em, 
     const uint64_t mask = (uint64_t)(kBins - 1) << (64 - kBinBits);
     radix_finish<kHT>(src, prefix, mask, 64 - kBinBits, need, nb, em, hist, scratch);
   }
-}
-
-// Shared scalars of one selection.
-struct SelVars {
-  uint32_t out, ln, above, nb;
-  int b;
-};
-
-// Exact top-k of entries held in registers: thread tid holds entries tid + u *
-// NT (u < U) as (k[u], id[u]), key 0 = empty.  Kt = min(top_k, valid entries)
-// ids and scores go to out_idx / out_score (LDS or device memory), slots
-// [Kt, top_k) are padded with (-1, -inf).
-//  * First-level bins are linear in the score over the valid entries' own
-//    range, bin = min(4095, (s - smin) * 4096 / (smax - smin)) (every step is
-//    monotone, so the bins are ordered like the keys), which spreads one
-//    query's scores evenly where bins of the key's top bits would put most of
-//    them into the few bins of their shared exponents.  When the range is not
-//    finite (infinite or NaN scores) the bins are the key's offset from the
-//    smallest key, shifted to 12 bits.
-//  * Entries above the k-th entry's bin b* take consecutive slots (a wave scan
-//    of the per-thread counts, one LDS atomic per wave), through the LDS
-//    `stage` (stage_cap pairs) when given, then in one coalesced copy.
-//  * Entries in b* go to the LDS list (or, when they overflow it, to `spill`,
-//    >= NT * U pairs of LDS that are free here) and are resolved there by
-//    brute force (up to 64) or by the radix finish over their whole (key, id)
-//    composites.
-// hist must be zero on entry when `hist_clear` is set; scratch >= 64 words.
-template <int NT, int U>
-DSA_DEVICE void select_regs(const uint32_t (&k)[U], const int32_t (&id)[U], int top_k,
-                            int32_t* out_idx, float* out_score, uint2* stage, uint32_t stage_cap,
-                            uint32_t* hist, uint32_t* scratch, uint2* list, uint2* tie,
-                            uint2* spill, SelVars& sv, bool hist_clear) {
-  typedef Hist<NT> H;
-  constexpr int PB = H::P;
-  constexpr int NW = NT / 64;
-  static_assert(3 * NW <= 64, "range reduction fits the scratch words");
-  const int tid = (int)threadIdx.x, lane = lane_id(), wv = tid >> 6;
-  // the valid entries' count and key range
-  uint32_t mn = 0xFFFFFFFFu, mx = 0u, nv = 0u;
-#pragma unroll
-  for (int u = 0; u < U; ++u)
-    if (k[u]) {
-      mn = k[u] < mn ? k[u] : mn;
-      mx = k[u] > mx ? k[u] : mx;
-      ++nv;
-    }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const uint32_t a = (uint32_t)__shfl_xor((int)mn, o, 64);
-    const uint32_t b = (uint32_t)__shfl_xor((int)mx, o, 64);
-    mn = a < mn ? a : mn;
-    mx = b > mx ? b : mx;
-    nv += (uint32_t)__shfl_xor((int)nv, o, 64);
-  }
-  if (lane == 0) {
-    scratch[wv] = mn;
-    scratch[NW + wv] = mx;
-    scratch[2 * NW + wv] = nv;
-  }
-  if (!hist_clear)
-    for (int i = tid; i < H::kWords; i += NT) hist[i] = 0;
-  if (tid == 0) {
-    sv.out = 0;
-    sv.ln = 0;
-  }
-  __syncthreads();
-  mn = 0xFFFFFFFFu;
-  mx = 0u;
-  nv = 0u;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const uint32_t a = scratch[w], b = scratch[NW + w];
-    mn = a < mn ? a : mn;
-    mx = b > mx ? b : mx;
-    nv += scratch[2 * NW + w];
-  }
-  const uint32_t Kt = nv < (uint32_t)top_k ? nv : (uint32_t)top_k;
-  for (int i = (int)Kt + tid; i < top_k; i += NT) {
-    out_idx[i] = -1;
-    if (out_score) out_score[i] = -__builtin_inff();
-  }
-  if (Kt == 0) {                               // (every path ends at a barrier)
-    __syncthreads();
-    return;
-  }
-  const Emitter em{out_idx, out_score, &sv.out, Kt};
-  if (nv <= (uint32_t)top_k) {                 // every valid entry
-#pragma unroll
-    for (int u = 0; u < U; ++u) em.put_wave(k[u] != 0u, k[u], id[u]);
-    __syncthreads();
-    return;
-  }
-  // first-level bins (see above)
-  const float smin = key_to_score(mn), span = key_to_score(mx) - smin;
-  const float scale = (float)kBins / span;
-  const bool lin = span > 0.f && span <= 3.402823466e38f && scale <= 3.402823466e38f;
-  const uint32_t range = mx - mn;
-  const int len = range ? 32 - __clz((int)range) : 0;          // bits of the key range
-  const int shift = len > kBinBits ? len - kBinBits : 0;
-  auto bin_of = [&](uint32_t x) -> int {
-    if (!lin) return (int)((x - mn) >> shift);
-    const int b = (int)((key_to_score(x) - smin) * scale);
-    return b < kBins - 1 ? b : kBins - 1;
-  };
-#pragma unroll
-  for (int u = 0; u < U; ++u)
-    if (k[u]) atomicAdd(&hist[H::at(bin_of(k[u]))], 1u);
-  __syncthreads();
-  const int b0 = kBins - PB * (tid + 1);                   // this thread's bins, from the top
-  uint32_t h[PB], mine = 0;
-#pragma unroll
-  for (int j = 0; j < PB; ++j) {
-    h[j] = hist[H::at(b0) + j];
-    mine += h[j];
-  }
-  uint32_t tot;
-  const uint32_t before = block_exclusive_sum<NT>(mine, scratch, &tot);
-  if (before < Kt && before + mine >= Kt) {
-    uint32_t acc = before;
-#pragma unroll
-    for (int j = PB - 1; j >= 0; --j) {
-      if (acc + h[j] >= Kt) {
-        sv.b = b0 + j;
-        sv.above = acc;
-        sv.nb = h[j];
-        break;
-      }
-      acc += h[j];
-    }
-  }
-  __syncthreads();
-  const int bstar = sv.b;
-  const uint32_t above = sv.above, nb = sv.nb;
-  const bool fits = nb <= kHisaListCap;
-  uint32_t na = 0, nt = 0;
-  int bu[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    bu[u] = k[u] ? bin_of(k[u]) : -1;
-    na += bu[u] > bstar ? 1u : 0u;
-    nt += (fits && bu[u] == bstar) ? 1u : 0u;
-  }
-  const uint32_t cnt = na | (nt << 16);
-  const uint32_t inc = wave_incl_scan(cnt);
-  uint32_t base = 0;
-  if (lane == 63) {
-    if (inc & 0xffffu) base = atomicAdd(&sv.out, inc & 0xffffu);
-    if (inc >> 16) base |= atomicAdd(&sv.ln, inc >> 16) << 16;
-  }
-  base = (uint32_t)__builtin_amdgcn_readlane((int)base, 63);
-  const uint32_t ex = inc - cnt;
-  uint32_t oa = (base & 0xffffu) + (ex & 0xffffu), ot = (base >> 16) + (ex >> 16);
-  const bool staged = stage != nullptr && above <= stage_cap;
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    if (bu[u] > bstar) {
-      if (oa < above) {
-        if (staged) {
-          stage[oa] = make_uint2(k[u], (uint32_t)id[u]);
-        } else {
-          out_idx[oa] = id[u];
-          if (out_score) out_score[oa] = key_to_score(k[u]);
-        }
-      }
-      ++oa;
-    } else if (fits && bu[u] == bstar) {
-      if (ot < kHisaListCap) list[ot] = make_uint2(k[u], (uint32_t)id[u]);
-      ++ot;
-    }
-  }
-  __syncthreads();
-  if (staged) {
-    for (uint32_t base2 = 0; base2 < above; base2 += 8 * NT) {
-      uint2 ev[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const uint32_t i = base2 + tid + u * NT;
-        ev[u] = i < above ? stage[i] : make_uint2(0u, 0u);
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const uint32_t i = base2 + tid + u * NT;
-        if (i < above) {
-          out_idx[i] = (int32_t)ev[u].y;
-          if (out_score) out_score[i] = key_to_score(ev[u].x);
-        }
-      }
-    }
-  }
-  const uint32_t need = Kt - above;                        // sv.out == above here
-  const uint2* ties = list;
-  uint32_t nl = sv.ln < nb ? sv.ln : nb;
-  if (!fits) {
-    // the tied bin's entries into spill (sv.ln is still 0: nothing was listed)
-    uint32_t c = 0;
-#pragma unroll
-    for (int u = 0; u < U; ++u) c += bu[u] == bstar ? 1u : 0u;
-    const uint32_t ci = wave_incl_scan(c);
-    uint32_t sb = 0;
-    if (lane == 63) sb = atomicAdd(&sv.ln, ci);
-    sb = (uint32_t)__builtin_amdgcn_readlane((int)sb, 63) + (ci - c);
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (bu[u] == bstar) spill[sb++] = make_uint2(k[u], (uint32_t)id[u]);
-    __syncthreads();
-    ties = spill;
-    nl = nb;
-  }
-  if (need < nl && nl <= 64) rank_finish64(ties, nl, need, em);
-  else radix_finish<NT>(PairSource{ties, nl}, 0ull, 0ull, 64, need, nl, em, hist, scratch);
 }
 
 // MISA head routing finished inside a workgroup: the router's per-slice sums
@@ -703,8 +484,8 @@ __global__ __launch_bounds__(kHT) __attribute__((amdgpu_waves_per_eu(2))) void k
           kk[u] = e.x;
           ii[u] = (int32_t)e.y;
         }
-        select_regs<kHT, kSU>(kk, ii, m1, sbid, sbsc, nullptr, 0u, hist, scratch, list, tie, cl,
-                              sv, true);
+        select_regs<kHT, kSU, kHisaListCap>(kk, ii, m1, sbid, sbsc, nullptr, 0u, hist, scratch,
+                                            list, tie, cl, sv, true);
       } else {
         const Emitter em{sbid, sbsc, &s_out, (uint32_t)m1};     // into LDS, then out
         const DevSegSource src{cbase, off, n1, a.ch1};
@@ -820,8 +601,8 @@ __global__ __launch_bounds__(kTT) void k_hisa_topk(HisaArgs a) {
       ++li;
     }
   }
-  select_regs<kTT, kSU>(k, idv, a.top_k, out_i, out_s, stage, kHisaCandCap, hist, scratch, list,
-                        tie, ent, sv, false);
+  select_regs<kTT, kSU, kHisaListCap>(k, idv, a.top_k, out_i, out_s, stage, kHisaCandCap, hist,
+                                      scratch, list, tie, ent, sv, false);
 }
 
 template <class SC, int NF, int D>
