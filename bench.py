@@ -15,7 +15,11 @@ dense indexer on the same inputs), misa_hisa (the same with the router's
 h = 8 heads), pool (mean
 pooling of the 128K caches), sparse_mla (the attention that consumes the
 index lists: 64 queries x 128 heads over 2048 listed rows of their own
-131072-row latent caches, absorbed-MLA rows of 576 bf16 values).  tiny, hisa,
+131072-row latent caches, absorbed-MLA rows of 576 bf16 values),
+dense_shared_decode (the 64 decode queries on one shared 131072-key cache),
+certified (the certified exact top-k on the dense decode inputs: 16 screened
+heads, bounds for the rest, survivors rescored; also times the dense call on
+the same inputs).  tiny, hisa,
 misa_hisa and sparse_mla touch less than the 256 MB last-level cache and are
 timed cold.
 
@@ -41,7 +45,7 @@ CSRC = os.path.join(ROOT, "sparse_attention_token_indexer_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 WORKLOADS = {"dense_decode": 2, "tiny": 1, "dense_prefill": 3, "misa": 4, "misa_dagger": 4,
-             "dense_shared_decode": 2,
+             "dense_shared_decode": 2, "certified": 2,
              "hisa": 5, "pool": 4, "misa_prefill": 3, "hisa_prefill": 3, "misa_hisa": 5,
              "sparse_mla": None}
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
@@ -55,7 +59,7 @@ DENSE_IOU_MAX_L = 131072
 KERNEL_SOURCE = {"dense_decode": "k_score_select.hip", "tiny": "k_score_select.hip",
                  "misa": "k_score_select.hip", "misa_dagger": "k_score_select.hip",
                  "hisa": "k_hisa.hip", "dense_prefill": "k_prefill.hip",
-                 "dense_shared_decode": "k_prefill.hip",
+                 "dense_shared_decode": "k_prefill.hip", "certified": "k_score_select.hip",
                  "misa_prefill": "k_prefill_routed.hip", "pool": "k_pool.hip",
                  "hisa_prefill": "k_hisa.hip", "misa_hisa": "k_hisa.hip",
                  "sparse_mla": "k_mla.hip"}
@@ -170,6 +174,8 @@ def cpu_baseline(wl, seed, seconds: float, mode: str):
             O.hisa_row(q_t, w_t, K, p, 128, 64, wl.top_k)
         elif mode == "misa_hisa":
             O.misa_hisa_row(q_t, w_t, K, p, wl.block, 8, wl.m_blocks, wl.top_k)
+        elif mode == "certified":
+            O.dosa_row(q_t, w_t, K, p, wl.top_k, 16)
         else:
             O.dense_row(q_t, w_t, K, p, wl.top_k)
         spent += time.perf_counter() - t0
@@ -327,6 +333,29 @@ def main() -> int:
         call_flops = kernel_flops
         bound_note = ("MFMA: the head contraction of every causal (query, key) pair; the shared "
                       "cache is staged once per 8-query group")
+    elif name == "certified":
+        # the certified exact top-k (16 screened heads, bounds for the other 48,
+        # survivors rescored with every head) on the dense decode inputs
+        hs = 16
+        nbytes = dsa.indexer_certified_topk_workspace_size(nq, H, d, wl.n_seq, L, hs, topk)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        surv = torch.zeros(nq, dtype=torch.int32, device=dev)
+
+        def step():
+            dsa.indexer_certified_topk(q, w, k, q_pos, q_seq, top_k=topk, n_screen_heads=hs,
+                                       out_idx=out_i, out_score=out_s, out_survivors=surv,
+                                       workspace=ws)
+        step()
+        torch.cuda.synchronize()
+        n_surv = int(surv.sum())
+        kind = "score_tokens"
+        kernel_bytes = pairs * d * eb + nq * hs * d * eb + nq * hs * 4 + nq * topk * 8 + pairs * 4
+        call_bytes = kernel_bytes + n_surv * (d * eb + 8) + nq * H * d * eb + nq * H * 4
+        call_flops = pairs * hs * d * 2 + n_surv * H * d * 2
+        bound_note = ("HBM: the screening pass reads every prefix key row once and writes its "
+                      "upper bound")
+        extra["certified"] = {"screened_heads": hs, "survivors": n_surv,
+                              "survivor_frac": n_surv / pairs}
     elif name == "dense_prefill":
         nbytes = dsa.indexer_score_topk_workspace_size(nq, H, d, wl.n_seq, L, topk, 0)
         ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
@@ -569,6 +598,28 @@ def main() -> int:
                                       "dense_over_hisa": dense_med / call_med_ms}
     if name in ("hisa", "misa_hisa", "hisa_prefill"):
         extra["timed_out_queries"] = int(status.sum())       # of the last call (0: complete)
+    if name == "certified":
+        # the dense call on the same inputs (the same result), timed the same way
+        dws = torch.empty(dsa.indexer_score_topk_workspace_size(nq, H, d, wl.n_seq, L, topk, 0),
+                          dtype=torch.uint8, device=dev)
+        d_i = torch.empty_like(out_i)
+        d_s = torch.empty_like(out_s)
+        for _ in range(args.warmup):
+            dsa.indexer_score_topk(q, w, k, q_pos, q_seq, top_k=topk, out_idx=d_i, out_score=d_s,
+                                   workspace=dws)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            dsa.indexer_score_topk(q, w, k, q_pos, q_seq, top_k=topk, out_idx=d_i, out_score=d_s,
+                                   workspace=dws)
+        e1.record()
+        torch.cuda.synchronize()
+        same = bool(torch.equal(torch.sort(out_i, dim=1).values, torch.sort(d_i, dim=1).values))
+        extra["dense_same_inputs"] = {"dense_us": e0.elapsed_time(e1) / args.steps * 1e3,
+                                      "same_selection": same}
+        del dws
     if name == "dense_shared_decode":
         # the same queries one short of the query-grouped path's 64: the
         # per-query decode kernels, which stream the shared cache per query
@@ -649,7 +700,8 @@ def main() -> int:
                                 "pool": "mean_pool_L128K_B64",
                                 "misa_prefill": "misa_prefill_L32K_H64_h8",
                                 "hisa_prefill": "hisa_prefill_L32K_H64_B128_m64",
-                                "misa_hisa": "misa_hisa_decode_L1M_H32_h8"}.get(name, wl.name),
+                                "misa_hisa": "misa_hisa_decode_L1M_H32_h8",
+                                "certified": "certified_decode_L128K_H64_h16"}.get(name, wl.name),
                    "queries": nq, "l_max": L, "n_heads": H, "head_dim": d,
                    "top_k": topk, ("attended_pairs" if name == "sparse_mla" else "causal_pairs"): pairs,
                    "parallelism": "single GPU",

@@ -122,6 +122,43 @@ int indexer_score_topk_noalloc(const void* q, const float* w, const void* k, int
                                hipStream_t stream);
 
 /*
+ * Certified exact top-k of the dense indexer (DoSA review, sections 1 and 3:
+ * screen with part of the heads, bound the others, prune, rescore the
+ * survivors with every head and select; the page gives no formulas, these
+ * bounds are derived from Cauchy-Schwarz).  Same result as indexer_score_topk
+ * on the same inputs (the rescoring scores every survivor with all heads
+ * exactly as the dense call does; ties: lower index):
+ *  1. screened heads S: the n_screen_heads heads of largest |w_j| * |q_j|
+ *     (ties: lower j); every other head j adds w_j * max(0, q_j . k) with
+ *     0 <= max(0, q_j . k) <= |q_j| |k|, so with s_S the score over S,
+ *       LB = s_S + |k| * sum_{j not in S, w_j < 0} w_j |q_j|,
+ *       UB = s_S + |k| * sum_{j not in S, w_j > 0} w_j |q_j|
+ *     (each widened by 2^-12 (|s_S| + |k| sum_j |w_j| |q_j|) for rounding);
+ *  2. tau = the top_k-th largest LB of the query (every key kept when its
+ *     prefix holds fewer than top_k keys);
+ *  3. survivors: the keys with UB >= tau (no other key can be selected);
+ *  4. every head over the survivors, then the exact top_k.
+ * The screening pass reads the whole key cache, like the dense call, and the
+ * rescoring gathers the survivors' rows again: the call pays off only when few
+ * keys survive (on inputs with little structure nearly every key survives).
+ *
+ *   out_survivors [nq] int32 survivor count of each query, or NULL
+ * Only DSA_DTYPE_BF16; 1 <= n_screen_heads <= min(n_heads, 16); l_max <=
+ * 65535 * 4096.  Other arguments as for indexer_score_topk.  Workspace:
+ * indexer_certified_topk_workspace_size(...) (8 * nq * l_max bytes for the
+ * bounds and survivor lists, plus one set of candidate segments).
+ */
+size_t indexer_certified_topk_workspace_size(int32_t nq, int32_t n_heads, int32_t head_dim,
+                                             int32_t n_seq, int64_t l_max,
+                                             int32_t n_screen_heads, int32_t top_k);
+int indexer_certified_topk(const void* q, const float* w, const void* k, int32_t dtype,
+                           const int32_t* q_seq, const int32_t* q_pos, int32_t nq,
+                           int32_t n_heads, int32_t head_dim, int32_t n_seq, int64_t l_max,
+                           int32_t n_screen_heads, int32_t top_k, int32_t* out_idx,
+                           float* out_score, int32_t* out_survivors, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Mean-pooled block keys (MISA summary, "method" step 1: M = ceil(L/B) blocks
  * and mean-pooled indexing keys; HISA review, section 3: pooled representative
  * vector per block of size B).  Block b of sequence s covers tokens
@@ -303,7 +340,8 @@ int indexer_selection_iou(const int32_t* a, const int32_t* b, int32_t nq, int32_
 #define DSA_KERNEL_PREFILL_ROUTED 12 /* MISA routed scoring on the prefill shape */
 #define DSA_KERNEL_HISA 13        /* HISA in one kernel: blocks, top-m, tokens, top-k */
 #define DSA_KERNEL_MLA 14         /* sparse attention over the index list (+ slice merge) */
-#define DSA_KERNEL_KINDS 15
+#define DSA_KERNEL_CERTIFY 15     /* certified top-k: screened heads and bounds, survivor lists */
+#define DSA_KERNEL_KINDS 16
 int dsa_kernel_timing(int enable);
 int dsa_kernel_timing_read(int32_t kind, int64_t* launches, double* total_ms, double* min_ms,
                            double* max_ms);

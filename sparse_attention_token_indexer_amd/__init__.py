@@ -28,7 +28,7 @@ DSA_DTYPE_F32 = 1
 KERNEL_KINDS = {
     "prepare": 0, "score_tokens": 1, "score_pooled": 2, "score_list": 3, "score_blocks": 4,
     "route": 5, "pool": 6, "iou": 7, "prefill": 8, "rowselect": 9, "merge": 10,
-    "route_heads": 11, "prefill_routed": 12, "hisa": 13, "mla": 14,
+    "route_heads": 11, "prefill_routed": 12, "hisa": 13, "mla": 14, "certify": 15,
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -188,6 +188,41 @@ def indexer_score_topk_noalloc(q: torch.Tensor, w: torch.Tensor, k: torch.Tensor
 
 
 NOALLOC_SCRATCH_BYTES = 80 << 20
+
+
+def indexer_certified_topk_workspace_size(nq: int, n_heads: int, head_dim: int, n_seq: int,
+                                          l_max: int, n_screen_heads: int, top_k: int) -> int:
+    return int(lib().indexer_certified_topk_workspace_size(nq, n_heads, head_dim, n_seq, l_max,
+                                                           n_screen_heads, top_k))
+
+
+def indexer_certified_topk(q: torch.Tensor, w: torch.Tensor, k: torch.Tensor, q_pos: torch.Tensor,
+                           q_seq: Optional[torch.Tensor] = None, top_k: int = 2048,
+                           n_screen_heads: int = 16, out_idx: Optional[torch.Tensor] = None,
+                           out_score: Optional[torch.Tensor] = None, with_scores: bool = True,
+                           with_survivors: bool = True, out_survivors: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """Certified exact top-k (screened heads, Cauchy-Schwarz bounds for the
+    others, survivors rescored with every head): the dense call's result.
+    Returns {"idx", "score", "survivors"} (survivor count per query)."""
+    dev, nq, H, d, n_seq, l_max = _common(q, w, k, q_pos, q_seq)
+    dt = _dtype_code(q)
+    out_idx, out_score = _outputs(dev, nq, top_k, out_idx, out_score, with_scores)
+    surv = out_survivors
+    if surv is None and with_survivors:
+        surv = torch.empty(nq, dtype=torch.int32, device=dev)
+    if surv is not None:
+        _need(surv, "out_survivors", torch.int32, 1)
+    nbytes = indexer_certified_topk_workspace_size(nq, H, d, n_seq, l_max, n_screen_heads, top_k)
+    ws = _workspace(nbytes, dev, workspace)
+    st = lib().indexer_certified_topk(_ptr(q), _ptr(w), _ptr(k), dt, _ptr(q_seq), _ptr(q_pos), nq,
+                                      H, d, n_seq, l_max, n_screen_heads, top_k, _ptr(out_idx),
+                                      _ptr(out_score), _ptr(surv), _ptr(ws), nbytes, _stream(dev))
+    _check(st, "indexer_certified_topk")
+    out = {"idx": out_idx, "score": out_score}
+    if surv is not None:
+        out["survivors"] = surv
+    return out
 
 
 def indexer_mean_pool_keys(k: torch.Tensor, block: int,
@@ -432,6 +467,7 @@ __all__ = [
     "kernel_timing", "kernel_timing_read", "KERNEL_KINDS",
     "DsaError", "LIB_PATH", "lib", "DSA_DTYPE_BF16", "DSA_DTYPE_F32",
     "indexer_score_topk", "indexer_score_topk_workspace_size", "indexer_score_topk_noalloc",
+    "indexer_certified_topk", "indexer_certified_topk_workspace_size",
     "indexer_mean_pool_keys",
     "misa_route_score_topk", "misa_route_score_topk_workspace_size",
     "hisa_block_filter_topk", "hisa_block_filter_topk_workspace_size",

@@ -16,6 +16,9 @@ _SIGS = {
                             _c_p, _c_p, _c_p, _sz, _c_p], ctypes.c_int),
     "indexer_score_topk_noalloc": ([_c_p, _c_p, _c_p, _i32, _c_p, _c_p, _i32, _i32, _i32, _i32,
                                     _i64, _i32, _c_p, _c_p, _c_p], ctypes.c_int),
+    "indexer_certified_topk_workspace_size": ([_i32, _i32, _i32, _i32, _i64, _i32, _i32], _sz),
+    "indexer_certified_topk": ([_c_p, _c_p, _c_p, _i32, _c_p, _c_p, _i32, _i32, _i32, _i32, _i64,
+                                _i32, _i32, _c_p, _c_p, _c_p, _c_p, _sz, _c_p], ctypes.c_int),
     "indexer_mean_pool_keys": ([_c_p, _i32, _i32, _i64, _i32, _i32, _c_p, _c_p], ctypes.c_int),
     "misa_route_score_topk_workspace_size": ([_i32, _i32, _i32, _i32, _i64, _i32, _i32, _i32, _i32,
                                               _i32], _sz),

@@ -18,7 +18,7 @@ OBJ = os.path.join(os.path.dirname(HERE), "_build")
 LIB = os.path.join(HERE, "libdsa_indexer.so")
 SOURCES = ["api.hip", "k_score_select.hip", "k_prefill.hip", "k_prefill_routed.hip", "k_pool.hip",
            "k_route.hip", "k_hisa.hip", "k_mla.hip",
-           "k_iou.hip"]
+           "k_iou.hip", "k_certify.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

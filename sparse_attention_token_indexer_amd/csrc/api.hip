@@ -695,7 +695,7 @@ extern "C" {
 
 const char* dsa_last_error(void) { return g_err.c_str(); }
 
-int dsa_abi_version(void) { return 2; }
+int dsa_abi_version(void) { return 3; }
 
 int dsa_hisa_wait_limit(int64_t ticks) {
   g_hisa_spin.store(ticks < 0 ? dsa::kHisaSpinTicks : (uint64_t)ticks, std::memory_order_relaxed);
@@ -1141,6 +1141,141 @@ int misa_hisa_topk(const void* q, const float* w, const void* k, const void* k_p
   return run_hisa_kernels(p.h, q, w, k, pooled, partial, q_seq, q_pos, route, nq, n_heads,
                           head_dim, n_seq, l_max, block, m_blocks, top_k, out_idx, out_score,
                           out_blocks, out_block_score, out_status, workspace, stream);
+}
+
+}  // extern "C"
+
+// --------------------------------------------------- certified exact top-k ----
+
+namespace {
+
+// workspace of the certified call: two histograms and the survivor counts
+// (cleared), the bounds, the screened heads, every key's upper bound, the
+// screening selection, the survivor lists, and one set of candidate segments
+// shared by the screening pass and the rescoring (they run one after the other)
+struct CertPlan {
+  StagePlan s0, s1;
+  size_t zero_bytes = 0, cnt = 0, cert = 0, heads = 0, ub = 0, lb_idx = 0, lb_score = 0,
+         list = 0, total = 0;
+};
+
+CertPlan plan_cert(int64_t nq, int head_dim, int64_t l_max, int h, int top_k) {
+  CertPlan p;
+  Arena A;
+  plan_zero(A, p.s0, nq);
+  plan_zero(A, p.s1, nq);
+  p.cnt = A.take((size_t)nq * 4);
+  p.zero_bytes = A.off;
+  p.cert = A.take((size_t)nq * 16);
+  p.heads = A.take((size_t)nq * h * 4);
+  p.ub = A.take((size_t)nq * l_max * 4);
+  p.lb_idx = A.take((size_t)nq * top_k * 4);
+  p.lb_score = A.take((size_t)nq * top_k * 4);
+  p.list = A.take((size_t)nq * l_max * 4);
+  plan_cand(A, p.s0, nq, l_max, 0, head_dim);
+  p.s1.chunk = p.s0.chunk;
+  p.s1.n_chunks = p.s0.n_chunks;
+  p.s1.cand = p.s0.cand;
+  p.s1.cnt = p.s0.cnt;
+  p.total = A.off;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t indexer_certified_topk_workspace_size(int32_t nq, int32_t n_heads, int32_t head_dim,
+                                             int32_t n_seq, int64_t l_max,
+                                             int32_t n_screen_heads, int32_t top_k) {
+  (void)n_heads;
+  (void)n_seq;
+  if (nq <= 0 || l_max <= 0 || top_k <= 0 || n_screen_heads <= 0) return 0;
+  return plan_cert(nq, head_dim, l_max, n_screen_heads, top_k).total;
+}
+
+int indexer_certified_topk(const void* q, const float* w, const void* k, int32_t dtype,
+                           const int32_t* q_seq, const int32_t* q_pos, int32_t nq,
+                           int32_t n_heads, int32_t head_dim, int32_t n_seq, int64_t l_max,
+                           int32_t n_screen_heads, int32_t top_k, int32_t* out_idx,
+                           float* out_score, int32_t* out_survivors, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  int st = check_common(q, w, k, dtype, q_pos, nq, n_heads, head_dim, n_seq, l_max, top_k, out_idx);
+  if (st) return st;
+  if (dtype != DSA_DTYPE_BF16) return fail(DSA_EUNSUPPORTED, "the certified call supports bf16 only");
+  if (n_screen_heads < 1 || n_screen_heads > n_heads || n_screen_heads > dsa::kCertMaxHeads)
+    return fail(DSA_EINVAL, "n_screen_heads must be in [1, min(n_heads, %d)] (got %d)",
+                dsa::kCertMaxHeads, n_screen_heads);
+  if (l_max > (int64_t)65535 * 4096)
+    return fail(DSA_EUNSUPPORTED, "l_max above %lld is not supported by the certified call",
+                (long long)65535 * 4096);
+  if (out_survivors && !aligned(out_survivors, 4))
+    return fail(DSA_EINVAL, "out_survivors must be 4-byte aligned");
+  if (nq == 0) return DSA_OK;
+  const CertPlan p = plan_cert(nq, head_dim, l_max, n_screen_heads, top_k);
+  if ((st = check_ws(workspace, workspace_bytes, p.total))) return st;
+  if ((st = run_prepare(workspace, p.zero_bytes, k, q_seq, q_pos, nq, n_seq, head_dim, 1, l_max,
+                        nullptr, stream)))
+    return st;
+  dsa::CertArgs c{};
+  c.q = reinterpret_cast<const uint16_t*>(q);
+  c.w = w;
+  c.q_seq = q_seq;
+  c.q_pos = q_pos;
+  c.nq = nq;
+  c.n_heads = n_heads;
+  c.head_dim = head_dim;
+  c.n_seq = n_seq;
+  c.h = n_screen_heads;
+  c.top_k = top_k;
+  c.l_max = l_max;
+  c.heads = at<int32_t>(workspace, p.heads);
+  c.cert = at<float>(workspace, p.cert);
+  c.lb_idx = at<int32_t>(workspace, p.lb_idx);
+  c.lb_score = at<float>(workspace, p.lb_score);
+  c.ub = at<float>(workspace, p.ub);
+  c.list = at<int32_t>(workspace, p.list);
+  c.cnt = at<uint32_t>(workspace, p.cnt);
+  if ((st = hip_status(timed(DSA_KERNEL_CERTIFY, stream,
+                             [&] { return dsa::launch_certify_heads(c, stream); }),
+                       "certify heads kernel", stream)))
+    return st;
+  // screening pass: the screened heads, ranked by lower bound, upper bounds stored
+  dsa::SelArgs a = stage_args(p.s0, workspace);
+  fill_common(a, q, w, k, q_seq, q_pos, nq, n_heads, head_dim, n_seq, l_max);
+  a.mode = dsa::MODE_RANGE;
+  a.heads = c.heads;
+  a.heads_stride = n_screen_heads;
+  a.h_use = n_screen_heads;
+  a.cert = c.cert;
+  a.ub = at<float>(workspace, p.ub);
+  a.ub_stride = l_max;
+  a.top_k = top_k;
+  a.out_idx = at<int32_t>(workspace, p.lb_idx);
+  a.out_score = at<float>(workspace, p.lb_score);
+  if ((st = hip_status(run_score_select(a, stream), "screening score/select kernel", stream)))
+    return st;
+  // survivors: upper bound at or above the k-th lower bound
+  if ((st = hip_status(timed(DSA_KERNEL_CERTIFY, stream,
+                             [&] { return dsa::launch_certify_compact(c, stream); }),
+                       "certify compact kernel", stream)))
+    return st;
+  // every head over the survivors
+  dsa::SelArgs b = stage_args(p.s1, workspace);
+  fill_common(b, q, w, k, q_seq, q_pos, nq, n_heads, head_dim, n_seq, l_max);
+  b.mode = dsa::MODE_LIST;
+  b.list = c.list;
+  b.list_len = (int)l_max;
+  b.list_count = reinterpret_cast<const int32_t*>(c.cnt);
+  b.top_k = top_k;
+  b.out_idx = out_idx;
+  b.out_score = out_score;
+  if ((st = hip_status(run_score_select(b, stream), "rescore/select kernel", stream))) return st;
+  if (!out_survivors) return DSA_OK;
+  c.out_survivors = out_survivors;
+  return hip_status(timed(DSA_KERNEL_CERTIFY, stream,
+                          [&] { return dsa::launch_certify_counts(c, stream); }),
+                    "certify counts kernel", stream);
 }
 
 }  // extern "C"

@@ -43,7 +43,40 @@ struct SelArgs {
   // outputs
   int32_t* out_idx;            // [nq, top_k]
   float* out_score;            // [nq, top_k] or null
+  // certified screening pass (RANGE mode over the screened heads): per query
+  // {N+, N-, M} of the heads left out; the selection key of every item is its
+  // lower bound, its upper bound goes to ub[t * ub_stride + item]
+  const float* cert;           // [nq, 4] or null
+  float* ub;                   // [nq, ub_stride]
+  int64_t ub_stride;
+  const int32_t* list_count;   // LIST: [nq] entries of each query's list, or null: list_len
 };
+
+// Certified exact top-k (bounds of the heads left out of a screening pass):
+// the screened heads of every query, the bounds, and the survivors.
+constexpr int kCertMaxHeads = 16;      // screened heads (the 16-row MFMA scorer)
+// relative error margin of the bounds (fp32 rounding of the screened score,
+// of the norms and of the full score is far below it)
+constexpr float kCertRel = 1.0f / 4096.0f;
+struct CertArgs {
+  const uint16_t* q;           // [nq, n_heads, head_dim] bf16
+  const float* w;              // [nq, n_heads]
+  const int32_t* q_seq;        // [nq] or null
+  const int32_t* q_pos;        // [nq]
+  int nq, n_heads, head_dim, n_seq, h, top_k;
+  int64_t l_max;
+  int32_t* heads;              // [nq, h] screened heads (largest |w_j| ||q_j||, ties: lower j)
+  float* cert;                 // [nq, 4] {N+, N-, M, 0}
+  const int32_t* lb_idx;       // [nq, top_k] the screening pass's selection by lower bound
+  const float* lb_score;       // [nq, top_k] its lower bounds
+  const float* ub;             // [nq, l_max] upper bounds
+  int32_t* list;               // [nq, l_max] survivors (first cnt[t] entries)
+  uint32_t* cnt;               // [nq] survivor counts (zeroed before the call)
+  int32_t* out_survivors;      // [nq] copy of cnt, or null
+};
+hipError_t launch_certify_heads(const CertArgs& a, hipStream_t stream);
+hipError_t launch_certify_compact(const CertArgs& a, hipStream_t stream);
+hipError_t launch_certify_counts(const CertArgs& a, hipStream_t stream);   // cnt -> out_survivors
 
 // A selection pass is the score-and-emit kernel followed by the merge kernel,
 // launched in that order on one stream.

@@ -142,6 +142,27 @@ struct ScorerMfma16 {
     }
     return ((lane_id() >> 4) & 1) ? p[1] : p[0];
   }
+
+  // squared norm of the key that score() returns the score of in this lane:
+  // its values are spread over the four lane groups (lanes m + 16 g)
+  DSA_DEVICE static float norm2(const Frag& b) {
+    float p[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      float x = 0.f;
+#pragma unroll
+      for (int s = 0; s < S; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float v = (float)b[c][s][e];
+          x = __builtin_fmaf(v, v, x);
+        }
+      x += shfl_xor_f(x, 16);
+      x += shfl_xor_f(x, 32);
+      p[c] = x;
+    }
+    return ((lane_id() >> 4) & 1) ? p[1] : p[0];
+  }
 };
 
 // float32 inputs on the vector ALUs (any H_use <= 64, D = 64 or 128): the

@@ -41,7 +41,10 @@ DSA_DEVICE Row row_of(const SelArgs& a, int t) {
   if (r.seq >= 0 && r.seq < a.n_seq && r.pos >= 0 && r.pos < a.l_max) {
     if (MODE == MODE_RANGE) r.n_items = r.pos + 1;
     else if (MODE == MODE_POOLED) r.n_items = (r.pos + a.block) / a.block;
-    else if (MODE == MODE_LIST) r.n_items = a.list_len;
+    else if (MODE == MODE_LIST)
+      r.n_items = a.list_count ? (a.list_count[t] < 0 ? 0
+                                  : (a.list_count[t] < a.list_len ? a.list_count[t] : a.list_len))
+                               : a.list_len;
     else r.n_items = (int64_t)a.list_len * a.block;
   }
   return r;
@@ -116,6 +119,25 @@ DSA_DEVICE void store_score(const SelArgs& a, int t, const Row& r, int64_t i0, i
   }
 }
 
+// Certified screening pass: the screened score s of the item this lane holds
+// and its key's norm |k| give the bounds of the full score,
+//   LB = s + |k| N- - e,  UB = s + |k| N+ + e,  e = kCertRel (|s| + |k| M)
+// (every head j left out adds w_j max(0, q_j . k) with 0 <= max(0, q_j . k)
+// <= |q_j| |k|, Cauchy-Schwarz); the item is ranked by LB and UB is stored.
+// A NaN bound ranks lowest (key 1), so it can only lower the threshold.
+DSA_DEVICE void cert_store(const SelArgs& a, int t, int64_t i0, int n_c, int tile, float s,
+                           float n2, const float (&cb)[3], uint32_t* skey) {
+  const int lane = lane_id();
+  const int j = tile * 32 + lane;
+  if (lane < 32 && j < n_c) {
+    const float nk = sqrtf(n2);
+    const float e = kCertRel * (fabsf(s) + nk * cb[2]);
+    const float lb = s + nk * cb[1] - e;
+    skey[j] = lb == lb ? score_to_key(lb) : 1u;
+    a.ub[(size_t)t * a.ub_stride + i0 + j] = s + nk * cb[0] + e;
+  }
+}
+
 // MISA head routing, finished by every workgroup of the routed pass: adds the
 // router's per-slice head sums in slice order, I_j = |w_j| * sum, and ranks the
 // heads by (I desc, j asc).  The order is fixed, so every workgroup of a query
@@ -149,7 +171,8 @@ DSA_DEVICE void route_heads(const SelArgs& a, int t, int32_t* s_heads, float* s_
 }
 
 // Kernel 1 of a selection pass: score one chunk of one query, emit candidates.
-template <class SC, int MODE>
+// CERT: the certified screening pass (ranked by lower bounds, see cert_store).
+template <class SC, int MODE, bool CERT>
 __global__ __launch_bounds__(kNT) void k_score_emit(SelArgs a) {
   extern __shared__ uint32_t smem[];
   uint32_t* skey = smem;
@@ -189,6 +212,15 @@ __global__ __launch_bounds__(kNT) void k_score_emit(SelArgs a) {
   const int n_c = (int)((r.n_items - i0) < a.chunk ? (r.n_items - i0) : a.chunk);
   const int n_tiles = (n_c + 31) / 32;
   const int wv = wave_id();
+  float cb[3] = {0.f, 0.f, 0.f};
+  if constexpr (CERT) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) cb[i] = a.cert[(size_t)t * 4 + i];
+  }
+  auto put = [&](int tl, const typename SC::Frag& f) {
+    if constexpr (CERT) cert_store(a, t, i0, n_c, tl, sc.score(f), SC::norm2(f), cb, skey);
+    else store_score<SC, MODE>(a, t, r, i0, n_c, tl, sc.score(f), skey);
+  };
   {
     // three tile fragments in rotation: while one tile is scored, the wave's
     // next two tiles are in flight.  The first two are requested before the
@@ -203,13 +235,13 @@ __global__ __launch_bounds__(kNT) void k_score_emit(SelArgs a) {
     for (; tile < n_tiles; tile += 3 * kNW) {
       const int t1 = tile + kNW, t2 = tile + 2 * kNW, t3 = tile + 3 * kNW, t4 = tile + 4 * kNW;
       if (t2 < n_tiles) load_tile<SC, MODE>(a, t, r, i0, n_c, t2, fc);
-      store_score<SC, MODE>(a, t, r, i0, n_c, tile, sc.score(fa), skey);
+      put(tile, fa);
       if (t1 >= n_tiles) break;
       if (t3 < n_tiles) load_tile<SC, MODE>(a, t, r, i0, n_c, t3, fa);
-      store_score<SC, MODE>(a, t, r, i0, n_c, t1, sc.score(fb), skey);
+      put(t1, fb);
       if (t2 >= n_tiles) break;
       if (t4 < n_tiles) load_tile<SC, MODE>(a, t, r, i0, n_c, t4, fb);
-      store_score<SC, MODE>(a, t, r, i0, n_c, t2, sc.score(fc), skey);
+      put(t2, fc);
     }
   }
   __syncthreads();
@@ -338,11 +370,11 @@ hipError_t launch_select_short_t(const SelArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <class SC, int MODE>
+template <class SC, int MODE, bool CERT = false>
 hipError_t launch_t(const SelArgs& a, hipStream_t stream) {
   if (a.n_chunks > kMaxChunks) return hipErrorInvalidValue;
   const size_t lds = score_select_lds_bytes(a.chunk, a.f32, a.head_dim);
-  auto k1 = k_score_emit<SC, MODE>;
+  auto k1 = k_score_emit<SC, MODE, CERT>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k1),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -402,6 +434,14 @@ hipError_t launch_merge(const SelArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_score_emit(const SelArgs& a, hipStream_t stream) {
+  if (a.cert) {                 // certified screening pass: bf16, prefix tokens, <= 16 heads
+    if (a.f32 || a.mode != MODE_RANGE || a.h_use < 1 || a.h_use > kCertMaxHeads || !a.ub ||
+        a.ub_stride < a.l_max)
+      return hipErrorInvalidValue;
+    if (a.head_dim == 128) return launch_t<ScorerMfma16<128>, MODE_RANGE, true>(a, stream);
+    if (a.head_dim == 64) return launch_t<ScorerMfma16<64>, MODE_RANGE, true>(a, stream);
+    return hipErrorInvalidValue;
+  }
   if (a.f32) {
     if (a.mode != MODE_RANGE) return hipErrorInvalidValue;
     if (a.head_dim == 64) return launch_t<ScorerF32<64>, MODE_RANGE>(a, stream);

@@ -123,6 +123,20 @@ def run_dense(A, tag, nq, H, d, n_seq, L, k, dtype=BF16, layout="decode", rng=No
     return A.finish(tag, st)
 
 
+def run_cert(A, tag, nq, H, d, n_seq, L, h, k, layout="decode", rng=None, invalid=0.0,
+             surv=True):
+    A.reset()
+    seq, pos = positions(layout, nq, n_seq, L, rng, invalid)
+    x = A.inputs(nq, H, d, n_seq, L, BF16, seq, pos)
+    ws = A.L.indexer_certified_topk_workspace_size(nq, H, d, n_seq, L, h, k)
+    st = A.L.indexer_certified_topk(x["q"], x["w"], x["k"], BF16, x["q_seq"], x["q_pos"], nq, H, d,
+                                    n_seq, L, h, k, A.buf(nq * k * 4, "out_idx"),
+                                    A.buf(nq * k * 4, "out_score"),
+                                    A.buf(nq * 4, "out_survivors") if surv else None,
+                                    A.buf(ws, "workspace"), ws, None)
+    return A.finish(tag, st)
+
+
 def run_misa(A, tag, nq, H, d, n_seq, L, B, h, kp, k, pooled=True, layout="decode", rng=None,
              invalid=0.0, outs=True):
     A.reset()
@@ -208,6 +222,8 @@ def workloads(A):
     run_iou(A, "iou 32 x 2048", 32, 2048)
     # dense decode, MISA / MISA dagger, tiny, prefill shapes, sparse attention
     run_dense(A, "dense C2", 64, 64, 128, 64, 131072, 2048)
+    run_cert(A, "certified C2, 16 screened heads", 64, 64, 128, 64, 131072, 16, 2048)
+    run_cert(A, "certified short rows (short passes)", 64, 64, 128, 64, 9000, 8, 2048)
     run_pool(A, "pool C4", 64, 131072, 128, 64)
     run_misa(A, "misa C4", 64, 64, 128, 64, 131072, 64, 8, 0, 2048)
     run_misa(A, "misa dagger C4", 64, 64, 128, 64, 131072, 64, 8, 8192, 2048)
@@ -271,6 +287,10 @@ def sweep(A, n, seed):
             run_mla(A, tag + f" mla H={Hm} k={km}", nq, Hm, n_seq, L, km, layout=layout, rng=rng,
                     invalid=inv)
         run_iou(A, tag + " iou", nq, min(k, 8192))
+        if H <= 64:
+            hc = int(rng.integers(1, min(H, 16) + 1))
+            run_cert(A, tag + f" certified h={hc}", nq, H, d, n_seq, L, hc, k, layout=layout,
+                     rng=rng, invalid=inv, surv=bool(rng.random() < 0.7))
 
 
 def planted(A):
@@ -304,6 +324,9 @@ def planted(A):
     run("prefill", "workspace", 16,       # (the last row's metadata word 3 is unused)
         lambda: run_dense(A, "p", 32768, 64, 128, 1, 32768, 2048, layout="prefill",
                           with_seq=False))
+    cert = lambda: run_cert(A, "p", 64, 64, 128, 64, 131072, 16, 2048)
+    for victim in ("k", "q", "w", "out_idx", "out_score", "out_survivors", "workspace"):
+        run("certified C2", victim, 4, cert)
     run("sparse attention", "kv", 2, lambda: run_mla(A, "p", 64, 128, 64, 131072, 2048))
     run("sparse attention", "workspace", 4, lambda: run_mla(A, "p", 64, 128, 64, 131072, 2048))
     return missed

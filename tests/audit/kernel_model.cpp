@@ -139,7 +139,7 @@ int64_t n_items_of(const dsa::SelArgs& a, const QRow& r) {
   switch (a.mode) {
     case dsa::MODE_RANGE: return r.pos + 1;
     case dsa::MODE_POOLED: return (r.pos + a.block) / a.block;
-    case dsa::MODE_LIST: return a.list_len;
+    case dsa::MODE_LIST: return a.list_len;   // (a per-query count is clamped to list_len)
     default: return (int64_t)a.list_len * a.block;
   }
 }
@@ -189,6 +189,9 @@ hipError_t launch_score_emit(const SelArgs& a, hipStream_t) {
   begin(a.store_all ? "k_score_emit(store_all)" : "k_score_emit");
   if (a.n_chunks > kMaxChunks) return hipErrorInvalidValue;
   if (a.f32 && a.mode != MODE_RANGE) return hipErrorInvalidValue;
+  if (a.cert && (a.f32 || a.mode != MODE_RANGE || a.h_use < 1 || a.h_use > kCertMaxHeads || !a.ub ||
+                 a.ub_stride < a.l_max))
+    return hipErrorInvalidValue;
   const size_t eb = a.f32 ? 4 : 2;
   for (int t = 0; t < a.nq; ++t) {
     const QRow r = qrow(a.q_seq, a.q_pos, t, a.n_seq, a.l_max);
@@ -209,12 +212,17 @@ hipError_t launch_score_emit(const SelArgs& a, hipStream_t) {
       if (a.out_heads) touch_elems(a.out_heads, (int64_t)t * a.h_use, (int64_t)(t + 1) * a.h_use, "out_heads");
       if (a.out_importance) touch_elems(a.out_importance, (int64_t)t * a.n_heads, (int64_t)(t + 1) * a.n_heads, "out_importance");
     }
+    if (a.mode == MODE_LIST && a.list_count)
+      touch_elems(a.list_count, t, t + 1, "list count");
     scorer_init(a.q, eb, a.w, t, a.n_heads, a.head_dim, a.h_use, a.route_part ? nullptr : a.heads,
                 a.heads_stride);
+    if (a.cert) touch_elems(a.cert, (int64_t)t * 4, (int64_t)t * 4 + 3, "bounds");
     for (int c = 0; c < std::min<int64_t>(n_chunks_t, a.n_chunks); ++c) {
       const int64_t i0 = (int64_t)c * a.chunk;
       const int64_t n_c = std::min<int64_t>(n_items - i0, a.chunk);
       items_rows(a, t, r, i0, n_c);
+      if (a.cert) touch_elems(a.ub, (int64_t)t * a.ub_stride + i0, (int64_t)t * a.ub_stride + i0 + n_c,
+                              "upper bounds");
       const int64_t seg = ((int64_t)t * a.n_chunks + c) * a.chunk;
       touch_elems(a.cand, seg, seg + n_c, "candidate segment");
       if (!a.store_all) {
@@ -242,6 +250,46 @@ hipError_t launch_merge(const SelArgs& a, hipStream_t) {
     touch_elems(a.out_idx, (int64_t)t * a.top_k, (int64_t)(t + 1) * a.top_k, "out_idx");
     if (a.out_score) touch_elems(a.out_score, (int64_t)t * a.top_k, (int64_t)(t + 1) * a.top_k, "out_score");
   }
+  return hipSuccess;
+}
+
+hipError_t launch_certify_heads(const CertArgs& a, hipStream_t) {
+  begin("k_certify_heads");
+  if (a.nq < 1 || a.n_heads < 1 || a.n_heads > 64 || a.h < 1 || a.h > a.n_heads ||
+      (a.head_dim != 64 && a.head_dim != 128))
+    return hipErrorInvalidValue;
+  for (int t = 0; t < a.nq; ++t) {
+    touch_elems(a.q, (int64_t)t * a.n_heads * a.head_dim, (int64_t)(t + 1) * a.n_heads * a.head_dim,
+                "q rows");
+    touch_elems(a.w, (int64_t)t * a.n_heads, (int64_t)(t + 1) * a.n_heads, "w");
+    touch_elems(a.heads, (int64_t)t * a.h, (int64_t)(t + 1) * a.h, "screened heads");
+    touch_elems(a.cert, (int64_t)t * 4, (int64_t)t * 4 + 4, "bounds");
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_certify_compact(const CertArgs& a, hipStream_t) {
+  begin("k_certify_compact");
+  if (a.nq < 1 || a.top_k < 1 || a.l_max < 1) return hipErrorInvalidValue;
+  if ((a.l_max + 4095) / 4096 > 65535) return hipErrorInvalidValue;
+  for (int t = 0; t < a.nq; ++t) {
+    const QRow r = qrow(a.q_seq, a.q_pos, t, a.n_seq, a.l_max);
+    if (!r.ok) continue;
+    touch_elems(a.lb_idx, (int64_t)t * a.top_k, (int64_t)(t + 1) * a.top_k, "screening selection");
+    touch_elems(a.lb_score, (int64_t)t * a.top_k, (int64_t)(t + 1) * a.top_k, "lower bounds");
+    touch_elems(a.ub, (int64_t)t * a.l_max, (int64_t)t * a.l_max + r.pos + 1, "upper bounds");
+    touch_elems(a.cnt, t, t + 1, "survivor count");
+    // at most every key of the prefix survives
+    touch_elems(a.list, (int64_t)t * a.l_max, (int64_t)t * a.l_max + r.pos + 1, "survivor list");
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_certify_counts(const CertArgs& a, hipStream_t) {
+  begin("k_certify_counts");
+  if (a.nq < 1 || !a.out_survivors) return hipErrorInvalidValue;
+  touch_elems(a.cnt, 0, a.nq, "survivor counts");
+  touch_elems(a.out_survivors, 0, a.nq, "out_survivors");
   return hipSuccess;
 }
 

@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(lib):
     missing = [n for n in _declared() if not hasattr(lib, n)]
     assert not missing, missing
     assert set(_declared()) <= set(dsa._SIGS)
-    assert lib.dsa_abi_version() == 2
+    assert lib.dsa_abi_version() == 3
 
 
 def test_workspace_sizes_are_positive_and_monotone(lib):
@@ -159,7 +159,7 @@ def test_hisa_wait_limit_hook(lib):
     GPU (it only sets the limit later calls pass to the kernel)."""
     assert lib.dsa_hisa_wait_limit(0) == 0
     assert lib.dsa_hisa_wait_limit(-1) == 0          # back to the default
-    assert lib.dsa_abi_version() == 2
+    assert lib.dsa_abi_version() == 3
 
 
 def test_noalloc_rejects_calls_beyond_its_scratch_before_any_device_work(lib):

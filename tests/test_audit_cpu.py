@@ -77,5 +77,5 @@ def test_every_kernel_access_stays_inside_its_buffers(audit_lib):
     for k in ("k_score_emit", "k_score_emit(store_all)", "k_merge", "k_select_short", "k_prepare",
               "k_mean_pool", "k_route", "k_route_rows", "k_route_prefill", "k_route_heads",
               "k_pool_prefix", "k_prefill_score", "k_prefill_routed_score", "k_prefill_select",
-              "k_hisa", "k_iou", "k_sparse_mla"):
+              "k_hisa", "k_iou", "k_sparse_mla", "k_certify_heads", "k_certify_compact"):
         assert res["launches"].get(k, 0) > 0, k
