@@ -719,7 +719,10 @@ def main() -> int:
                  "tflop_per_s": call_flops / (ms_per_step * 1e-3) / 1e12,
                  "hbm_frac": call_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
                  "pair_scores_per_s": pairs / (ms_per_step * 1e-3),
-                 "head_dots_per_s": call_flops / (2 * d) / (ms_per_step * 1e-3)},
+                 "head_dots_per_s": call_flops / (2 * d) / (ms_per_step * 1e-3),
+                 # the whole call's flops against the bf16 MFMA peak (next to the
+                 # dominant kernel's fraction in roofline.frac)
+                 "mfma_frac": call_flops / (ms_per_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
         "cold_cache": (args.flush + " 512 MiB") if flush is not None else False,
         "kernel_avg_us": per_kernel,
         "roofline": roofline,
