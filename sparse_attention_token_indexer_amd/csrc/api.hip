@@ -124,6 +124,7 @@ constexpr int kBins = 4096;
 constexpr int kMaxChunk = 8192;
 constexpr int kMinChunk = 256;
 constexpr int64_t kTargetWorkgroups = 512;   // >= 2 per compute unit on MI355X
+constexpr int64_t kComputeUnits = 256;       // MI355X
 constexpr size_t kMaxLds = 64 * 1024;
 constexpr int64_t kMaxItems = (int64_t)kMaxChunk * dsa::kMaxChunks;   // per query and pass
 constexpr int kMaxTopK = 1 << 20;
@@ -1293,7 +1294,10 @@ struct MlaPlan {
 MlaPlan plan_mla(int64_t nq, int n_heads, int top_k) {
   MlaPlan p;
   const int64_t tiles = cdiv(top_k, dsa::kMlaTile);
-  int64_t splits = std::max<int64_t>(1, cdiv(kTargetWorkgroups / 2, nq));
+  // about one workgroup per compute unit: a workgroup takes one (query,
+  // slice) and 64 heads (32 when 64 does not divide n_heads)
+  const int64_t head_blocks = n_heads % 64 == 0 ? n_heads / 64 : n_heads / 32;
+  int64_t splits = std::max<int64_t>(1, cdiv(kComputeUnits, nq * head_blocks));
   splits = std::min<int64_t>({splits, tiles, dsa::kMlaMaxSplits});
   splits = std::max<int64_t>(splits, cdiv(tiles, dsa::kMlaMaxTiles));
   p.tiles_per_split = (int)cdiv(tiles, splits);

@@ -12,7 +12,6 @@ constexpr int kMlaTile = 32;     // selected rows per step
 constexpr int kMlaMaxSplits = 16;
 constexpr int kMlaMaxTiles = 64;     // steps per slice (the slice's row ids stay in LDS)
 constexpr int kMlaMaxTopK = kMlaMaxSplits * kMlaMaxTiles * kMlaTile;
-constexpr int kMlaQLds = 8;          // k-steps of each wave's query rows kept in LDS
 
 struct MlaArgs {
   const uint16_t* q;       // [nq, n_heads, kMlaDqk] bf16
@@ -30,15 +29,14 @@ struct MlaArgs {
   float2* part_ml;         // [nq, splits, n_heads] (running max in log2 units, sum)
 };
 
-// LDS of the attention kernel: the step's rows (padded), their value part
-// transposed (padded), the last kMlaQLds k-steps of every wave's query rows
-// (padded), and the slice's row ids.
-constexpr int kMlaCRow = kMlaDqk * 2 + 16;        // bytes per staged row
-constexpr int kMlaVRow = kMlaTile * 2 + 8;        // bytes per transposed value row (18 banks:
-                                                  // 16 consecutive rows hit distinct bank pairs)
-constexpr int kMlaQRow = kMlaQLds * 64 + 16;      // bytes per query row kept in LDS
+// LDS of the attention kernel: three steps of staged rows (32 rows of
+// kMlaDqk bf16 each, unpadded: the rows' chunks are swizzled instead), the
+// partial score blocks of its waves (4 KiB per wave: 2 per group of 32 heads,
+// two groups when 64 divides n_heads), a flag word (and padding), and the
+// slice's row ids.
 inline size_t mla_lds_bytes(int n_heads, int tiles_per_split) {
-  return (size_t)kMlaTile * kMlaCRow + (size_t)kMlaDv * kMlaVRow + (size_t)n_heads * kMlaQRow +
+  const int waves = n_heads % 64 == 0 ? 4 : 2;
+  return (size_t)3 * kMlaTile * kMlaDqk * 2 + (size_t)waves * 4096 + 16 +
          (size_t)tiles_per_split * kMlaTile * 4;
 }
 

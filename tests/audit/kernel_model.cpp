@@ -621,7 +621,7 @@ hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t) {
       a.n_heads % 32 || a.splits < 1 || a.splits > kMlaMaxSplits || a.tiles_per_split < 1 ||
       a.tiles_per_split > kMlaMaxTiles ||
       (int64_t)a.splits * a.tiles_per_split * kMlaTile < a.top_k ||
-      (int64_t)a.nq * a.splits > 0x7FFFFFFF ||
+      (int64_t)a.nq * a.splits > 0x3FFFFFF ||
       mla_lds_bytes(a.n_heads, a.tiles_per_split) > 160 * 1024 ||
       (a.splits > 1 && (!a.part_o || !a.part_ml)))
     return hipErrorInvalidValue;

@@ -118,10 +118,11 @@ def test_sparse_attention_rejects_bad_arguments(lib):
 
 
 def test_sparse_attention_workspace_sizes(lib):
-    # 64 queries x 128 heads x 2048 rows: 2 head groups do not change the
-    # slices; 4 slices of 16 steps, bf16 slice outputs and (max, sum) pairs
+    # 64 queries x 128 heads x 2048 rows: two 64-head workgroups per (query,
+    # slice), so 2 slices of 32 steps fill 256 compute units; bf16 slice
+    # outputs and (reference, sum) pairs
     n = dsa.sparse_mla_workspace_size(64, 128, 576, 512, 2048)
-    assert n == 64 * 4 * 128 * 512 * 2 + 64 * 4 * 128 * 8
+    assert n == 64 * 2 * 128 * 512 * 2 + 64 * 2 * 128 * 8
     assert dsa.sparse_mla_workspace_size(256, 128, 576, 512, 2048) == 0   # one slice each
     assert dsa.sparse_mla_workspace_size(2, 32, 576, 512, 16) == 0        # one step
     assert dsa.sparse_mla_workspace_size(2, 32, 576, 512, 32769) == 0     # unsupported
