@@ -128,6 +128,40 @@ def test_mla_after_the_indexer(dsa):
     _case(dsa, wl, seed=6, idx=idx, what="mla after indexer")
 
 
+def test_mla_score_far_above_the_first_steps(dsa):
+    """A listed row whose score for some heads exceeds everything before it
+    in its slice by far more than the kernel's fixed softmax reference allows
+    (the row is 8 times one head's query row, a score near 8 |q|^2), placed
+    after the first step of its slice: the kernel redoes the slice with the
+    slice's largest score as the reference, and the result must meet the same
+    bound against the oracle."""
+    wl = M.WORKLOADS["sparse_mla_decode_L128K_H128"].replace(
+        nq=4, n_seq=1, l_max=4096, n_heads=128, top_k=2048, layout="tail")
+    q = M.queries(wl, 11)
+    C = M.cache(wl, 11).copy()
+    qs, qp = M.positions(wl)
+    idx = M.index_lists(wl, 11)
+    qf = datagen.bf16_bits_to_f32(q)
+    # entries 100 and 1500: step 3 of the first 128-entry slice and step 2 of
+    # the twelfth (the call splits each list into 16 slices of 4 steps)
+    for t in range(wl.nq):
+        for j, h in ((100, 5), (1500, 77)):
+            C[int(qs[t]), int(idx[t, j])] = datagen.f32_to_bf16_bits(8.0 * qf[t, h])
+    say(f"[mla far scores] nq={wl.nq} L={wl.l_max} H={wl.n_heads} k={wl.top_k}")
+    out = dsa.sparse_mla_attention(_bf16(q), _bf16(C), torch.from_numpy(qp).cuda(),
+                                   torch.from_numpy(idx).cuda(), torch.from_numpy(qs).cuda(),
+                                   softmax_scale=wl.scale)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy().astype(np.float64)
+    _check_rows(o, q, lambda s, p: _f64(C[s, :p + 1]), idx, qs, qp, wl, range(wl.nq),
+                "mla far scores")
+    # the planted heads attend almost only to their row
+    for t in range(wl.nq):
+        for j, h in ((100, 5), (1500, 77)):
+            row = _f64(C[int(qs[t]), int(idx[t, j])])[:wl.d_v]
+            assert np.abs(o[t, h] - row).max() < 2.0 ** -6 * np.abs(row).max() + 1e-3
+
+
 def test_mla_full_size_sampled_queries(dsa):
     """64 queries x 128 heads over their own 131072-row caches, k = 2048, as
     timed: the rows the lists name are generated and placed in a zeroed cache
