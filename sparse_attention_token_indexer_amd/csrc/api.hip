@@ -240,8 +240,29 @@ int prefill_key_chunk(int64_t nq, int64_t l_max, int rows_per_group = 8) {
   return (int)((((l_max + chunks - 1) / chunks) + 127) / 128 * 128);
 }
 
+// (key-split rows: each row's counters, its parts' histograms and its
+// threshold-bin buffer, for the select)
+int row_parts(int64_t l_max) { return (int)((l_max + dsa::kRowPartKeys - 1) / dsa::kRowPartKeys); }
+struct RowSelectPlan {
+  size_t ctl = 0, parthist = 0, ties = 0;
+};
+RowSelectPlan plan_row_select(Arena& A, int64_t nq, int64_t l_max) {
+  RowSelectPlan r;
+  r.ctl = A.take((size_t)nq * dsa::kRowCtlWords * 4);
+  r.parthist = A.take((size_t)nq * row_parts(l_max) * (kBins / 2) * 4);
+  r.ties = A.take((size_t)nq * dsa::kRowTieCap * 8);
+  return r;
+}
+void set_row_select(dsa::PrefillArgs& pa, const RowSelectPlan& r, void* ws) {
+  pa.rowctl = at<uint32_t>(ws, r.ctl);
+  pa.parthist = at<uint32_t>(ws, r.parthist);
+  pa.row_parts = row_parts(pa.l_max);
+  pa.ties = at<uint2>(ws, r.ties);
+}
+
 struct PrefillPlan {
   size_t scores = 0, rowmeta = 0, total = 0;
+  RowSelectPlan rs;
 };
 
 // score rows span whole 128-key stages (the scorers store every key of a
@@ -253,6 +274,7 @@ PrefillPlan plan_prefill(int64_t nq, int64_t l_max) {
   Arena A;
   p.scores = A.take((size_t)(nq + 1) * prefill_row_stride(l_max) * 4);
   p.rowmeta = A.take((size_t)nq * 16);
+  if (prefill_key_chunk(nq, l_max) > 0) p.rs = plan_row_select(A, nq, l_max);
   p.total = A.off;
   return p;
 }
@@ -577,6 +599,7 @@ bool use_misa_prefill(int32_t dtype, int64_t nq, int n_seq, int64_t l_max, int h
 
 struct MisaPrefillPlan {
   size_t part = 0, heads = 0, prefix = 0, pooled = 0, scores = 0, rowmeta = 0, total = 0;
+  RowSelectPlan rs;
   int splits = 1, bps = 1;
   int64_t m_max = 0, row_stride = 0;
 };
@@ -595,6 +618,7 @@ MisaPrefillPlan plan_misa_prefill(int64_t nq, int n_heads, int head_dim, int n_s
   p.row_stride = prefill_row_stride(l_max);
   p.scores = A.take((size_t)(nq + 1) * p.row_stride * 4);
   p.rowmeta = A.take((size_t)nq * 16);
+  if (prefill_key_chunk(nq, l_max, 32) > 0) p.rs = plan_row_select(A, nq, l_max);
   p.total = A.off;
   return p;
 }
@@ -679,6 +703,7 @@ int misa_prefill(const void* q, const float* w, const void* k, const void* k_poo
   pa.rowmeta = at<int32_t>(workspace, p.rowmeta);
   pa.key_chunk = prefill_key_chunk(nq, l_max, 32);
   pa.bin_bits = pa.key_chunk ? 12 : 10;
+  if (pa.key_chunk) set_row_select(pa, p.rs, workspace);
   pa.heads = rh.heads;
   pa.heads_stride = rh.heads_stride;
   pa.h_use = h;
@@ -787,6 +812,7 @@ int dense_call(const void* q, const float* w, const void* k, int32_t dtype, cons
     pa.rowmeta = at<int32_t>(workspace, pp.rowmeta);
     pa.key_chunk = prefill_key_chunk(nq, l_max);
     pa.bin_bits = pa.key_chunk ? 12 : prefill_bin_bits(l_max);   // first-level bins of the rows
+    if (pa.key_chunk) set_row_select(pa, pp.rs, workspace);
     pa.out_idx = out_idx;
     pa.out_score = out_score;
     st = hip_status(timed(DSA_KERNEL_PREFILL, stream,

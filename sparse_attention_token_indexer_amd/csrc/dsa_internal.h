@@ -145,16 +145,33 @@ struct PrefillArgs {
   int32_t* rowmeta;            // [nq, 4] workspace: threshold bin, count above, count in bin
   int bin_bits;                // first-level histogram bits (dense: 12 up to 65535 keys per
                                // row, 11 beyond; routed: 10)
-  int key_chunk;               // dense only: > 0 splits every row's keys into chunks of this
-                               // many (a multiple of 128), one workgroup per (row group, chunk),
-                               // and the select kernel counts the rows itself (12-bit bins)
+  int key_chunk;               // > 0 splits every row's keys into chunks of this many (a
+                               // multiple of 128), one workgroup per (row group, chunk), and
+                               // the select counts the rows itself (12-bit bins, parthist)
   const int32_t* heads;        // routed pass: [nq, heads_stride] head ids (first h_use used)
   int heads_stride, h_use;
   float* spare_row;            // [row_stride] scratch row taking the stores of rows that are
                                // not scored
+  uint32_t* rowctl;            // key_chunk > 0: [nq, kRowCtlWords] the select's counters per
+                               // row
+  uint32_t* parthist;          // key_chunk > 0: [nq, row_parts, kBins / 2] each part's 12-bit
+                               // histogram (16-bit counts)
+  int row_parts;               // parts of kRowPartKeys keys per row (l_max rounded up)
+  uint2* ties;                 // key_chunk > 0: [nq, kRowTieCap] entries of each row's
+                               // threshold bin
   int32_t* out_idx;
   float* out_score;
 };
+// Select of rows whose keys were split over workgroups: every row in parts of
+// kRowPartKeys keys, one workgroup each, in four kernels (count, threshold,
+// emission, finish) whose boundaries carry the data between workgroups; per
+// row kRowCtlWords words: [emitted entries, threshold bin entries, threshold
+// bin, count above it, count in it] and padding, written by the threshold
+// kernel.
+constexpr int kRowPartKeys = 8192;
+constexpr int kRowCtlWords = 8;
+constexpr int kRowTieCap = 2048;
+enum : int { RH_EMIT = 0, RH_TIES, RH_BSTAR, RH_ABOVE, RH_NB };
 hipError_t launch_prefill_score(const PrefillArgs& a, hipStream_t stream);
 // MISA on the prefill shape: rows scored with their h_use <= 8 routed heads,
 // four rows per 32-row MFMA tile; 10-bit per-row histograms.

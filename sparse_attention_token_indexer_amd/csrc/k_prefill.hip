@@ -18,8 +18,14 @@
 // When there are too few row groups to fill the chip (decode queries sharing
 // one cache, a short chunk of a long prefill), the keys are split as well:
 // workgroup (g, c) scores its rows over key chunk c only, keeps no histogram
-// (two workgroups then share a compute unit) and the select kernel finds each
-// row's threshold itself with one more pass over the stored row.
+// (two workgroups then share a compute unit), and the row select splits each
+// stored row into parts of 8192 keys: k_rows_count (one workgroup per part:
+// the part's 12-bit histogram), k_rows_threshold (one per row: the parts'
+// sum and the k-th key's bin), k_rows_emit (one per part: keys above the bin
+// to the output, keys in it to a tie buffer) and k_rows_finish (one per row:
+// the tie bin resolved exactly).  Kernel boundaries order the four; an
+// agent-scope fence inside a kernel would write back and invalidate the whole
+// L2 once per workgroup on this chip.
 // k_prefill_select: one workgroup per row emits every score above that bin and
 // resolves the bin itself exactly (radix digits over (score, ~index)).
 #include "dsa_internal.h"
@@ -307,19 +313,15 @@ struct RowSource {
   }
 };
 
-// FB: first-level bins of the rows' histograms (rowmeta); SELF: the scoring
-// kernel kept no histogram (keys split across workgroups), this kernel counts
-// each row's scores in 12-bit bins itself first.
-template <int FB, bool SELF, int NT>
+// FB: first-level bins of the rows' histograms (rowmeta).
+template <int FB, int NT>
 __global__ __launch_bounds__(NT) void k_prefill_select(PrefillArgs a) {
-  static_assert(!SELF || FB == 12, "rows counted here use 12-bit bins");
   constexpr int kFBShift = 32 - FB;
   extern __shared__ __align__(16) uint8_t smem[];
   uint2* list = reinterpret_cast<uint2*>(smem);                          // [kSelListCap]
   uint2* tie = list + kSelListCap;                                        // [64]
   uint32_t* hist = reinterpret_cast<uint32_t*>(tie + 64);                 // [1024]
   uint32_t* scratch = hist + 1024;                                        // [64]
-  uint32_t* hist1 = scratch + 64;                                         // [4096] (SELF)
   __shared__ uint32_t s_out, s_ln;
   const int t = (int)gridDim.x - 1 - (int)blockIdx.x;          // longest rows first
   int pos = -1;
@@ -345,8 +347,7 @@ __global__ __launch_bounds__(NT) void k_prefill_select(PrefillArgs a) {
     }
     return;
   }
-  // (few long rows when SELF: more loads in flight per thread)
-  constexpr int U = SELF ? 8 : 4;
+  constexpr int U = 4;
   const uint32_t n4 = (n + 3) / 4;
   auto load_iter = [&](uint32_t base, auto& v) {
     constexpr int UU = sizeof(v) / sizeof(v[0]);
@@ -359,26 +360,7 @@ __global__ __launch_bounds__(NT) void k_prefill_select(PrefillArgs a) {
   };
   int bstar;
   uint32_t above, nb;
-  if constexpr (SELF) {
-    // the row's 12-bit histogram from its stored scores, then the k-th bin
-    constexpr int UH = 16;
-    for (int i = threadIdx.x; i < (1 << FB); i += NT) hist1[i] = 0u;
-    __syncthreads();
-    for (uint32_t base = 0; base < n4; base += NT * UH) {
-      f32x4 v[UH];
-      load_iter(base, v);
-#pragma unroll
-      for (int j = 0; j < UH; ++j) {
-        const uint32_t i4 = base + threadIdx.x + j * NT;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (i4 < n4 && 4 * i4 + e < n) atomicAdd(&hist1[fast_key(v[j][e]) >> kFBShift], 1u);
-      }
-    }
-    __syncthreads();
-    bstar = block_find_threshold<NT>(hist1, 1 << FB, Kt, scratch, &above);
-    nb = hist1[bstar];
-  } else {
+  {
     const int32_t* meta = a.rowmeta + (size_t)t * 4;
     bstar = meta[0];
     above = (uint32_t)meta[1];
@@ -515,6 +497,231 @@ __global__ __launch_bounds__(NT) void k_prefill_select(PrefillArgs a) {
   }
 }
 
+// ---- select of key-split rows: every row in parts of kRowPartKeys scores,
+// one 256-thread workgroup per (part, row).
+constexpr int kRT = 256;
+
+DSA_DEVICE int row_pos(const PrefillArgs& a, int t) {   // the row's last key, or -1
+  const int seq = a.q_seq ? a.q_seq[t] : 0;
+  const int p = a.q_pos[t];
+  return (seq == 0 && p >= 0 && (int64_t)p < a.l_max) ? p : -1;
+}
+
+// A part's scores (16-byte loads, all issued first; the part starts on a
+// multiple of 4 and the row stride covers the last piece).
+template <int U>
+DSA_DEVICE void load_part(const float* sc, uint32_t u0, uint32_t u1, f32x4 (&v)[U]) {
+#pragma unroll
+  for (int j = 0; j < U; ++j) {
+    const uint32_t i4 = (u0 >> 2) + threadIdx.x + j * kRT;
+    v[j] = 4 * i4 < u1 ? *reinterpret_cast<const f32x4*>(sc + 4 * (size_t)i4) : f32x4{0, 0, 0, 0};
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Count: each part of a row longer than top_k stores its 12-bit histogram
+// (16-bit counts, plain stores: the next kernel reads them).
+__global__ __launch_bounds__(kRT) void k_rows_count(PrefillArgs a) {
+  __shared__ uint32_t hist[kBins];
+  const int t = (int)blockIdx.y, p = (int)blockIdx.x, tid = (int)threadIdx.x;
+  const int pos = row_pos(a, t);
+  const uint32_t n = (uint32_t)pos + 1u;
+  if (pos < 0 || n <= (uint32_t)a.top_k) return;
+  const uint32_t parts = (n + kRowPartKeys - 1) / kRowPartKeys;
+  if ((uint32_t)p >= parts) return;
+  for (int i = tid; i < kBins; i += kRT) hist[i] = 0u;
+  __syncthreads();
+  const float* sc = a.scores + (size_t)t * (size_t)a.row_stride;
+  const uint32_t u0 = (uint32_t)p * kRowPartKeys, u1 = min(n, u0 + kRowPartKeys);
+  constexpr int U = kRowPartKeys / 4 / kRT;
+  f32x4 v[U];
+  load_part<U>(sc, u0, u1, v);
+#pragma unroll
+  for (int j = 0; j < U; ++j) {
+    const uint32_t i4 = (u0 >> 2) + tid + j * kRT;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (4 * i4 + e < u1) atomicAdd(&hist[fast_key(v[j][e]) >> kBinShift], 1u);
+  }
+  __syncthreads();
+  // thread i: bins 16 i .. 16 i + 15, as 8 words of two 16-bit counts
+  static_assert(kBins == 16 * kRT && kRowPartKeys < 65536, "16 bins per thread, 16-bit counts");
+  uint32_t* ph = a.parthist + ((size_t)t * a.row_parts + p) * (kBins / 2) + 8 * tid;
+  u32x4 w0, w1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    w0[i] = hist[16 * tid + 2 * i] | (hist[16 * tid + 2 * i + 1] << 16);
+    w1[i] = hist[16 * tid + 8 + 2 * i] | (hist[16 * tid + 8 + 2 * i + 1] << 16);
+  }
+  *reinterpret_cast<u32x4*>(ph) = w0;
+  *reinterpret_cast<u32x4*>(ph + 4) = w1;
+}
+
+// Threshold: one workgroup per row adds its parts' histograms (every load of
+// up to 16 parts in flight at once) and finds the bin of the row's k-th best
+// key and the count above it; it also clears the emission's counters.  Rows
+// of at most top_k keys keep every key.
+constexpr int kRowT = 1024;                     // threads of the per-row kernels
+__global__ __launch_bounds__(kRowT) void k_rows_threshold(PrefillArgs a) {
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t scratch[64];
+  const int t = (int)blockIdx.x, tid = (int)threadIdx.x;
+  const int pos = row_pos(a, t);
+  if (pos < 0) return;                          // (the finish pads the row)
+  const uint32_t n = (uint32_t)pos + 1u;
+  uint32_t* rc = a.rowctl + (size_t)t * kRowCtlWords;
+  if (n <= (uint32_t)a.top_k) {
+    if (tid == 0) {
+      rc[RH_EMIT] = 0u;
+      rc[RH_TIES] = 0u;
+      rc[RH_BSTAR] = 0xFFFFFFFFu;               // every bin is above
+      rc[RH_ABOVE] = n;
+      rc[RH_NB] = 0u;
+    }
+    return;
+  }
+  const uint32_t parts = (n + kRowPartKeys - 1) / kRowPartKeys;
+  // thread i: bins 4 i .. 4 i + 3, one word pair of 16-bit counts per part
+  static_assert(kBins == 4 * kRowT, "4 bins per thread");
+  const uint2* ph0 = reinterpret_cast<const uint2*>(a.parthist + (size_t)t * a.row_parts * (kBins / 2)) + tid;
+  uint32_t s0 = 0, s1 = 0, s2 = 0, s3 = 0;
+  for (uint32_t q0 = 0; q0 < parts; q0 += 16) {
+    uint2 x[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+      x[q] = q0 + q < parts ? ph0[(size_t)(q0 + q) * (kBins / 4)] : make_uint2(0u, 0u);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      s0 += x[q].x & 0xFFFFu;
+      s1 += x[q].x >> 16;
+      s2 += x[q].y & 0xFFFFu;
+      s3 += x[q].y >> 16;
+    }
+  }
+  hist[4 * tid] = s0;
+  hist[4 * tid + 1] = s1;
+  hist[4 * tid + 2] = s2;
+  hist[4 * tid + 3] = s3;
+  __syncthreads();
+  uint32_t above;
+  const int bstar = block_find_threshold<kRowT>(hist, kBins, (uint32_t)a.top_k, scratch, &above);
+  if (tid == 0) {
+    rc[RH_EMIT] = 0u;
+    rc[RH_TIES] = 0u;
+    rc[RH_BSTAR] = (uint32_t)bstar;
+    rc[RH_ABOVE] = above;
+    rc[RH_NB] = hist[bstar];
+  }
+}
+
+// Emission: every part writes its keys above the threshold bin to the output
+// and those in the bin to the row's tie buffer (up to its capacity), at slots
+// reserved with one atomic per wave.
+__global__ __launch_bounds__(kRT) void k_rows_emit(PrefillArgs a) {
+  const int t = (int)blockIdx.y, p = (int)blockIdx.x, tid = (int)threadIdx.x, lane = lane_id();
+  const int pos = row_pos(a, t);
+  if (pos < 0) return;
+  const uint32_t n = (uint32_t)pos + 1u;
+  const uint32_t parts = (n + kRowPartKeys - 1) / kRowPartKeys;
+  if ((uint32_t)p >= parts) return;
+  const uint32_t Kt = n < (uint32_t)a.top_k ? n : (uint32_t)a.top_k;
+  uint32_t* rc = a.rowctl + (size_t)t * kRowCtlWords;
+  const int bstar = (int)rc[RH_BSTAR];          // -1: every key is selected
+  int32_t* out_i = a.out_idx + (size_t)t * a.top_k;
+  float* out_s = a.out_score ? a.out_score + (size_t)t * a.top_k : nullptr;
+  const float* sc = a.scores + (size_t)t * (size_t)a.row_stride;
+  uint2* ties = a.ties + (size_t)t * kRowTieCap;
+  const uint32_t u0 = (uint32_t)p * kRowPartKeys, u1 = min(n, u0 + kRowPartKeys);
+  constexpr int U = kRowPartKeys / 4 / kRT;
+  f32x4 v[U];
+  load_part<U>(sc, u0, u1, v);
+  uint32_t take_m = 0, tie_m = 0;               // bit 4 j + e: key taken / in the bin
+#pragma unroll
+  for (int j = 0; j < U; ++j) {
+    const uint32_t i4 = (u0 >> 2) + tid + j * kRT;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool ok = 4 * i4 + e < u1;
+      const int b = (int)(fast_key(v[j][e]) >> kBinShift);
+      take_m |= (uint32_t)(ok && b > bstar) << (4 * j + e);
+      tie_m |= (uint32_t)(ok && b == bstar) << (4 * j + e);
+    }
+  }
+  const uint32_t packed = (uint32_t)__builtin_popcount(take_m) |
+                          ((uint32_t)__builtin_popcount(tie_m) << 16);
+  const uint32_t incl = wave_incl_scan(packed);
+  const uint32_t tot = __builtin_amdgcn_readlane(incl, 63);
+  if (tot == 0) return;                         // wave-uniform
+  uint32_t bt = 0, bk = 0;
+  if (lane == 63) {
+    if (tot & 0xFFFFu) bt = atomicAdd(&rc[RH_EMIT], tot & 0xFFFFu);
+    if (tot >> 16) bk = atomicAdd(&rc[RH_TIES], tot >> 16);
+  }
+  const uint32_t excl = incl - packed;
+  uint32_t o = __builtin_amdgcn_readlane(bt, 63) + (excl & 0xFFFFu);
+  uint32_t l = __builtin_amdgcn_readlane(bk, 63) + (excl >> 16);
+#pragma unroll
+  for (int j = 0; j < U; ++j) {
+    const uint32_t u = 4 * ((u0 >> 2) + tid + j * kRT);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int bit = 4 * j + e;
+      if ((take_m >> bit) & 1u) {
+        if (o < Kt) {
+          out_i[o] = (int32_t)(u + e);
+          if (out_s) out_s[o] = v[j][e];
+        }
+        ++o;
+      }
+      if ((tie_m >> bit) & 1u) {
+        if (l < (uint32_t)kRowTieCap) ties[l] = make_uint2(fast_key(v[j][e]), u + e);
+        ++l;
+      }
+    }
+  }
+}
+
+// Finish: one workgroup per row pads the row past its key count and takes the
+// best entries of the threshold bin: from the tie buffer when the bin fit in
+// it, else with a radix select over the row's stored scores.
+__global__ __launch_bounds__(kRowT) void k_rows_finish(PrefillArgs a) {
+  __shared__ uint2 list[kRowTieCap];
+  __shared__ uint2 tie[64];
+  __shared__ uint32_t hist[1024];
+  __shared__ uint32_t scratch[64];
+  __shared__ uint32_t s_out;
+  const int t = (int)blockIdx.x, tid = (int)threadIdx.x;
+  const int pos = row_pos(a, t);
+  int32_t* out_i = a.out_idx + (size_t)t * a.top_k;
+  float* out_s = a.out_score ? a.out_score + (size_t)t * a.top_k : nullptr;
+  const uint32_t n = (uint32_t)pos + 1u;
+  const uint32_t Kt = pos < 0 ? 0u : (n < (uint32_t)a.top_k ? n : (uint32_t)a.top_k);
+  for (uint32_t i = Kt + tid; i < (uint32_t)a.top_k; i += kRowT) {
+    out_i[i] = -1;
+    if (out_s) out_s[i] = -__builtin_inff();
+  }
+  if (Kt == 0) return;
+  const uint32_t* rc = a.rowctl + (size_t)t * kRowCtlWords;
+  const int bstar = (int)rc[RH_BSTAR];
+  const uint32_t above = rc[RH_ABOVE], nb = rc[RH_NB];
+  const uint32_t need = Kt - above;             // entries of the threshold bin to take
+  if (need == 0) return;
+  if (tid == 0) s_out = above;
+  __syncthreads();
+  const Emitter em{out_i, out_s, &s_out, Kt};
+  if (nb <= (uint32_t)kRowTieCap) {
+    const uint2* ties = a.ties + (size_t)t * kRowTieCap;
+    for (uint32_t i = tid; i < nb; i += kRowT) list[i] = ties[i];
+    __syncthreads();
+    finish_bin<kRowT, kBinBits>(list, nb, need, bstar, em, hist, scratch, tie);
+  } else {
+    const float* sc = a.scores + (size_t)t * (size_t)a.row_stride;
+    const uint64_t prefix = (uint64_t)bstar << (64 - kBinBits);
+    const uint64_t mask = (uint64_t)(kBins - 1) << (64 - kBinBits);
+    radix_finish<kRowT>(RowSource{sc, n}, prefix, mask, 64 - kBinBits, need, nb, em, hist, scratch);
+  }
+}
+
 template <int HT, int D, bool W32, bool SPLIT>
 hipError_t launch_score_t(const PrefillArgs& a, hipStream_t stream) {
   constexpr int ROWS = kRows;
@@ -557,12 +764,11 @@ hipError_t launch_prefill_score(const PrefillArgs& a, hipStream_t stream) {
   return hipErrorInvalidValue;
 }
 
-template <int FB, bool SELF = false>
+template <int FB>
 hipError_t launch_select_t(const PrefillArgs& a, hipStream_t stream) {
-  const size_t lds = (size_t)kSelListCap * 8 + 64 * 8 + (1024 + 64) * 4 + (SELF ? (4 << FB) : 0);
-  // (rows of a split call are few and long: 1024 threads each)
-  constexpr int NT = SELF ? 1024 : kST;
-  auto k = k_prefill_select<FB, SELF, NT>;
+  const size_t lds = (size_t)kSelListCap * 8 + 64 * 8 + (1024 + 64) * 4;
+  constexpr int NT = kST;
+  auto k = k_prefill_select<FB, NT>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -572,8 +778,23 @@ hipError_t launch_select_t(const PrefillArgs& a, hipStream_t stream) {
 
 hipError_t launch_prefill_select(const PrefillArgs& a, hipStream_t stream) {
   if (a.nq <= 0) return hipSuccess;
-  if (a.key_chunk > 0) return a.bin_bits == 12 ? launch_select_t<12, true>(a, stream)
-                                                : hipErrorInvalidValue;
+  if (a.key_chunk > 0) {
+    // (parts along x, rows along y: at most 65535 rows)
+    const int64_t parts = (a.l_max + kRowPartKeys - 1) / kRowPartKeys;
+    if (a.bin_bits != 12 || !a.rowctl || !a.parthist || !a.ties || a.row_parts < parts ||
+        a.nq > 65535 || parts > 65535)
+      return hipErrorInvalidValue;
+    const dim3 grid((unsigned)parts, (unsigned)a.nq);
+    hipLaunchKernelGGL(k_rows_count, grid, dim3(kRT), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_rows_threshold, dim3(a.nq), dim3(kRowT), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_rows_emit, grid, dim3(kRT), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_rows_finish, dim3(a.nq), dim3(kRowT), 0, stream, a);
+    return hipGetLastError();
+  }
   if (a.bin_bits == 12) return launch_select_t<12>(a, stream);
   if (a.bin_bits == 11) return launch_select_t<11>(a, stream);
   if (a.bin_bits == 10) return launch_select_t<10>(a, stream);

@@ -478,6 +478,38 @@ hipError_t launch_prefill_routed_score(const PrefillArgs& a, hipStream_t) {
 hipError_t launch_prefill_select(const PrefillArgs& a, hipStream_t) {
   begin("k_prefill_select");
   if (a.nq <= 0) return hipSuccess;
+  if (a.key_chunk > 0) {
+    // k_rows_count and k_rows_emit: grid (parts, rows), a part reads its
+    // 16-byte pieces below n (the last one whole); the count stores the part's
+    // histogram, the emission writes the output row and the tie buffer.
+    // k_rows_threshold and k_rows_finish: one workgroup per row, on the row's
+    // select words, part histograms, tie buffer and output row; the finish
+    // reads the whole stored row when the tie bin overflows the buffer
+    g_kernel = "k_rows_count / k_rows_threshold / k_rows_emit / k_rows_finish";
+    const int64_t parts = (a.l_max + kRowPartKeys - 1) / kRowPartKeys;
+    if (a.bin_bits != 12 || !a.rowctl || !a.parthist || !a.ties || a.row_parts < parts ||
+        a.nq > 65535 || parts > 65535)
+      return hipErrorInvalidValue;
+    for (int t = 0; t < a.nq; ++t) {
+      const QRow r = qrow(a.q_seq, a.q_pos, t, 1, a.l_max);
+      touch_elems(a.out_idx, (int64_t)t * a.top_k, (int64_t)(t + 1) * a.top_k, "out_idx");
+      if (a.out_score) touch_elems(a.out_score, (int64_t)t * a.top_k, (int64_t)(t + 1) * a.top_k, "out_score");
+      if (!(r.ok && r.seq == 0)) continue;
+      const int64_t n = r.pos + 1;
+      touch_elems(a.rowctl, (int64_t)t * kRowCtlWords, (int64_t)(t + 1) * kRowCtlWords, "row select counters");
+      const int64_t row_parts = (n + kRowPartKeys - 1) / kRowPartKeys;
+      if (row_parts > parts) violation("row %d has %lld parts of %lld", t, (long long)row_parts, (long long)parts);
+      // each part stores (and the threshold kernel reads) 2048 words of the row's
+      if (n > a.top_k)
+        touch_elems(a.parthist, (int64_t)t * a.row_parts * 2048,
+                    ((int64_t)t * a.row_parts + row_parts) * 2048, "part histograms");
+      const int64_t hi = 4 * ((n + 3) / 4);
+      if (hi > a.row_stride) violation("row %d reads %lld floats of a %lld stride", t, (long long)hi, (long long)a.row_stride);
+      touch_elems(a.scores, (int64_t)t * a.row_stride, (int64_t)t * a.row_stride + hi, "score row");
+      touch_elems(a.ties, (int64_t)t * kRowTieCap, (int64_t)(t + 1) * kRowTieCap, "tie buffer");
+    }
+    return hipSuccess;
+  }
   if (a.bin_bits != 12 && a.bin_bits != 11 && a.bin_bits != 10) return hipErrorInvalidValue;
   for (int t = 0; t < a.nq; ++t) {
     const QRow r = qrow(a.q_seq, a.q_pos, t, 1, a.l_max);
