@@ -600,7 +600,7 @@ hipError_t launch_hisa(const HisaArgs& a, hipStream_t) {
     touch_elems(a.cand1, (int64_t)t * g1 * a.ch1, (int64_t)t * g1 * a.ch1 + std::min<int64_t>(n1, g1) * a.ch1,
                 "block candidates (selection)");
     {
-      const int S = std::min<int>(std::min<int>((int)kHisaCandCap / (int)n1, a.ch1), 96);
+      const int S = std::min<int>(std::min<int>((int)kHisaCandCap / (int)n1, a.ch1), 128);
       const int U = (int)kHisaCandCap / 256;
       for (int tid = 0; tid < 256; ++tid)
         for (int u = 0; u < U; ++u) {
