@@ -112,6 +112,18 @@ def test_long_prefill_chunk_arbitrary_positions(dsa):
     _run(dsa, wl, 1000, seed=7, pos=pos, seq=seq, rows=list(range(0, 96, 7)) + [1, 2, 3, 4, 5])
 
 
+def test_key_split_rows_at_part_boundaries(dsa):
+    """24 rows of one 70000-key cache: 3 row groups, so the keys are split over
+    workgroups and the row select works in parts of 8192 keys.  Rows end
+    exactly at, just past and just before part boundaries, at and just past
+    k, and on a single key; every row."""
+    wl = datagen.small(3, nq=24, l_max=70000, n_heads=16, head_dim=64, n_plant=32)
+    k = 1500
+    pos = [8191, 8192, 8190, 16383, 16384, 24575, 24576, 65535, 65536, 69999, k - 1, k,
+           k - 2, 0, 40959, 40960, 57343, 57344, 12345, 33333, 49151, 49152, 1, 69998]
+    _run(dsa, wl, k, seed=12, pos=pos)
+
+
 def test_long_rows_all_equal_keys(dsa):
     """All scores tie in 70000-key rows (11-bit bins, the tie bin overflows
     LDS): the lowest indices are selected."""
