@@ -271,44 +271,56 @@ def test_hisa_and_misa_hisa_full_all_rows(dsa):
     assert not errs, "\n".join(errs[:10])
 
 
+def _prefill_rows(edges, seed, n=248, L=32768):
+    """The edge rows plus n more drawn (seeded, without repeats) from the whole
+    triangle, in order."""
+    extra = np.random.default_rng(seed).choice(L, size=n, replace=False)
+    return sorted(set(edges) | {int(x) for x in extra})
+
+
 def test_dense_prefill_full_sampled_rows(dsa):
     """32768 causal rows x 32768 keys, 64 heads, k 2048 (rows shorter than k
-    return every key); sampled rows across the triangle."""
+    return every key); the edge rows and 248 seeded rows across the triangle."""
     wl = datagen.WORKLOADS[3]
     say("[full] dense prefill 32768 x 32768")
     dev, h = _device_inputs(wl)
     idx, val = dsa.indexer_score_topk(dev["q"], dev["w"], dev["k"], dev["q_pos"], None,
                                       top_k=wl.top_k)
-    rows = [0, 1, 2046, 2047, 2048, 5000, 16383, 32767]
+    rows = _prefill_rows([0, 1, 2046, 2047, 2048, 5000, 16383, 32767], seed=31)
     gi, gv = idx[rows].cpu().numpy(), val[rows].cpu().numpy()
     K = O.to_f64(datagen.keys(wl, 0, h["q"], h["w"]), wl.dtype)
-    errs = []
-    for i, t in enumerate(rows):
+
+    def row(i):
+        t = rows[i]
         q_t, w_t = O.to_f64(h["q"][t], wl.dtype), h["w"][t].astype(np.float64)
         r = O.dense_row(q_t, w_t, K, t, wl.top_k)
-        errs += _check(gi[i], gv[i], r, wl.top_k, q_t, w_t, K, f"row {t}")
+        return _check(gi[i], gv[i], r, wl.top_k, q_t, w_t, K, f"row {t}")
+
+    errs = _rows_parallel(row, range(len(rows)))
     assert not errs, "\n".join(errs[:10])
 
 
 def test_misa_prefill_full_sampled_rows(dsa):
     """MISA on the prefill geometry at full size: the dense prefill workload's
     32768 rows x 32768 keys, 64 heads, routed to h = 8 over 64-key pooled
-    blocks, k 2048; sampled rows, each checked on its routed heads and then on
-    the selection given the GPU's heads."""
+    blocks, k 2048; the edge rows and 248 seeded rows, each checked on its
+    routed heads and then on the selection given the GPU's heads."""
     wl = datagen.WORKLOADS[3]
     h, B = 8, 64
     say("[full] MISA prefill 32768 x 32768, h 8")
     dev, hin = _device_inputs(wl)
     res = dsa.misa_route_score_topk(dev["q"], dev["w"], dev["k"], dev["q_pos"], None, block=B,
                                     n_active_heads=h, top_k=wl.top_k, with_importance=True)
-    rows = [0, 63, 64, 2047, 2048, 9999, 32767]
+    rows = _prefill_rows([0, 63, 64, 2047, 2048, 9999, 32767], seed=32)
     gi = res["idx"][rows].cpu().numpy()
     gv = res["score"][rows].cpu().numpy()
     gh = res["heads"][rows].cpu().numpy().astype(np.int64)
     gI = res["importance"][rows].cpu().numpy().astype(np.float64)
     K = O.to_f64(datagen.keys(wl, 0, hin["q"], hin["w"]), wl.dtype)
-    errs = []
-    for i, t in enumerate(rows):
+
+    def row(i):
+        t = rows[i]
+        errs = []
         q_t, w_t = O.to_f64(hin["q"][t], wl.dtype), hin["w"][t].astype(np.float64)
         pooled = O.misa_pooled_for_query(K, B, t)
         I = O.misa_importance(q_t, w_t, pooled)
@@ -320,35 +332,41 @@ def test_misa_prefill_full_sampled_rows(dsa):
                                 what=f"heads row {t}")
         r = O.misa_row(q_t, w_t, K, t, B, h, wl.top_k, heads=gh[i])
         errs += _check(gi[i], gv[i], r, wl.top_k, q_t, w_t, K, f"misa row {t}", gh[i])
+        return errs
+
+    errs = _rows_parallel(row, range(len(rows)))
     assert not errs, "\n".join(errs[:10])
 
 
 def test_hisa_prefill_full_sampled_rows(dsa):
     """HISA on the prefill geometry at full size: 32768 rows x 32768 keys, 64
-    heads, 128-key blocks, m 64, k 2048; sampled rows (short rows that keep
-    every block, rows whose last block is partial, the longest row), each
-    checked on its block selection and then on the token selection inside the
-    GPU's blocks."""
+    heads, 128-key blocks, m 64, k 2048; the edge rows (short rows that keep
+    every block, rows whose last block is partial, the longest row) and 248
+    seeded rows, each checked on its block selection and then on the token
+    selection inside the GPU's blocks."""
     wl = datagen.WORKLOADS[3]
     B, m = 128, 64
     say("[full] HISA prefill 32768 x 32768, B 128, m 64")
     dev, hin = _device_inputs(wl)
     res = dsa.hisa_block_filter_topk(dev["q"], dev["w"], dev["k"], dev["q_pos"], None, block=B,
                                      m_blocks=m, top_k=wl.top_k)
-    rows = [0, 127, 2047, 8191, 8192, 20000, 32767]
+    rows = _prefill_rows([0, 127, 2047, 8191, 8192, 20000, 32767], seed=33)
     gi = res["idx"][rows].cpu().numpy()
     gv = res["score"][rows].cpu().numpy()
     gb = res["blocks"][rows].cpu().numpy()
     gbs = res["block_score"][rows].cpu().numpy()
     K = O.to_f64(datagen.keys(wl, 0, hin["q"], hin["w"]), wl.dtype)
-    errs = []
-    for i, t in enumerate(rows):
+
+    def row(i):
+        t = rows[i]
         q_t, w_t = O.to_f64(hin["q"][t], wl.dtype), hin["w"][t].astype(np.float64)
         pooled = O.misa_pooled_for_query(K, B, t)
         bs, bA = O.hisa_block_scores(q_t, w_t, pooled)
         Fb = O.dot_magnitude(q_t, w_t, pooled)
-        errs += check_selection(gb[i], gbs[i], np.arange(pooled.shape[0]), bs, bA, m, Fb,
-                                what=f"blocks row {t}")
+        errs = check_selection(gb[i], gbs[i], np.arange(pooled.shape[0]), bs, bA, m, Fb,
+                               what=f"blocks row {t}")
         r = O.hisa_row(q_t, w_t, K, t, B, m, wl.top_k, blocks=gb[i])
-        errs += _check(gi[i], gv[i], r, wl.top_k, q_t, w_t, K, f"hisa row {t}")
+        return errs + _check(gi[i], gv[i], r, wl.top_k, q_t, w_t, K, f"hisa row {t}")
+
+    errs = _rows_parallel(row, range(len(rows)))
     assert not errs, "\n".join(errs[:10])
