@@ -96,9 +96,19 @@ __global__ __launch_bounds__(256) void k_prepare(PrepArgs a, int n_zero_blocks) 
   if (n == 0) return;
   const int64_t r0 = pos + 1 - n;
   const uint16_t* base = a.keys + ((size_t)seq * (size_t)a.l_max + (size_t)r0) * a.head_dim;
+  // rows are read eight at a time (the loads in flight together), then added
+  // in row order, so the float64 sum is the same as a row-by-row loop's
   for (int e = threadIdx.x; e < a.head_dim; e += 256) {
     double acc = 0.0;
-    for (int64_t r = 0; r < n; ++r) acc += bf16_to_f64(base[(size_t)r * a.head_dim + e]);
+    int64_t r = 0;
+    for (; r + 8 <= n; r += 8) {
+      uint16_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = base[(size_t)(r + u) * a.head_dim + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc += bf16_to_f64(v[u]);
+    }
+    for (; r < n; ++r) acc += bf16_to_f64(base[(size_t)r * a.head_dim + e]);
     a.partial[(size_t)t * a.head_dim + e] = f64_to_bf16(acc / (double)n);
   }
 }
